@@ -1,0 +1,439 @@
+/*
+ * mxq_oracle.c -- CPU oracle (test infrastructure only; see mxq_oracle.h).
+ *
+ * Every function restates a definition: the OCP E4M3FN / E2M1 formats, the
+ * bfloat16 format, the Walsh-Hadamard butterfly, the FP8 1x128 recipe of the
+ * onnxruntime QMoE PR (Description), the NVFP4 two-level scaling with the
+ * per-section reading of the tensor scale, and Philox4x32-10 from the SC'11 paper.
+ * Nothing here is tuned; clarity wins over speed wherever they disagree.
+ */
+#include "mxq_oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Constants, each the binary32 value nearest to the real number named.      */
+/* ------------------------------------------------------------------------ */
+/* IEEE division and square root are correctly rounded, so these are exact
+ * statements of F(r).  sqrtf(2)/16 is F(sqrt 2)/16 = F(1/sqrt 128) because
+ * dividing by 16 is exact. */
+static float f_one_over(float d) { volatile float one = 1.0f; return one / d; }
+static float F_1E_10(void)      { return 1e-10f; }
+static float F_1_OVER_448(void) { return f_one_over(448.0f); }
+static float F_1_OVER_2688(void){ return f_one_over(2688.0f); }
+static float F_1_OVER_6(void)   { return f_one_over(6.0f); }
+static float F_C128(void)       { volatile float two = 2.0f; return sqrtf(two) / 16.0f; }
+
+static uint32_t f32_bits(float v) { uint32_t b; memcpy(&b, &v, 4); return b; }
+static float    bits_f32(uint32_t b) { float v; memcpy(&v, &b, 4); return v; }
+
+/* ------------------------------------------------------------------------ */
+/* bfloat16                                                                  */
+/* ------------------------------------------------------------------------ */
+float oracle_bf16_to_f32(uint16_t b) { return bits_f32((uint32_t)b << 16); }
+
+/* Nearest bfloat16 with ties to the even significand.  For a finite v, the two
+ * candidates are v with its low 16 bits cleared (same sign, magnitude rounded
+ * toward zero) and the next bfloat16 away from zero.  Comparing the dropped
+ * 16 bits with one half of a bfloat16 ulp (0x8000) decides; a carry out of the
+ * mantissa moves to the next binade (or to infinity), which is correct. */
+uint16_t oracle_f32_to_bf16(float v)
+{
+    uint32_t b = f32_bits(v);
+    if (isnan(v)) return (uint16_t)((b >> 16) | 0x0040u); /* stays a (quiet) NaN */
+    uint32_t lo    = b & 0xFFFF0000u;
+    uint32_t rest  = b & 0x0000FFFFu;
+    uint32_t up    = lo + 0x00010000u;
+    uint32_t pick;
+    if (rest < 0x8000u)      pick = lo;
+    else if (rest > 0x8000u) pick = up;
+    else                     pick = ((lo >> 16) & 1u) ? up : lo; /* tie: even significand */
+    return (uint16_t)(pick >> 16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;  */
+/* S.1111.111 is NaN; largest finite value 448.                              */
+/* ------------------------------------------------------------------------ */
+static double e4m3_magnitude(int c) /* c in 0..126 */
+{
+    int e = (c >> 3) & 15, m = c & 7;
+    if (e == 0) return ldexp((double)m / 8.0, -6);
+    return ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+float oracle_e4m3_value(uint8_t code)
+{
+    int c = code & 0x7F;
+    if (c == 0x7F) return NAN;
+    double m = e4m3_magnitude(c);
+    return (float)((code & 0x80) ? -m : m);
+}
+
+/* Nearest code among 0x00..0x7E (magnitudes increase with the code), ties to
+ * the even code; |v| >= 448 saturates to 0x7E; NaN -> 0x7F; the sign bit of v
+ * is kept, so -0 and negative values that round to zero give 0x80. */
+uint8_t oracle_e4m3_encode(float v)
+{
+    if (isnan(v)) return 0x7F;
+    uint8_t s = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(s | 0x7E);
+    /* bracket: lo = largest code with magnitude <= a (binary search) */
+    int lo = 0, hi = 126;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (e4m3_magnitude(mid) <= a) lo = mid; else hi = mid - 1;
+    }
+    if (e4m3_magnitude(lo) == a) return (uint8_t)(s | lo);
+    int up = lo + 1;                               /* exists because a < 448 */
+    double twice_a = 2.0 * a;                      /* exact in double */
+    double sum = e4m3_magnitude(lo) + e4m3_magnitude(up); /* exact in double */
+    int c;
+    if (twice_a < sum)      c = lo;
+    else if (twice_a > sum) c = up;
+    else                    c = (lo % 2 == 0) ? lo : up;
+    return (uint8_t)(s | c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* E2M1 (FP4): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7; bit 3 is */
+/* the sign.                                                                 */
+/* ------------------------------------------------------------------------ */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+float oracle_e2m1_value(uint8_t code)
+{
+    double m = E2M1_MAG[code & 7];
+    return (float)((code & 8) ? -m : m);
+}
+
+/* Nearest code, ties to the even code, |v| >= 6 saturates to 7, sign kept. */
+uint8_t oracle_e2m1_encode(float v)
+{
+    uint8_t s = signbit(v) ? 0x8 : 0x0;
+    double a = fabs((double)v);
+    if (!(a < 6.0)) return (uint8_t)(s | 7); /* also NaN: callers never pass one */
+    int lo = 0;
+    for (int c = 1; c < 8; ++c) if (E2M1_MAG[c] <= a) lo = c;
+    if (E2M1_MAG[lo] == a) return (uint8_t)(s | lo);
+    int up = lo + 1;
+    double twice_a = 2.0 * a, sum = E2M1_MAG[lo] + E2M1_MAG[up];
+    int c;
+    if (twice_a < sum)      c = lo;
+    else if (twice_a > sum) c = up;
+    else                    c = (lo % 2 == 0) ? lo : up;
+    return (uint8_t)(s | c);
+}
+
+/* Stochastic rounding on the E2M1 grid with 8 random bits r: the magnitude is
+ * written a = (k + f) * D with D the local grid spacing (0.5 below 2, 1 below 4,
+ * 2 above); with F = floor(256 f) the value rounds up iff F + r >= 256, so it
+ * rounds up with probability F/256.  Values at or above 6 saturate. */
+uint8_t oracle_e2m1_encode_sr(float v, uint8_t r)
+{
+    uint8_t s = signbit(v) ? 0x8 : 0x0;
+    float a = fabsf(v);
+    if (!(a < 6.0f)) return (uint8_t)(s | 7);
+    float D = (a < 2.0f) ? 0.5f : (a < 4.0f) ? 1.0f : 2.0f;
+    float u = a / D;                 /* exact: D is a power of two */
+    float k = floorf(u);
+    float f = u - k;                 /* exact */
+    int F = (int)floorf(256.0f * f); /* exact product */
+    if (F + (int)r >= 256) k += 1.0f;
+    double mag = (double)k * (double)D; /* on the grid by construction */
+    for (int c = 0; c < 8; ++c)
+        if (E2M1_MAG[c] == mag) return (uint8_t)(s | c);
+    return (uint8_t)(s | 7); /* unreachable */
+}
+
+float oracle_amax(const float* v, int64_t n)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        if (isnan(v[i])) continue;
+        float a = fabsf(v[i]);
+        if (a > m) m = a;
+    }
+    return m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon et al., SC'11): ten rounds of the 4x32 S-box with   */
+/* multipliers 0xD2511F53 / 0xCD9E8D57; the key is bumped by the Weyl        */
+/* constants 0x9E3779B9 / 0xBB67AE85 between rounds.                         */
+/* ------------------------------------------------------------------------ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0;
+        uint32_t n1 = lo1;
+        uint32_t n2 = hi0 ^ c3 ^ k1;
+        uint32_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* 16 random bytes for one 1x16 block: counter (lo(off), hi(off), lo(beta),
+ * hi(beta)), key (lo(seed), hi(seed)); byte t of the block is byte t&3 of
+ * output word t>>2. */
+static void block_random_bytes(uint64_t seed, uint64_t off, uint64_t beta, uint8_t r[16])
+{
+    uint32_t ctr[4] = {(uint32_t)off, (uint32_t)(off >> 32), (uint32_t)beta, (uint32_t)(beta >> 32)};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    oracle_philox4x32_10(ctr, key, w);
+    for (int t = 0; t < 16; ++t) r[t] = (uint8_t)((w[t >> 2] >> (8 * (t & 3))) & 0xFFu);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Walsh-Hadamard transform, Sylvester order, stages h = 1, 2, 4, ...        */
+/* ------------------------------------------------------------------------ */
+void oracle_wht(const float* in, int n, uint32_t sign_mask, float c, float* out)
+{
+    float v[128];
+    for (int i = 0; i < n; ++i) {
+        int flip = (i < 32) && ((sign_mask >> i) & 1u);
+        v[i] = flip ? -in[i] : in[i];
+    }
+    for (int h = 1; h < n; h *= 2) {
+        for (int i = 0; i < n; ++i) {
+            if (i & h) continue;
+            float a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = a - b;
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        float scaled = v[i] * c;
+        out[i] = oracle_bf16_to_f32(oracle_f32_to_bf16(scaled));
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 1x128                                                                 */
+/* ------------------------------------------------------------------------ */
+float oracle_fp8_group(const float* x, uint8_t* codes)
+{
+    float a = oracle_amax(x, 128);
+    float floor_ = F_1E_10();
+    float s = ((a > floor_) ? a : floor_) * F_1_OVER_448();
+    for (int i = 0; i < 128; ++i) {
+        float q = x[i] / s;
+        codes[i] = oracle_e4m3_encode(q);
+    }
+    return s;
+}
+
+void oracle_quant_fp8_1x128(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                            uint8_t* q, int64_t ldq, float* scales,
+                            int64_t scale_stride_row, int64_t scale_stride_group)
+{
+    float g[128];
+    for (int64_t r = 0; r < m; ++r) {
+        for (int64_t gi = 0; gi < k / 128; ++gi) {
+            for (int i = 0; i < 128; ++i) g[i] = oracle_bf16_to_f32(x[r * ldx + gi * 128 + i]);
+            float s = oracle_fp8_group(g, q + r * ldq + gi * 128);
+            scales[r * scale_stride_row + gi * scale_stride_group] = s;
+        }
+    }
+}
+
+void oracle_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                               const uint16_t* nope, int64_t ld_nope, int64_t m,
+                               uint8_t* q, float* scales)
+{
+    float v[128], y[128];
+    float c = F_C128();
+    for (int64_t r = 0; r < m; ++r) {
+        for (int i = 0; i < d_pe; ++i)        v[i] = oracle_bf16_to_f32(pe[r * ld_pe + i]);
+        for (int i = d_pe; i < 128; ++i)      v[i] = oracle_bf16_to_f32(nope[r * ld_nope + (i - d_pe)]);
+        oracle_wht(v, 128, 0u, c, y);
+        scales[r] = oracle_fp8_group(y, q + r * 128);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4                                                                     */
+/* ------------------------------------------------------------------------ */
+float oracle_nvfp4_global_scale(float amax)
+{
+    float floor_ = F_1E_10();
+    return ((amax > floor_) ? amax : floor_) * F_1_OVER_2688();
+}
+
+void oracle_nvfp4_block(const float* v, float g, const uint8_t* rbits,
+                        uint8_t* scale_code, uint8_t* codes)
+{
+    for (int i = 0; i < 16; ++i) {
+        if (isnan(v[i])) {              /* a NaN block has no finite encoding */
+            *scale_code = 0x7F;
+            for (int j = 0; j < 16; ++j) codes[j] = 0;
+            return;
+        }
+    }
+    float a  = oracle_amax(v, 16);
+    float a6 = a * F_1_OVER_6();
+    float t  = a6 / g;
+    uint8_t sc = oracle_e4m3_encode(t);
+    *scale_code = sc;
+    if (sc == 0x00) {                   /* scale underflow: the block decodes to zero */
+        for (int j = 0; j < 16; ++j) codes[j] = 0;
+        return;
+    }
+    float d = oracle_e4m3_value(sc) * g;
+    for (int i = 0; i < 16; ++i) {
+        float q = v[i] / d;
+        codes[i] = rbits ? oracle_e2m1_encode_sr(q, rbits[i]) : oracle_e2m1_encode(q);
+    }
+}
+
+/* The 16 column-wise values of column c, 16-row block b of a section. */
+static void column_block_values(const uint16_t* x, int64_t k, uint16_t sign_mask,
+                                int64_t c, int64_t b, float* y)
+{
+    float col[16];
+    for (int t = 0; t < 16; ++t) col[t] = oracle_bf16_to_f32(x[(16 * b + t) * k + c]);
+    oracle_wht(col, 16, sign_mask, 0.25f, y);
+}
+
+void oracle_nvfp4_section_amax(const uint16_t* x, int64_t rows, int64_t k,
+                               uint16_t sign_mask, float* amax_row, float* amax_col)
+{
+    float ar = 0.0f, ac = 0.0f, y[16];
+    for (int64_t i = 0; i < rows * k; ++i) {
+        float v = oracle_bf16_to_f32(x[i]);
+        if (!isnan(v) && fabsf(v) > ar) ar = fabsf(v);
+    }
+    for (int64_t b = 0; b < rows / 16; ++b) {
+        for (int64_t c = 0; c < k; ++c) {
+            column_block_values(x, k, sign_mask, c, b, y);
+            float m = oracle_amax(y, 16);
+            if (m > ac) ac = m;
+        }
+    }
+    *amax_row = ar;
+    *amax_col = ac;
+}
+
+static void pack_nibbles(const uint8_t* codes16, uint8_t* out8)
+{
+    for (int j = 0; j < 8; ++j)
+        out8[j] = (uint8_t)((codes16[2 * j] & 0xF) | ((codes16[2 * j + 1] & 0xF) << 4));
+}
+
+void oracle_nvfp4_section(const uint16_t* x, int64_t rows, int64_t k, uint16_t sign_mask,
+                          uint32_t flags, float g_row, float g_col,
+                          int use_sr_row, int use_sr_col, uint64_t seed,
+                          uint64_t row_offset, uint64_t col_offset,
+                          int64_t row_begin, int64_t row_end,
+                          int64_t col_begin, int64_t col_end,
+                          uint8_t* row_codes, uint8_t* row_scales,
+                          uint8_t* col_codes, uint8_t* col_scales,
+                          uint8_t* fp8_codes, float* fp8_scales)
+{
+    float v[128];
+    uint8_t codes[16], rb[16], sc;
+    if (flags & ORACLE_ROWWISE) {
+        for (int64_t r = row_begin; r < row_end; ++r) {
+            for (int64_t kb = 0; kb < k / 16; ++kb) {
+                for (int t = 0; t < 16; ++t) v[t] = oracle_bf16_to_f32(x[r * k + 16 * kb + t]);
+                if (use_sr_row) block_random_bytes(seed, row_offset, (uint64_t)(r * (k / 16) + kb), rb);
+                oracle_nvfp4_block(v, g_row, use_sr_row ? rb : NULL, &sc, codes);
+                row_scales[r * (k / 16) + kb] = sc;
+                pack_nibbles(codes, row_codes + r * (k / 2) + 8 * kb);
+            }
+        }
+    }
+    if (flags & ORACLE_FP8_ROWWISE) {
+        for (int64_t r = row_begin; r < row_end; ++r) {
+            for (int64_t gi = 0; gi < k / 128; ++gi) {
+                for (int i = 0; i < 128; ++i) v[i] = oracle_bf16_to_f32(x[r * k + 128 * gi + i]);
+                fp8_scales[r * (k / 128) + gi] = oracle_fp8_group(v, fp8_codes + r * k + 128 * gi);
+            }
+        }
+    }
+    if (flags & ORACLE_COLUMNWISE) {
+        for (int64_t c = col_begin; c < col_end; ++c) {
+            for (int64_t b = 0; b < rows / 16; ++b) {
+                column_block_values(x, k, sign_mask, c, b, v);
+                if (use_sr_col) block_random_bytes(seed, col_offset, (uint64_t)(c * (rows / 16) + b), rb);
+                oracle_nvfp4_block(v, g_col, use_sr_col ? rb : NULL, &sc, codes);
+                col_scales[c * (rows / 16) + b] = sc;
+                pack_nibbles(codes, col_codes + c * (rows / 2) + 8 * b);
+            }
+        }
+    }
+}
+
+int oracle_group_rht_quant_nvfp4(const uint16_t* x, int64_t k,
+                                 const int64_t* split_sections, int64_t num_sections,
+                                 uint16_t sign_mask, uint32_t flags, uint64_t seed,
+                                 const uint64_t* row_offsets, const uint64_t* col_offsets,
+                                 uint8_t* row_codes, uint8_t* row_scales, float* row_global,
+                                 uint8_t* col_codes, uint8_t* col_scales, float* col_global,
+                                 uint8_t* fp8_codes, float* fp8_scales)
+{
+    if (k <= 0 || k % 128 != 0) return 1;
+    int64_t R = 0; /* first row of the current section */
+    for (int64_t s = 0; s < num_sections; ++s) {
+        int64_t m = split_sections[s];
+        if (m < 0 || m % 128 != 0) return 2;
+        const uint16_t* xs = x + R * k;
+        float ar = 0.0f, ac = 0.0f;
+        oracle_nvfp4_section_amax(xs, m, k, sign_mask, &ar, &ac);
+        float gr = oracle_nvfp4_global_scale(ar);
+        float gc = oracle_nvfp4_global_scale(ac);
+        if (flags & ORACLE_ROWWISE)    row_global[s] = gr;
+        if (flags & ORACLE_COLUMNWISE) col_global[s] = gc;
+        oracle_nvfp4_section(xs, m, k, sign_mask, flags, gr, gc,
+                             row_offsets != NULL, col_offsets != NULL, seed,
+                             row_offsets ? row_offsets[s] : 0, col_offsets ? col_offsets[s] : 0,
+                             0, m, 0, k,
+                             (flags & ORACLE_ROWWISE) ? row_codes + R * (k / 2) : NULL,
+                             (flags & ORACLE_ROWWISE) ? row_scales + R * (k / 16) : NULL,
+                             (flags & ORACLE_COLUMNWISE) ? col_codes + k * R / 2 : NULL,
+                             (flags & ORACLE_COLUMNWISE) ? col_scales + k * R / 16 : NULL,
+                             (flags & ORACLE_FP8_ROWWISE) ? fp8_codes + R * k : NULL,
+                             (flags & ORACLE_FP8_ROWWISE) ? fp8_scales + R * (k / 128) : NULL);
+        R += m;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Element-wise loops                                                        */
+/* ------------------------------------------------------------------------ */
+void oracle_e4m3_encode_n(const float* v, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(v[i]);
+}
+
+void oracle_e2m1_encode_n(const float* v, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(v[i]);
+}
+
+void oracle_e2m1_encode_sr_n(const float* v, const uint8_t* r, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_encode_sr(v[i], r[i]);
+}
+
+void oracle_f32_to_bf16_n(const float* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(v[i]);
+}
+
+void oracle_wht_n(const float* in, int64_t count, int n, uint32_t sign_mask, float c, float* out)
+{
+    for (int64_t i = 0; i < count; ++i) oracle_wht(in + i * n, n, sign_mask, c, out + i * n);
+}
