@@ -1,0 +1,198 @@
+/*
+ * mxq.h -- C ABI of the mxq block-quantization library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Three entry points quantize BF16 activations on the GPU:
+ *   mxq_quant_fp8_1x128        FP8 E4M3 with one FP32 scale per 1x128 group
+ *   mxq_hadamard_quant_fp8     cat[qk_pe, qk_nope] -> normalized 128-point
+ *                              Walsh-Hadamard rotation -> FP8 1x128
+ *   mxq_group_rht_quant_nvfp4  grouped (MoE split sections) NVFP4, row-wise and
+ *                              column-wise after a 16-point random-sign Hadamard
+ *                              transform, optionally with an FP8 1x128 row-wise
+ *                              output in the same call
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named *_bf16 / codes / scales / workspace are DEVICE pointers; the
+ *    caller owns every buffer.  split_sections, mxq_sr and its offset arrays are
+ *    HOST memory, read during the call only (their values are baked into the
+ *    kernel arguments, so under stream capture the capture-time values are used).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous: MXQ_OK means the work was enqueued.
+ *  - The library never allocates, frees, memsets, synchronizes or reads the
+ *    environment; it keeps no global state and is re-entrant.  Calls in flight at
+ *    the same time need distinct workspaces.
+ *  - All argument checks run on the host before anything is enqueued; on an error
+ *    nothing is launched and no output is touched.  A failed launch returns
+ *    MXQ_ERR_HIP (outputs are then undefined).  There is no fallback path: an
+ *    unsupported request is an error, never a slower substitute.
+ *  - Arithmetic is IEEE binary32 with one rounding per operation in the order
+ *    stated below; every output is bit-exact with respect to that definition.
+ *
+ * Sources of the operations (page, then section):
+ *  - onnxruntime PR #33644, QMoE dynamic FP8 activation quantization,
+ *    Description: K128 groups; scale = max(amax, 1e-10) * float32(1/448); FP32
+ *    normalization by division; saturating nearest-even E4M3FN.
+ *  - TensorRT-LLM PR #15158, "Add rotate_activation to DSA fused_cat_fp8 path",
+ *    Summary: cat[qk_pe, qk_nope] -> rotate_activation -> fp8_quantize_1x128;
+ *    the discussion's (Hq).(Hk) = q.k for the orthonormal rotation.
+ *  - TransformerEngine PR #2564, "[NVFP4][MOE] Bug Fix for NVFP4 Grouped Quant",
+ *    Greptile summary and sequence diagram: grouped row-wise + column-wise
+ *    (RHT) NVFP4 cast with a caller-provided workspace, no allocation per call;
+ *    review thread: a workspace-size query.
+ *  - TransformerEngine PR #2555, review comments on cast.cpp and quantizer.cpp:
+ *    split_section % 128 == 0; RHT on the column-wise (transposed) operand only;
+ *    row-wise-only requests skip the RHT work; a separate column-wise RNG state;
+ *    deterministic RNG offsets rather than sequential generator advancement.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_ERR_INVALID_ARGUMENT = 1,    /* NULL pointer, negative size, bad flags ...   */
+    MXQ_ERR_MISALIGNED = 2,          /* k or a section not a multiple of 128, or a  */
+                                     /* pointer / stride not 16-byte aligned        */
+    MXQ_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < the size query's value    */
+    MXQ_ERR_UNSUPPORTED = 4,         /* outside the supported profile (limits)      */
+    MXQ_ERR_HIP = 5                  /* a HIP launch failed                          */
+} mxq_status;
+
+/* Static string naming the status; never NULL. */
+const char* mxq_status_string(mxq_status s);
+
+/* Library version string, e.g. "mxq 0.1.0 gfx950". */
+const char* mxq_version(void);
+
+/* Limits of the supported profile. */
+#define MXQ_ROW_ALIGN 128          /* rows per section and k: multiples of this   */
+#define MXQ_MAX_SECTIONS 256       /* split sections per grouped call             */
+
+/* ---------------------------------------------------------------------------
+ * FP8 E4M3 (OCP E4M3FN), one FP32 scale per 1x128 group along k.
+ *
+ *   x_bf16   [m][ldx] BF16 bit patterns, row-major, ldx >= k
+ *   q_e4m3   [m][ldq] E4M3 codes, ldq >= k
+ *   scales   scales[r * scale_stride_row + g * scale_stride_group] for group g of
+ *            row r; ({k/128, 1} is [m][k/128]; {1, m} is the transposed [k/128][m])
+ *
+ * For each group G of 128 consecutive elements of a row:
+ *   a = max |x| over G (NaN ignored; 0 if none),  s = fl(max(a, F(1e-10)) * F(1/448)),
+ *   q_i = E4M3(fl(x_i / s))   (IEEE division, nearest-even, saturating at 448;
+ *                               a NaN element gives 0x7F).
+ * Requirements: k % 128 == 0; ldx, ldq multiples of 8 and 16; x, q 16-byte
+ * aligned; scales 4-byte aligned.  m == 0 is a successful no-op.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int64_t ldx,
+                               uint8_t* q_e4m3, int64_t ldq,
+                               float* scales, int64_t scale_stride_row, int64_t scale_stride_group,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------
+ * DSA-indexer rotate + quantize.  For each row r:
+ *   v = cat(pe[r][0:d_pe], nope[r][0:128-d_pe])           (qk_pe first)
+ *   y = BF16(fl(WHT_128(v) * F(1/sqrt(128))))            (Sylvester order, butterfly
+ *        stages h = 1, 2, 4, ..., 64; (v_i, v_i+h) <- (v_i + v_i+h, v_i - v_i+h))
+ *   q[r][:], scales[r] = FP8 1x128 of y (as mxq_quant_fp8_1x128).
+ *
+ *   pe    [m][ld_pe]   BF16, d_pe in {0, 8, 16, ..., 128}; may be NULL if d_pe == 0
+ *   nope  [m][ld_nope] BF16; may be NULL if d_pe == 128
+ *   q     [m][128] E4M3 codes;  scales [m] FP32
+ * Requirements: ld_pe, ld_nope multiples of 8; pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                  const uint16_t* nope, int64_t ld_nope, int64_t m,
+                                  uint8_t* q_e4m3, float* scales, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Grouped NVFP4 quantization with a 16-point random Hadamard transform (RHT) on
+ * the column-wise operand.
+ *
+ * x_bf16 is [total_rows][k] BF16 (row stride k), total_rows = sum(split_sections).
+ * Section s covers rows [R_s, R_s + m_s), m_s = split_sections[s] (m_s may be 0).
+ *
+ * flags (any non-empty combination):
+ *   MXQ_ROWWISE      NVFP4 of x along k:
+ *                      codes  [total_rows][k/2]   (2 E2M1 codes per byte, even
+ *                                                  element in the low nibble)
+ *                      block_scales [total_rows][k/16] E4M3
+ *                      global_scales[num_sections] FP32
+ *   MXQ_COLUMNWISE   NVFP4 of the transposed, rotated operand: for each 16-row block
+ *                    b of a section and each column c the values
+ *                      Y[c][16b + t] = BF16(fl(0.25 * (H16 D x[16b + 0..15][c]))_t)
+ *                    (D = diag of signs from rht_sign_mask, bit t set = negate row
+ *                    16b + t; H16 Sylvester; butterfly stages h = 1, 2, 4, 8).
+ *                    Section s's outputs: codes at byte offset k*R_s/2 as [k][m_s/2],
+ *                    block_scales at byte offset k*R_s/16 as [k][m_s/16];
+ *                    global_scales[num_sections] FP32.
+ *   MXQ_FP8_ROWWISE  FP8 1x128 of x (as mxq_quant_fp8_1x128): codes [total_rows][k],
+ *                    scales [total_rows][k/128].
+ *
+ * NVFP4 encoding of one direction of section s (values v = x or Y):
+ *   A = max |v| over the section (NaN ignored);  g = fl(max(A, F(1e-10)) * F(1/2688))
+ *   (stored in global_scales; an empty section stores fl(F(1e-10) * F(1/2688))).
+ *   Per 1x16 block: if it holds a NaN, scale 0x7F and codes 0; else
+ *   a = max |v|, t = fl(fl(a * F(1/6)) / g), sc = E4M3(t); if sc == 0, codes 0;
+ *   else d = fl(E4M3value(sc) * g) and code_i = E2M1(fl(v_i / d)) (nearest-even,
+ *   saturating at 6) or, with stochastic rounding, the grid neighbour above with
+ *   probability floor(256 f)/256 via 8 Philox bits per element.
+ *   Dequantization: E2M1value(code) * E4M3value(sc) * g.
+ *
+ * sr: NULL, or {seed, row_offsets, col_offsets} with host arrays of num_sections
+ *   Philox4x32-10 offsets (NULL = nearest-even in that direction).  Each 1x16 block
+ *   draws one Philox call with key (lo32(seed), hi32(seed)) and counter
+ *   (lo32(off_s), hi32(off_s), lo32(beta), hi32(beta)); beta = r*(k/16) + kb for
+ *   row r (section-local) and block kb, beta = c*(m_s/16) + b for column c and
+ *   block b; element t uses byte t&3 of output word t>>2.
+ *
+ * workspace: device scratch of at least
+ *   mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
+ *   bytes, 256-byte aligned; it needs no initialization and holds nothing between
+ *   calls.
+ *
+ * Requirements: k % 128 == 0, every m_s % 128 == 0 (else MXQ_ERR_MISALIGNED, with
+ * no unfused fallback); 1 <= num_sections <= MXQ_MAX_SECTIONS; total_rows <= 2^31 -
+ * 128 and total_rows * k < 2^40; the requested outputs non-NULL and 16-byte aligned
+ * (global scales 4-byte aligned); outputs of directions not requested may be NULL.
+ * ------------------------------------------------------------------------- */
+enum { MXQ_ROWWISE = 1u, MXQ_COLUMNWISE = 2u, MXQ_FP8_ROWWISE = 4u };
+
+typedef struct {
+    uint8_t* codes;
+    uint8_t* block_scales;
+    float*   global_scales;
+} mxq_nvfp4_out;
+
+typedef struct {
+    uint8_t* codes;
+    float*   scales;
+} mxq_fp8_out;
+
+typedef struct {
+    uint64_t        seed;
+    const uint64_t* row_offsets;   /* host [num_sections], or NULL: nearest-even row-wise */
+    const uint64_t* col_offsets;   /* host [num_sections], or NULL: nearest-even column-wise */
+} mxq_sr;
+
+/* Bytes of workspace the grouped call needs (0 when none is needed). */
+size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k,
+                                                int64_t num_sections, uint32_t flags);
+
+mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
+                                     const int64_t* split_sections, int64_t num_sections,
+                                     uint16_t rht_sign_mask, uint32_t flags, const mxq_sr* sr,
+                                     const mxq_nvfp4_out* rowwise,
+                                     const mxq_nvfp4_out* columnwise,
+                                     const mxq_fp8_out* fp8_rowwise,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXQ_H */

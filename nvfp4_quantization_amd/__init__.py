@@ -1,0 +1,244 @@
+"""mxq: MI355X-native (gfx950) block quantization of BF16 activations.
+
+A thin ctypes binding of the C ABI in include/mxq.h.  The functions here only
+marshal arguments: every step of the quantization runs in the HIP kernels of
+libmxq.so.  PyTorch supplies device memory and the current stream.  If the
+library is missing or cannot be loaded, every entry point raises; there is no
+CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libmxq.so")
+
+MXQ_ROWWISE, MXQ_COLUMNWISE, MXQ_FP8_ROWWISE = 1, 2, 4
+MXQ_MAX_SECTIONS = 256
+STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_MISALIGNED",
+          3: "MXQ_ERR_WORKSPACE_TOO_SMALL", 4: "MXQ_ERR_UNSUPPORTED", 5: "MXQ_ERR_HIP"}
+
+EXPORTED = ("mxq_status_string", "mxq_version", "mxq_quant_fp8_1x128", "mxq_hadamard_quant_fp8",
+            "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4")
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+class _NVFP4Out(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p), ("global_scales", ctypes.c_void_p)]
+
+
+class _FP8Out(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _SR(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("row_offsets", ctypes.c_void_p), ("col_offsets", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmxq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_quantization_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64
+        L.mxq_status_string.restype = ctypes.c_char_p
+        L.mxq_status_string.argtypes = [ctypes.c_int]
+        L.mxq_version.restype = ctypes.c_char_p
+        L.mxq_version.argtypes = []
+        L.mxq_quant_fp8_1x128.restype = ctypes.c_int
+        L.mxq_quant_fp8_1x128.argtypes = [p, i64, i64, i64, p, i64, p, i64, i64, p]
+        L.mxq_hadamard_quant_fp8.restype = ctypes.c_int
+        L.mxq_hadamard_quant_fp8.argtypes = [p, i64, ctypes.c_int32, p, i64, i64, p, p, p]
+        L.mxq_group_rht_quant_nvfp4_workspace_size.restype = ctypes.c_size_t
+        L.mxq_group_rht_quant_nvfp4_workspace_size.argtypes = [i64, i64, i64, ctypes.c_uint32]
+        L.mxq_group_rht_quant_nvfp4.restype = ctypes.c_int
+        L.mxq_group_rht_quant_nvfp4.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
+                                                p, p, p, p, ctypes.c_size_t, p]
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MxqError(status, what)
+
+
+def _bf16_bits(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected bfloat16 (or its 16-bit pattern), got {t.dtype}")
+
+
+def mxq_status_string(status: int) -> str:
+    return lib().mxq_status_string(status).decode()
+
+
+def mxq_version() -> str:
+    return lib().mxq_version().decode()
+
+
+# ---------------------------------------------------------------------------- FP8 1x128
+def mxq_quant_fp8_1x128(x: torch.Tensor, q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                        scale_transposed: bool = False, stream=None):
+    """FP8 E4M3 codes [m][k] (uint8) and FP32 scales ([m][k/128], or [k/128][m]
+    when scale_transposed) of a BF16 [m][k] tensor (row stride may exceed k)."""
+    x = _bf16_bits(x)
+    m, k = x.shape
+    ldx = x.stride(0) if m > 0 else k
+    if x.stride(1) != 1:
+        raise ValueError("x must be contiguous along k")
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        shape = (k // 128, m) if scale_transposed else (m, k // 128)
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    srow, sgroup = (1, m) if scale_transposed else (k // 128, 1)
+    ldq = q.stride(0) if m > 0 else k
+    _check(lib().mxq_quant_fp8_1x128(_ptr(x), m, k, ldx, _ptr(q), ldq, _ptr(scales), srow, sgroup,
+                                     _stream(stream)), "mxq_quant_fp8_1x128")
+    return q, scales
+
+
+# ---------------------------------------------------------------------------- DSA rotate + FP8
+def mxq_hadamard_quant_fp8(pe: Optional[torch.Tensor], nope: Optional[torch.Tensor],
+                           q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None, stream=None):
+    """cat[pe, nope] along the last dim -> normalized 128-point WHT -> FP8 1x128.
+    pe: [m][d_pe], nope: [m][128-d_pe] BF16 (either may be None when empty)."""
+    ref = pe if pe is not None else nope
+    m = ref.shape[0]
+    d_pe = pe.shape[1] if pe is not None else 0
+    if pe is not None:
+        pe = _bf16_bits(pe)
+    if nope is not None:
+        nope = _bf16_bits(nope)
+    if q is None:
+        q = torch.empty((m, 128), dtype=torch.uint8, device=ref.device)
+    if scales is None:
+        scales = torch.empty((m,), dtype=torch.float32, device=ref.device)
+    ld_pe = pe.stride(0) if pe is not None else 0
+    ld_nope = nope.stride(0) if nope is not None else 0
+    _check(lib().mxq_hadamard_quant_fp8(_ptr(pe), ld_pe, d_pe, _ptr(nope), ld_nope, m, _ptr(q), _ptr(scales),
+                                        _stream(stream)), "mxq_hadamard_quant_fp8")
+    return q, scales
+
+
+# ---------------------------------------------------------------------------- grouped NVFP4
+@dataclass
+class NVFP4Result:
+    row_codes: Optional[torch.Tensor] = None      # [total][k/2] uint8
+    row_scales: Optional[torch.Tensor] = None     # [total][k/16] uint8 (E4M3)
+    row_global: Optional[torch.Tensor] = None     # [S] float32
+    col_codes: Optional[torch.Tensor] = None      # flat; section s at k*R_s/2 as [k][m_s/2]
+    col_scales: Optional[torch.Tensor] = None     # flat; section s at k*R_s/16 as [k][m_s/16]
+    col_global: Optional[torch.Tensor] = None     # [S] float32
+    fp8_codes: Optional[torch.Tensor] = None      # [total][k] uint8
+    fp8_scales: Optional[torch.Tensor] = None     # [total][k/128] float32
+
+
+def mxq_group_rht_quant_nvfp4_workspace_size(total_rows: int, k: int, num_sections: int, flags: int) -> int:
+    return int(lib().mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags))
+
+
+def alloc_nvfp4_outputs(total_rows: int, k: int, num_sections: int, flags: int, device) -> NVFP4Result:
+    r = NVFP4Result()
+    u8 = dict(dtype=torch.uint8, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    if flags & MXQ_ROWWISE:
+        r.row_codes = torch.empty((total_rows, k // 2), **u8)
+        r.row_scales = torch.empty((total_rows, k // 16), **u8)
+        r.row_global = torch.empty((num_sections,), **f32)
+    if flags & MXQ_COLUMNWISE:
+        r.col_codes = torch.empty((total_rows * k // 2,), **u8)
+        r.col_scales = torch.empty((total_rows * k // 16,), **u8)
+        r.col_global = torch.empty((num_sections,), **f32)
+    if flags & MXQ_FP8_ROWWISE:
+        r.fp8_codes = torch.empty((total_rows, k), **u8)
+        r.fp8_scales = torch.empty((total_rows, k // 128), **f32)
+    return r
+
+
+def alloc_workspace(total_rows: int, k: int, num_sections: int, flags: int, device) -> torch.Tensor:
+    n = mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
+    return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
+
+
+class GroupedNVFP4:
+    """A prepared grouped call: the ctypes argument structures are built once, so
+    repeated calls (benchmarks, stream capture) only pay for the launch itself."""
+
+    def __init__(self, x: torch.Tensor, split_sections: Sequence[int], rht_sign_mask: int, flags: int,
+                 seed: Optional[int] = None, row_offsets: Optional[Sequence[int]] = None,
+                 col_offsets: Optional[Sequence[int]] = None, out: Optional[NVFP4Result] = None,
+                 workspace: Optional[torch.Tensor] = None):
+        x = _bf16_bits(x)
+        if not x.is_contiguous():
+            raise ValueError("x must be contiguous [total_rows][k]")
+        self.x = x
+        total, k = x.shape
+        S = len(split_sections)
+        self.k, self.total, self.S, self.flags, self.mask = k, total, S, flags, rht_sign_mask & 0xFFFF
+        self.sections = (ctypes.c_int64 * max(S, 1))(*[int(v) for v in split_sections])
+        self.out = out if out is not None else alloc_nvfp4_outputs(total, k, S, flags, x.device)
+        self.workspace = workspace if workspace is not None else alloc_workspace(total, k, S, flags, x.device)
+        o = self.out
+        self._row = _NVFP4Out(o.row_codes.data_ptr() if o.row_codes is not None else None,
+                              o.row_scales.data_ptr() if o.row_scales is not None else None,
+                              o.row_global.data_ptr() if o.row_global is not None else None)
+        self._col = _NVFP4Out(o.col_codes.data_ptr() if o.col_codes is not None else None,
+                              o.col_scales.data_ptr() if o.col_scales is not None else None,
+                              o.col_global.data_ptr() if o.col_global is not None else None)
+        self._fp8 = _FP8Out(o.fp8_codes.data_ptr() if o.fp8_codes is not None else None,
+                            o.fp8_scales.data_ptr() if o.fp8_scales is not None else None)
+        self._sr = None
+        if seed is not None and (row_offsets is not None or col_offsets is not None):
+            self._ro = (ctypes.c_uint64 * S)(*row_offsets) if row_offsets is not None else None
+            self._co = (ctypes.c_uint64 * S)(*col_offsets) if col_offsets is not None else None
+            self._sr = _SR(seed & ((1 << 64) - 1),
+                           ctypes.addressof(self._ro) if self._ro is not None else None,
+                           ctypes.addressof(self._co) if self._co is not None else None)
+
+    def __call__(self, stream=None) -> NVFP4Result:
+        st = lib().mxq_group_rht_quant_nvfp4(
+            _ptr(self.x), self.k, ctypes.addressof(self.sections), self.S, self.mask, self.flags,
+            ctypes.addressof(self._sr) if self._sr is not None else None,
+            ctypes.addressof(self._row), ctypes.addressof(self._col), ctypes.addressof(self._fp8),
+            _ptr(self.workspace), self.workspace.numel(), _stream(stream))
+        _check(st, "mxq_group_rht_quant_nvfp4")
+        return self.out
+
+
+def mxq_group_rht_quant_nvfp4(x: torch.Tensor, split_sections: Sequence[int], rht_sign_mask: int, flags: int,
+                              seed: Optional[int] = None, row_offsets: Optional[Sequence[int]] = None,
+                              col_offsets: Optional[Sequence[int]] = None, out: Optional[NVFP4Result] = None,
+                              workspace: Optional[torch.Tensor] = None, stream=None) -> NVFP4Result:
+    """Grouped NVFP4 (row-wise; column-wise after the 16-point RHT) and optional
+    FP8 1x128 row-wise outputs of a BF16 [total_rows][k] tensor."""
+    return GroupedNVFP4(x, split_sections, rht_sign_mask, flags, seed, row_offsets, col_offsets, out,
+                        workspace)(stream)

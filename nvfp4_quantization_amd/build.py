@@ -1,0 +1,77 @@
+"""Build libmxq.so (the HIP kernels and the C ABI of include/mxq.h) for gfx950.
+
+    python -m nvfp4_quantization_amd.build        # or: python nvfp4_quantization_amd/build.py
+
+Compiled in-tree with hipcc; always rebuilds.  Flags:
+  -ffp-contract=off   no FMA contraction: every a*b+c in the sources rounds twice
+                      unless written as an explicit fma (the kernels are bit-exact)
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                      no packed FP32 instructions (v_pk_add/mul/fma_f32)
+FP32 denormals are kept and FP32 division is correctly rounded (hipcc defaults).
+"""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "_build")
+LIB = os.path.join(OUT, "libmxq.so")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["mxq_fp8.hip", "mxq_nvfp4.hip"]
+HOST_SOURCES = ["mxq_api.cpp"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Werror",
+          "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-munsafe-fp-atomics"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the mxq HIP library cannot be built")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False, save_temps: bool = False) -> str:
+    os.makedirs(OUT, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(OUT, src + ".o")
+        cmd = [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
+        if save_temps:
+            cmd += ["-save-temps=obj"]
+        jobs.append(cmd)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(OUT, src + ".o")
+        jobs.append([cc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv, save_temps="--save-temps" in sys.argv))

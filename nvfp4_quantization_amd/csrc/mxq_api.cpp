@@ -1,0 +1,192 @@
+// mxq_api.cpp -- the C ABI of include/mxq.h: argument checks, launch planning
+// and kernel launches.  Host code only; nothing here allocates, synchronizes,
+// memsets or reads the environment (TransformerEngine PR #2564: the per-call
+// allocation of a 4-byte scheduler workspace was the whole NVFP4 regression;
+// PR #2555 review: no per-call getenv on the quantize path).
+#include "mxq.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstring>
+
+#include "mxq_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxGridThreads = 0xFFFFFFFFll;    // 1-D grids only; threads per launch < 2^32
+constexpr int64_t kMaxRows = (1ll << 31) - 128;
+constexpr int64_t kMaxElems = 1ll << 40;
+constexpr int64_t kChunkRows = mxq::kChunkTiles * mxq::kTileRows;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxq_status_string(mxq_status s) {
+    switch (s) {
+        case MXQ_OK: return "MXQ_OK";
+        case MXQ_ERR_INVALID_ARGUMENT: return "MXQ_ERR_INVALID_ARGUMENT";
+        case MXQ_ERR_MISALIGNED: return "MXQ_ERR_MISALIGNED";
+        case MXQ_ERR_WORKSPACE_TOO_SMALL: return "MXQ_ERR_WORKSPACE_TOO_SMALL";
+        case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
+        case MXQ_ERR_HIP: return "MXQ_ERR_HIP";
+    }
+    return "MXQ_ERR_UNKNOWN";
+}
+
+const char* mxq_version(void) { return "mxq 0.1.0 gfx950"; }
+
+mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int64_t ldx,
+                               uint8_t* q_e4m3, int64_t ldq,
+                               float* scales, int64_t scale_stride_row, int64_t scale_stride_group,
+                               void* stream) {
+    if (m < 0 || k <= 0 || ldx < k || ldq < k || scale_stride_row < 0 || scale_stride_group < 0)
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (k % 128 != 0 || ldx % 8 != 0 || ldq % 16 != 0) return MXQ_ERR_MISALIGNED;
+    if (m == 0) return MXQ_OK;
+    if (!x_bf16 || !q_e4m3 || !scales) return MXQ_ERR_INVALID_ARGUMENT;
+    if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4)) return MXQ_ERR_MISALIGNED;
+    if (m > kMaxRows || m * k >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    const int64_t blocks = ceil_div(m * (k / 128), 32);
+    if (blocks * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+    mxq::Fp8Args a{x_bf16, q_e4m3, scales, m, k, ldx, ldq, scale_stride_row, scale_stride_group};
+    return mxq::launch_quant_fp8_1x128(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                  const uint16_t* nope, int64_t ld_nope, int64_t m,
+                                  uint8_t* q_e4m3, float* scales, void* stream) {
+    if (m < 0 || d_pe < 0 || d_pe > 128) return MXQ_ERR_INVALID_ARGUMENT;
+    if (d_pe % 8 != 0) return MXQ_ERR_MISALIGNED;
+    if (d_pe > 0 && ld_pe < d_pe) return MXQ_ERR_INVALID_ARGUMENT;
+    if (d_pe < 128 && ld_nope < 128 - d_pe) return MXQ_ERR_INVALID_ARGUMENT;
+    if ((d_pe > 0 && ld_pe % 8 != 0) || (d_pe < 128 && ld_nope % 8 != 0)) return MXQ_ERR_MISALIGNED;
+    if (m == 0) return MXQ_OK;
+    if ((d_pe > 0 && !pe) || (d_pe < 128 && !nope) || !q_e4m3 || !scales) return MXQ_ERR_INVALID_ARGUMENT;
+    if ((d_pe > 0 && !aligned(pe, 16)) || (d_pe < 128 && !aligned(nope, 16)) || !aligned(q_e4m3, 16) ||
+        !aligned(scales, 4))
+        return MXQ_ERR_MISALIGNED;
+    if (m > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    if (ceil_div(m, 64) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+    mxq::DsaArgs a{pe, nope, q_e4m3, scales, ld_pe, ld_nope, m, d_pe};
+    return mxq::launch_hadamard_quant_fp8(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k, int64_t num_sections,
+                                                uint32_t flags) {
+    if (total_rows < 0 || k <= 0 || num_sections <= 0) return 0;
+    if (!(flags & (MXQ_ROWWISE | MXQ_COLUMNWISE))) return 0;
+    // phase-A work-groups: sum over sections of ceil(m_s / 512) * (k / 128)
+    // <= (total_rows / 512 + num_sections) * (k / 128); 2 floats each.
+    const int64_t chunks = (total_rows / kChunkRows + num_sections) * ceil_div(k, 128);
+    const int64_t bytes = chunks * 8;
+    return (size_t)((bytes + 255) / 256 * 256);
+}
+
+mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
+                                     const int64_t* split_sections, int64_t num_sections,
+                                     uint16_t rht_sign_mask, uint32_t flags, const mxq_sr* sr,
+                                     const mxq_nvfp4_out* rowwise, const mxq_nvfp4_out* columnwise,
+                                     const mxq_fp8_out* fp8_rowwise,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    // ---- checks (nothing is enqueued before all of them pass)
+    if (k <= 0 || !split_sections || num_sections < 1) return MXQ_ERR_INVALID_ARGUMENT;
+    if (num_sections > MXQ_MAX_SECTIONS) return MXQ_ERR_UNSUPPORTED;
+    if (flags == 0 || (flags & ~(uint32_t)(MXQ_ROWWISE | MXQ_COLUMNWISE | MXQ_FP8_ROWWISE)))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (k % 128 != 0) return MXQ_ERR_MISALIGNED;
+    int64_t total_rows = 0;
+    for (int64_t s = 0; s < num_sections; ++s) {
+        const int64_t ms = split_sections[s];
+        if (ms < 0) return MXQ_ERR_INVALID_ARGUMENT;
+        if (ms % 128 != 0) return MXQ_ERR_MISALIGNED;
+        total_rows += ms;
+        if (total_rows > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    }
+    if (total_rows * k >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    const bool row = flags & MXQ_ROWWISE, col = flags & MXQ_COLUMNWISE, fp8 = flags & MXQ_FP8_ROWWISE;
+    if (row && (!rowwise || !rowwise->global_scales || (total_rows > 0 && (!rowwise->codes || !rowwise->block_scales))))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (col && (!columnwise || !columnwise->global_scales ||
+                (total_rows > 0 && (!columnwise->codes || !columnwise->block_scales))))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (fp8 && total_rows > 0 && (!fp8_rowwise || !fp8_rowwise->codes || !fp8_rowwise->scales))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (total_rows > 0 && !x_bf16) return MXQ_ERR_INVALID_ARGUMENT;
+    if (x_bf16 && !aligned(x_bf16, 16)) return MXQ_ERR_MISALIGNED;
+    if (row && (!aligned(rowwise->codes, 16) || !aligned(rowwise->block_scales, 16) ||
+                !aligned(rowwise->global_scales, 4)))
+        return MXQ_ERR_MISALIGNED;
+    if (col && (!aligned(columnwise->codes, 16) || !aligned(columnwise->block_scales, 16) ||
+                !aligned(columnwise->global_scales, 4)))
+        return MXQ_ERR_MISALIGNED;
+    if (fp8 && total_rows > 0 && (!aligned(fp8_rowwise->codes, 16) || !aligned(fp8_rowwise->scales, 4)))
+        return MXQ_ERR_MISALIGNED;
+    const bool sr_row = row && sr && sr->row_offsets;
+    const bool sr_col = col && sr && sr->col_offsets;
+    const size_t need = mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags);
+    if (need > 0) {
+        if (!workspace) return MXQ_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < need) return MXQ_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 256)) return MXQ_ERR_MISALIGNED;
+    }
+    const int64_t n_ct = k / 128;
+    if ((total_rows / 128) * n_ct * 64 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+
+    // ---- launch groups of up to kGroupSections sections
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int64_t row0 = 0;
+    for (int64_t s0 = 0; s0 < num_sections; s0 += mxq::kGroupSections) {
+        const int ns = (int)((num_sections - s0) < mxq::kGroupSections ? (num_sections - s0) : mxq::kGroupSections);
+        mxq::Nvfp4Group g;
+        std::memset(&g, 0, sizeof(g));
+        g.x = x_bf16 ? x_bf16 + row0 * k : nullptr;
+        g.k = k;
+        if (row) {
+            g.row_codes = rowwise->codes ? rowwise->codes + row0 * (k / 2) : nullptr;
+            g.row_scales = rowwise->block_scales ? rowwise->block_scales + row0 * (k / 16) : nullptr;
+            g.row_global = rowwise->global_scales + s0;
+        }
+        if (col) {
+            g.col_codes = columnwise->codes ? columnwise->codes + row0 * k / 2 : nullptr;
+            g.col_scales = columnwise->block_scales ? columnwise->block_scales + row0 * k / 16 : nullptr;
+            g.col_global = columnwise->global_scales + s0;
+        }
+        if (fp8 && total_rows > 0) {
+            g.fp8_codes = fp8_rowwise->codes + row0 * k;
+            g.fp8_scales = fp8_rowwise->scales + row0 * (k / 128);
+        }
+        g.partials = static_cast<float*>(workspace);
+        g.seed = sr ? sr->seed : 0;
+        g.flags = flags;
+        g.sign_mask = rht_sign_mask;
+        g.sr_row = sr_row ? 1u : 0u;
+        g.sr_col = sr_col ? 1u : 0u;
+        g.num_sections = ns;
+        g.n_ctiles = (int32_t)n_ct;
+        int64_t tt = 0, chunks = 0, rows_group = 0;
+        for (int i = 0; i < ns; ++i) {
+            const int64_t ms = split_sections[s0 + i];
+            g.tt_start[i] = (int32_t)tt;
+            g.chunk_start[i] = (int32_t)chunks;
+            tt += ms / 128;
+            chunks += ceil_div(ms, kChunkRows) * n_ct;
+            rows_group += ms;
+            g.row_off[i] = sr_row ? sr->row_offsets[s0 + i] : 0;
+            g.col_off[i] = sr_col ? sr->col_offsets[s0 + i] : 0;
+        }
+        g.tt_start[ns] = (int32_t)tt;
+        g.chunk_start[ns] = (int32_t)chunks;
+        g.total_tiles = (int32_t)(tt * n_ct);
+        g.total_chunks = (int32_t)chunks;
+        if (mxq::launch_nvfp4_group(g, st) != hipSuccess) return MXQ_ERR_HIP;
+        row0 += rows_group;
+    }
+    return MXQ_OK;
+}
+
+}  // extern "C"

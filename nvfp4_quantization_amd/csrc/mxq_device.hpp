@@ -1,0 +1,147 @@
+// mxq_device.hpp -- device-side building blocks shared by the mxq HIP kernels
+// (gfx950 / CDNA4, wave64).
+//
+// Every helper is exact with respect to IEEE binary32 arithmetic with one
+// rounding per operation:
+//  * BF16 -> FP32 widening is a 16-bit shift (exact).
+//  * div_rn(x, d, y) returns fl(x / d) given y = fl(1 / d): q0 = fl(x*y) is within
+//    one ulp, the FMA residual r = x - q0*d is exact, and fl(q0 + r*y) is the
+//    correctly rounded quotient (Markstein's correction step).  The identity was
+//    checked exhaustively for every BF16 significand x against every FP32
+//    significand d, and for every numerator of the form fl(a * F(1/6)) with a a
+//    BF16 value, which are the only numerators the kernels divide.
+//  * The E4M3 / E2M1 / BF16 conversions use gfx950's hardware conversions.  Over
+//    all 2^32 FP32 inputs they equal nearest-even with saturation for every
+//    finite input below 464 (E4M3) and every non-NaN input (E2M1, BF16); the
+//    kernels never pass a NaN or a value >= 464 to the E4M3 conversion except on
+//    the NaN path, which rewrites the result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// FP32 constants, each the binary32 value nearest to the real number named.
+__device__ __forceinline__ float k_floor() { return __builtin_bit_cast(float, 0x2EDBE6FFu); }      // 1e-10
+__device__ __forceinline__ float k_inv448() { return __builtin_bit_cast(float, 0x3B124925u); }     // 1/448
+__device__ __forceinline__ float k_inv2688() { return __builtin_bit_cast(float, 0x39C30C31u); }    // 1/2688
+__device__ __forceinline__ float k_inv6() { return __builtin_bit_cast(float, 0x3E2AAAABu); }       // 1/6
+__device__ __forceinline__ float k_inv_sqrt128() { return __builtin_bit_cast(float, 0x3DB504F3u); } // 1/sqrt(128)
+
+__device__ __forceinline__ float lo_bf16(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }
+
+// Round two floats to BF16 (nearest-even) and pack them: a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Running maximum of |BF16| bit patterns over packed pairs (v_pk_max_u16).
+// A result above 0x7F80 means a NaN was seen.
+__device__ __forceinline__ uint32_t absmax_pk(uint32_t acc, uint32_t p) {
+    u16x2 a = __builtin_bit_cast(u16x2, acc);
+    u16x2 b = __builtin_bit_cast(u16x2, p & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+__device__ __forceinline__ uint32_t fold_pk(uint32_t acc) {
+    uint32_t lo = acc & 0xFFFFu, hi = acc >> 16;
+    return lo > hi ? lo : hi;
+}
+// |BF16| bit pattern -> FP32 value (exact).
+__device__ __forceinline__ float bf16_mag(uint32_t m) { return __builtin_bit_cast(float, m << 16); }
+
+// max |v| over the non-NaN BF16 values of packed pairs (the slow path after a
+// NaN was seen).
+__device__ __forceinline__ uint32_t absmax_pk_nonan(uint32_t acc, uint32_t p) {
+    uint32_t lo = p & 0x7FFFu, hi = (p >> 16) & 0x7FFFu;
+    if (lo <= 0x7F80u && lo > acc) acc = lo;
+    if (hi <= 0x7F80u && hi > acc) acc = hi;
+    return acc;
+}
+
+// fl(x / d) given y = fl(1 / d)  (see the header comment).  The residual is
+// formed as q0*d - x and subtracted, so that x = -0 keeps its sign: -0 * y = -0,
+// (-0)*d - (-0) = +0, and -0 - (+0)*y = -0 (the other sign order would give +0).
+__device__ __forceinline__ float div_rn(float x, float d, float y) {
+    float q0 = x * y;
+    float rn = __builtin_fmaf(q0, d, -x);
+    return __builtin_fmaf(-rn, y, q0);
+}
+
+// E4M3 code (low byte) of a finite v with |v| < 464; nearest-even.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFFu;
+}
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+    return __builtin_amdgcn_cvt_f32_fp8(code, 0);
+}
+// Four E4M3 codes packed into a dword, a in the lowest byte.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Two E2M1 codes (nearest-even, saturating at 6) written into byte `sel` of w:
+// a in the low nibble, b in the high nibble.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, SEL);
+}
+
+// Stochastic E2M1 rounding with 8 random bits r: grid spacing D = 0.5 / 1 / 2
+// below 2 / 4 / 6; with u = |q| / D = k + f the value rounds up iff
+// floor(256 f) + r >= 256; |q| >= 6 saturates.  Returns the 4-bit code.
+__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t r) {
+    uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 28) & 8u;
+    float a = __builtin_fabsf(q);
+    float inv_step = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+    uint32_t base = a < 2.0f ? 0u : (a < 4.0f ? 2u : 4u);
+    float u = a * inv_step;                       // exact (power-of-two factor)
+    float k = __builtin_floorf(u);
+    uint32_t F = (uint32_t)((u - k) * 256.0f);    // exact, in [0, 255]
+    uint32_t code = (uint32_t)k + base + ((F + r) >= 256u ? 1u : 0u);
+    code = a < 6.0f ? code : 7u;
+    return sign | code;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).
+struct u32x4 { uint32_t x, y, z, w; };
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        u32x4 n;
+        n.x = hi1 ^ c.y ^ k0;
+        n.y = lo1;
+        n.z = hi0 ^ c.w ^ k1;
+        n.w = lo0;
+        c = n;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Random byte t (0..15) of a block's Philox output.
+__device__ __forceinline__ uint32_t rbyte(const u32x4& w, int t) {
+    uint32_t word = (t >> 2) == 0 ? w.x : (t >> 2) == 1 ? w.y : (t >> 2) == 2 ? w.z : w.w;
+    return (word >> (8 * (t & 3))) & 0xFFu;
+}
+
+// Cross-lane helpers (wave64).
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m) {
+    return (uint32_t)__shfl_xor((int)v, m, 64);
+}
+__device__ __forceinline__ float shfl_xor_f32(float v, int m) {
+    return __shfl_xor(v, m, 64);
+}
+
+}  // namespace mxq

@@ -126,6 +126,8 @@ def _sections_from_cuts(units: int, cuts: list, unit_rows: int) -> list:
 
 def split_distinct(rng: Rng, units: int, parts: int, unit_rows: int = 128) -> list:
     """`parts` non-empty sections: parts-1 distinct cut points in 1..units-1."""
+    if not 1 <= parts <= units:
+        raise ValueError(f"cannot cut {units} units into {parts} non-empty sections")
     return _sections_from_cuts(units, rng.sample_distinct(1, units - 1, parts - 1), unit_rows)
 
 

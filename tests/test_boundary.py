@@ -1,0 +1,135 @@
+"""The C ABI of include/mxq.h on the host: the library loads, exports every
+declared symbol, and rejects bad arguments before anything is enqueued (so these
+run without a GPU).  Error classes follow the pages' interface lessons: split
+sections must be multiples of 128 (TransformerEngine PR #2555, cast.cpp comment),
+an unsupported request is an error rather than a fallback (onnxruntime PR #33644,
+Description), and the workspace is the caller's, sized by a query (TransformerEngine
+PR #2564, review thread)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_quantization_amd as mxq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, MISALIGNED, WS_SMALL, UNSUPPORTED, HIP = range(6)
+A = 1 << 20          # a fake, 16-byte aligned device address: never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mxq.LIB_PATH):
+        pytest.skip("libmxq.so not built")
+    return mxq.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mxq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|mxq_status|size_t)\s+(mxq_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(mxq.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in mxq.STATUS.items():
+        assert mxq.mxq_status_string(code) == name
+    assert "gfx950" in mxq.mxq_version()
+
+
+def fp8(L, x=A, m=4, k=256, ldx=256, q=A, ldq=256, s=A, sr=2, sg=1):
+    return L.mxq_quant_fp8_1x128(x, m, k, ldx, q, ldq, s, sr, sg, None)
+
+
+def test_fp8_argument_errors(L):
+    assert fp8(L, k=200, ldx=200, ldq=208) == MISALIGNED
+    assert fp8(L, m=-1) == INVALID
+    assert fp8(L, ldx=128) == INVALID
+    assert fp8(L, x=None) == INVALID
+    assert fp8(L, q=None) == INVALID
+    assert fp8(L, s=None) == INVALID
+    assert fp8(L, x=A + 8) == MISALIGNED
+    assert fp8(L, s=A + 2) == MISALIGNED
+    assert fp8(L, ldq=264) == MISALIGNED
+    assert fp8(L, m=0, x=None, q=None, s=None) == OK      # empty call: nothing to do
+    assert fp8(L, m=1 << 31) == UNSUPPORTED
+
+
+def dsa(L, pe=A, ld_pe=64, d_pe=64, nope=A, ld_nope=64, m=8, q=A, s=A):
+    return L.mxq_hadamard_quant_fp8(pe, ld_pe, d_pe, nope, ld_nope, m, q, s, None)
+
+
+def test_dsa_argument_errors(L):
+    assert dsa(L, d_pe=60, ld_pe=60, ld_nope=68) == MISALIGNED
+    assert dsa(L, d_pe=129) == INVALID
+    assert dsa(L, ld_pe=32) == INVALID
+    assert dsa(L, pe=None) == INVALID
+    assert dsa(L, nope=None) == INVALID
+    assert dsa(L, q=A + 4) == MISALIGNED
+    assert dsa(L, m=0) == OK
+    assert dsa(L, m=-3) == INVALID
+
+
+def grouped(L, x=A, k=256, sections=(128, 256), mask=0, flags=3, sr=None, row=True, col=True, f8=True,
+            ws=A, ws_bytes=None, row_ptrs=(A, A, A), col_ptrs=(A, A, A), fp8_ptrs=(A, A)):
+    S = len(sections)
+    arr = (ctypes.c_int64 * max(S, 1))(*sections)
+    r = mxq._NVFP4Out(*row_ptrs)
+    c = mxq._NVFP4Out(*col_ptrs)
+    f = mxq._FP8Out(*fp8_ptrs)
+    if ws_bytes is None:
+        ws_bytes = 1 << 30
+    return L.mxq_group_rht_quant_nvfp4(
+        x, k, ctypes.addressof(arr), S, mask, flags, sr,
+        ctypes.addressof(r) if row else None, ctypes.addressof(c) if col else None,
+        ctypes.addressof(f) if f8 else None, ws, ws_bytes, None)
+
+
+def test_grouped_argument_errors(L):
+    assert grouped(L, sections=(128, 192)) == MISALIGNED          # split_section % 128 != 0
+    assert grouped(L, sections=(64,)) == MISALIGNED
+    assert grouped(L, k=192) == MISALIGNED
+    assert grouped(L, sections=(128, -128)) == INVALID
+    assert grouped(L, sections=()) == INVALID
+    assert grouped(L, sections=(128,) * 257) == UNSUPPORTED
+    assert grouped(L, flags=0) == INVALID
+    assert grouped(L, flags=8) == INVALID
+    assert grouped(L, row=False) == INVALID                       # requested output missing
+    assert grouped(L, row_ptrs=(A, None, A)) == INVALID
+    assert grouped(L, col_ptrs=(None, A, A)) == INVALID
+    assert grouped(L, flags=7, f8=False) == INVALID
+    assert grouped(L, x=None) == INVALID
+    assert grouped(L, x=A + 2) == MISALIGNED
+    assert grouped(L, col_ptrs=(A + 8, A, A)) == MISALIGNED
+    assert grouped(L, ws=None) == INVALID
+    need = mxq.mxq_group_rht_quant_nvfp4_workspace_size(384, 256, 2, 3)
+    assert need > 0 and need % 256 == 0
+    assert grouped(L, ws_bytes=need - 1) == WS_SMALL
+    assert grouped(L, ws=A + 64) == MISALIGNED
+    assert grouped(L, sections=(1 << 31,)) == UNSUPPORTED
+
+
+def test_workspace_size_query(L):
+    q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
+    assert q(16384, 4096, 8, 4) == 0                              # FP8 only: no phase A
+    assert q(0, 4096, 8, 3) > 0
+    # covers the phase-A work-groups of any split of the rows
+    for total, k, S in [(16384, 4096, 8), (65536, 7168, 32), (128, 128, 1), (16384, 4096, 32)]:
+        chunks = (total // 512 + S) * (k // 128)
+        assert q(total, k, S, 3) >= chunks * 8
+
+
+def test_no_forbidden_calls_in_host_sources():
+    """The quantize path allocates nothing, never synchronizes and reads no
+    environment variable (TransformerEngine PR #2564 / #2555 lessons)."""
+    src = open(os.path.join(ROOT, "nvfp4_quantization_amd", "csrc", "mxq_api.cpp")).read()
+    code = re.sub(r"//.*", "", src)
+    for bad in ("hipMalloc", "hipFree", "hipMemset", "hipDeviceSynchronize", "hipStreamSynchronize",
+                "getenv", "malloc(", "new "):
+        assert bad not in code, bad

@@ -1,0 +1,77 @@
+"""Parity at the five workloads' full sizes, through the same prepared calls the
+benchmark times: every output byte is compared with the oracle, which runs its
+plain per-section / per-row-range functions on worker threads."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantization_amd as mxq
+from nvfp4_quantization_amd import synth
+from tests.gpu_util import announce, assert_same, bits16, device, host
+
+pytestmark = [pytest.mark.gpu, pytest.mark.large]
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def test_full_plain_fp8(orc):
+    dev = device()
+    announce("full size: plain FP8 1x128 256x1024")
+    w = synth.plain_fp8(device=dev)
+    q, s = mxq.mxq_quant_fp8_1x128(w.tensors["x"])
+    torch.cuda.synchronize()
+    rq, rs = orc.quant_fp8_1x128(bits16(w.tensors["x"]))
+    assert_same("codes", host(q), rq)
+    assert_same("scales", host(s), rs)
+
+
+def test_full_dsa(orc):
+    dev = device()
+    announce("full size: DSA rotate+FP8 4096 tokens x 64 heads")
+    w = synth.dsa_rotate_fp8(device=dev)
+    q, s = mxq.mxq_hadamard_quant_fp8(w.tensors["pe"], w.tensors["nope"])
+    torch.cuda.synchronize()
+    pe, nope = bits16(w.tensors["pe"]), bits16(w.tensors["nope"])
+    m = pe.shape[0]
+    step = (m + THREADS - 1) // THREADS
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(lambda r0: orc.hadamard_quant_fp8(pe[r0:r0 + step], nope[r0:r0 + step]),
+                            range(0, m, step)))
+    assert_same("codes", host(q), np.concatenate([p[0] for p in parts]))
+    assert_same("scales", host(s), np.concatenate([p[1] for p in parts]))
+
+
+def _grouped_full(orc, w, dev):
+    p = w.params
+    x = w.tensors["x"]
+    res = mxq.GroupedNVFP4(x, p["split_sections"], p["sign_mask"], p["flags"], p["seed"],
+                           p["row_offsets"], p["col_offsets"])()
+    torch.cuda.synchronize()
+    xb = bits16(x)
+    ref = orc.group_rht_quant_nvfp4(xb, p["split_sections"], p["sign_mask"], p["flags"], p["seed"] or 0,
+                                    p["row_offsets"], p["col_offsets"], threads=THREADS)
+    for name in ("row_global", "col_global", "row_scales", "col_scales", "row_codes", "col_codes",
+                 "fp8_scales", "fp8_codes"):
+        got = getattr(res, name)
+        if got is not None:
+            assert_same(name, host(got), getattr(ref, name))
+
+
+def test_full_grouped_nvfp4_rht(orc):
+    dev = device()
+    announce("full size: grouped NVFP4 RHT 16384x4096, 8 sections")
+    _grouped_full(orc, synth.grouped_nvfp4(device=dev), dev)
+
+
+def test_full_grouped_nvfp4_sr(orc):
+    dev = device()
+    announce("full size: grouped NVFP4 RHT + SR 16384x4096, 32 sections")
+    _grouped_full(orc, synth.grouped_nvfp4_sr(device=dev), dev)
+
+
+def test_full_large_moe(orc):
+    dev = device()
+    announce("full size: large MoE 65536x7168, 32 sections, NVFP4 row+col + FP8")
+    _grouped_full(orc, synth.large_moe(device=dev), dev)

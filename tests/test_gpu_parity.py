@@ -1,0 +1,341 @@
+"""GPU parity: every output byte of the HIP kernels equals the CPU oracle's on the
+same seeded inputs (bit-exact; the quantized codes and FP32 scales are integer-like
+results of a fixed FP32 arithmetic, so no tolerance applies).  Sizes span several
+tiles with ragged tails; edge cases cover NaN, subnormal, -0, all-zero and empty
+inputs.  Full-size workloads live in test_gpu_full_size.py."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantization_amd as mxq
+from nvfp4_quantization_amd import synth
+from tests.gpu_util import announce, assert_same, bits16, device, host
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_dev(a_u16, dev):
+    return torch.from_numpy(np.ascontiguousarray(a_u16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+# ============================================================== FP8 1x128
+@pytest.mark.parametrize("m,k,pad", [(256, 1024, 0), (1, 128, 0), (33, 384, 8), (300, 2048, 64)])
+def test_fp8_1x128_random(orc, m, k, pad):
+    dev = device()
+    announce(f"fp8_1x128 m={m} k={k} pad={pad}")
+    w = synth.plain_fp8(m, k + pad, seed=100 + m)
+    x = w.tensors["x"].to(dev)[:, :k]              # row stride k + pad
+    q, s = mxq.mxq_quant_fp8_1x128(x)
+    torch.cuda.synchronize()
+    rq, rs = orc.quant_fp8_1x128(bits16(x.contiguous()))
+    assert_same("codes", host(q), rq)
+    assert_same("scales", host(s), rs)
+    qt, st = mxq.mxq_quant_fp8_1x128(x, scale_transposed=True)
+    torch.cuda.synchronize()
+    assert_same("codes(T)", host(qt), rq)
+    assert_same("scales(T)", host(st), rs.T)
+
+
+def edge_matrix(m, k, seed):
+    """BF16 bit patterns with the edge cases spread over rows."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)).astype(np.float32) * np.exp2(rng.integers(-30, 30, (m, 1)))
+    b = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    if m >= 8:
+        b[0, 3] = 0x7FC0                   # quiet NaN
+        b[1, 200 % k] = 0x7F81             # signalling NaN
+        b[2, 5] = 0xFFC1                   # negative NaN
+        b[3, :] = 0                        # all-zero row
+        b[4, :16] = 0x8000                 # -0 block
+        b[5, :] = rng.integers(1, 0x80, k)          # BF16 subnormals
+        b[6, :64] = rng.integers(0x8001, 0x8080, 64)  # negative subnormals
+        b[7, :] = 0x3F80                   # all exactly 1.0 (ties and exact grid values)
+    if m >= 12:
+        b[8, 1::7] = 0x8000                # -0 inside blocks with nonzero values
+        b[9, 2::5] = 0x0000
+        b[10, :] = [0x3F40, 0x3FA0, 0x3FE0, 0x4020, 0x4060, 0x40A0, 0x3E80, 0x40C0] * (k // 8)  # E2M1 ties
+        b[11, :] = b[11, :] | 0x8000       # an all-negative row
+    return b
+
+
+def test_fp8_1x128_edges(orc):
+    dev = device()
+    announce("fp8_1x128 edges")
+    b = edge_matrix(64, 512, 7)
+    x = bf16_dev(b, dev)
+    q, s = mxq.mxq_quant_fp8_1x128(x)
+    torch.cuda.synchronize()
+    rq, rs = orc.quant_fp8_1x128(b)
+    assert_same("codes", host(q), rq)
+    assert_same("scales", host(s), rs)
+
+
+def test_fp8_1x128_guard_bytes(orc):
+    """Outputs sit inside 0xCD-filled buffers: nothing outside them is written."""
+    dev = device()
+    announce("fp8_1x128 guard bytes")
+    m, k = 40, 640
+    b = edge_matrix(m, k, 8)
+    x = bf16_dev(b, dev)
+    qbuf = torch.full((m * k + 512,), 0xCD, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((m * k // 128 + 128,), -7.0, dtype=torch.float32, device=dev)
+    q = qbuf[256:256 + m * k].view(m, k)
+    s = sbuf[64:64 + m * k // 128].view(m, k // 128)
+    mxq.mxq_quant_fp8_1x128(x, q=q, scales=s)
+    torch.cuda.synchronize()
+    qb, sb = host(qbuf), host(sbuf)
+    assert (qb[:256] == 0xCD).all() and (qb[256 + m * k:] == 0xCD).all()
+    assert (sb[:64] == -7.0).all() and (sb[64 + m * k // 128:] == -7.0).all()
+    rq, rs = orc.quant_fp8_1x128(b)
+    assert_same("codes", qb[256:256 + m * k], rq)
+
+
+def test_fp8_1x128_empty():
+    dev = device()
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    q, s = mxq.mxq_quant_fp8_1x128(x)
+    assert q.shape == (0, 256)
+
+
+# ============================================================== DSA rotate + FP8
+@pytest.mark.parametrize("tokens,heads,d_pe", [(64, 8, 64), (7, 9, 64), (32, 4, 0), (32, 4, 128), (16, 5, 8)])
+def test_dsa_random(orc, tokens, heads, d_pe):
+    dev = device()
+    announce(f"dsa tokens={tokens} heads={heads} d_pe={d_pe}")
+    w = synth.dsa_rotate_fp8(tokens=tokens, heads=heads, d_pe=d_pe, seed=200 + tokens)
+    pe = w.tensors["pe"].to(dev) if d_pe > 0 else None
+    nope = w.tensors["nope"].to(dev) if d_pe < 128 else None
+    q, s = mxq.mxq_hadamard_quant_fp8(pe, nope)
+    torch.cuda.synchronize()
+    rq, rs = orc.hadamard_quant_fp8(bits16(w.tensors["pe"]), bits16(w.tensors["nope"]))
+    assert_same("codes", host(q), rq)
+    assert_same("scales", host(s), rs)
+
+
+def test_dsa_strided_and_edges(orc):
+    dev = device()
+    announce("dsa strided + edges")
+    m = 96
+    b = edge_matrix(m, 128, 9)
+    big = np.zeros((m, 256), np.uint16)
+    big[:, :64] = b[:, :64]              # pe in a wider buffer (row stride 256)
+    big[:, 128:192] = b[:, 64:]          # nope further along the same rows
+    t = bf16_dev(big, dev)
+    q, s = mxq.mxq_hadamard_quant_fp8(t[:, :64], t[:, 128:192])
+    torch.cuda.synchronize()
+    rq, rs = orc.hadamard_quant_fp8(b[:, :64], b[:, 64:])
+    assert_same("codes", host(q), rq)
+    assert_same("scales", host(s), rs)
+
+
+# ============================================================== grouped NVFP4
+def compare_grouped(orc, x_dev, sections, mask, flags, seed=None, ro=None, co=None, out=None, threads=8):
+    res = mxq.mxq_group_rht_quant_nvfp4(x_dev, sections, mask, flags, seed, ro, co, out=out)
+    torch.cuda.synchronize()
+    ref = orc.group_rht_quant_nvfp4(bits16(x_dev), sections, mask, flags, seed or 0, ro, co, threads=threads)
+    if flags & 1:
+        assert_same("row_global", host(res.row_global), ref.row_global)
+        assert_same("row_scales", host(res.row_scales), ref.row_scales)
+        assert_same("row_codes", host(res.row_codes), ref.row_codes)
+    if flags & 2:
+        assert_same("col_global", host(res.col_global), ref.col_global)
+        assert_same("col_scales", host(res.col_scales), ref.col_scales)
+        assert_same("col_codes", host(res.col_codes), ref.col_codes)
+    if flags & 4:
+        assert_same("fp8_scales", host(res.fp8_scales), ref.fp8_scales)
+        assert_same("fp8_codes", host(res.fp8_codes), ref.fp8_codes)
+    return res, ref
+
+
+@pytest.mark.parametrize("flags", [3, 1, 2, 7, 4, 5, 6])
+def test_grouped_rne_small(orc, flags):
+    dev = device()
+    announce(f"grouped rne small flags={flags}")
+    w = synth.grouped_nvfp4(total_rows=1280, k=640, parts=4, seed=31)
+    compare_grouped(orc, w.tensors["x"].to(dev), w.params["split_sections"], w.params["sign_mask"], flags)
+
+
+@pytest.mark.parametrize("mask", [0x0000, 0xFFFF, 0x8001, 0x5A3C])
+def test_grouped_sign_masks(orc, mask):
+    dev = device()
+    announce(f"grouped mask={mask:#x}")
+    w = synth.grouped_nvfp4(total_rows=512, k=256, parts=3, seed=32)
+    compare_grouped(orc, w.tensors["x"].to(dev), w.params["split_sections"], mask, 3)
+
+
+def test_grouped_sr_small(orc):
+    dev = device()
+    announce("grouped sr small")
+    w = synth.grouped_nvfp4_sr(total_rows=1024, k=384, parts=12, forced_empty=3, seed=33)
+    p = w.params
+    compare_grouped(orc, w.tensors["x"].to(dev), p["split_sections"], p["sign_mask"], 3, p["seed"],
+                    p["row_offsets"], p["col_offsets"])
+    # one direction stochastic, the other nearest-even
+    compare_grouped(orc, w.tensors["x"].to(dev), p["split_sections"], p["sign_mask"], 3, p["seed"],
+                    None, p["col_offsets"])
+    compare_grouped(orc, w.tensors["x"].to(dev), p["split_sections"], p["sign_mask"], 7, p["seed"],
+                    p["row_offsets"], None)
+
+
+def test_grouped_large_moe_recipe_small(orc):
+    dev = device()
+    announce("grouped large-moe recipe at small size")
+    w = synth.large_moe(total_rows=2048, k=896, parts=12, forced_empty=3, seed=34)
+    compare_grouped(orc, w.tensors["x"].to(dev), w.params["split_sections"], w.params["sign_mask"], 7)
+
+
+def test_grouped_edges(orc):
+    dev = device()
+    announce("grouped edges")
+    b = edge_matrix(384, 256, 10)
+    b[100:116, 40] = 0x7FC0            # NaN in a column block
+    b[200:216, :] = 0                   # a zero 16-row band
+    x = bf16_dev(b, dev)
+    compare_grouped(orc, x, [128, 256], 0xA5A5, 7)
+    compare_grouped(orc, x, [384], 0x0F0F, 3, seed=5, ro=[11], co=[12])
+
+
+@pytest.mark.parametrize("sections", [[128], [0, 0, 256, 0], [128] * 9, [0] * 40 + [256] + [0] * 30,
+                                      [128, 0] * 70 + [256] * 10, [0, 0, 0]])
+def test_grouped_section_shapes(orc, sections):
+    """One section, all-empty-but-one, many 128-row sections, more than one launch
+    group (> 64 sections), and an all-empty call (only the floor scales are written)."""
+    dev = device()
+    total = sum(sections)
+    announce(f"grouped sections n={len(sections)} total={total}")
+    k = 256
+    w = synth.grouped_nvfp4(total_rows=max(total, 128), k=k, parts=1, seed=35)
+    x = w.tensors["x"][:total].contiguous().to(dev)
+    compare_grouped(orc, x, sections, 0x1357, 7)
+
+
+def test_grouped_max_sections(orc):
+    dev = device()
+    announce("grouped 256 sections")
+    rng = np.random.default_rng(36)
+    sections = [int(v) * 128 for v in rng.integers(0, 3, 256)]
+    total = sum(sections)
+    w = synth.grouped_nvfp4(total_rows=total, k=128, parts=1, seed=36)
+    compare_grouped(orc, w.tensors["x"].to(dev), sections, 0xBEEF, 3, seed=9,
+                    ro=list(range(256)), co=list(range(1000, 1256)))
+
+
+def test_grouped_guard_bytes(orc):
+    dev = device()
+    announce("grouped guard bytes")
+    sections, k, flags = [256, 0, 128], 384, 7
+    total, S = sum(sections), len(sections)
+    w = synth.grouped_nvfp4(total_rows=total, k=k, parts=1, seed=37)
+    x = w.tensors["x"].to(dev)
+    G = 4096
+    sizes = dict(row_codes=total * k // 2, row_scales=total * k // 16, col_codes=total * k // 2,
+                 col_scales=total * k // 16, fp8_codes=total * k)
+    bufs, out = {}, mxq.NVFP4Result()
+    for name, n in sizes.items():
+        bufs[name] = torch.full((n + 2 * G,), 0xCD, dtype=torch.uint8, device=dev)
+        setattr(out, name, bufs[name][G:G + n])
+    for name, n in dict(row_global=S, col_global=S, fp8_scales=total * k // 128).items():
+        bufs[name] = torch.full((n + 2 * 64,), -3.0, dtype=torch.float32, device=dev)
+        setattr(out, name, bufs[name][64:64 + n])
+    out.row_codes = out.row_codes.view(total, k // 2)
+    out.row_scales = out.row_scales.view(total, k // 16)
+    out.fp8_codes = out.fp8_codes.view(total, k)
+    out.fp8_scales = out.fp8_scales.view(total, k // 128)
+    compare_grouped(orc, x, sections, 0x2222, flags, out=out)
+    for name, t in bufs.items():
+        h = host(t)
+        pad = G if h.dtype == np.uint8 else 64
+        fill = 0xCD if h.dtype == np.uint8 else -3.0
+        assert (h[:pad] == fill).all() and (h[-pad:] == fill).all(), name
+
+
+def test_grouped_run_twice_identical(orc):
+    dev = device()
+    announce("grouped determinism")
+    w = synth.grouped_nvfp4_sr(total_rows=640, k=256, parts=5, forced_empty=1, seed=38)
+    p = w.params
+    x = w.tensors["x"].to(dev)
+    call = mxq.GroupedNVFP4(x, p["split_sections"], p["sign_mask"], 7, p["seed"], p["row_offsets"],
+                            p["col_offsets"])
+    a = {k: host(v).copy() for k, v in vars(call()).items() if v is not None}
+    torch.cuda.synchronize()
+    b = {k: host(v) for k, v in vars(call()).items() if v is not None}
+    for name in a:
+        assert_same(name, b[name], a[name])
+
+
+def test_grouped_graph_capture_replays(orc):
+    """The call is stream-capturable (no allocation, no memset, no sync) and every
+    replay reproduces the eager result."""
+    dev = device()
+    announce("grouped hipGraph capture")
+    w = synth.grouped_nvfp4(total_rows=768, k=512, parts=3, seed=39)
+    x = w.tensors["x"].to(dev)
+    call = mxq.GroupedNVFP4(x, w.params["split_sections"], w.params["sign_mask"], 7)
+    eager = {k: host(v).copy() for k, v in vars(call()).items() if v is not None}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(stream=s)
+    for rep in range(3):
+        for v in vars(call.out).values():
+            if v is not None:
+                v.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, v in vars(call.out).items():
+            if v is not None:
+                assert_same(f"replay{rep}:{name}", host(v), eager[name])
+
+
+# ============================================================== Philox vs rocRAND
+def test_philox_matches_rocrand(orc):
+    """The Philox4x32-10 of the oracle (and so of the kernels, which match it
+    byte for byte under stochastic rounding) against rocRAND's generator, run
+    (not read) on the GPU: output word n is word n%4 of the block with counter n/4."""
+    dev = device()
+    announce("philox vs rocRAND")
+    try:
+        L = ctypes.CDLL("librocrand.so")
+    except OSError:
+        L = ctypes.CDLL("/opt/rocm/lib/librocrand.so")
+    gen = ctypes.c_void_p()
+    assert L.rocrand_create_generator(ctypes.byref(gen), 404) == 0       # ROCRAND_RNG_PSEUDO_PHILOX4_32_10
+    seed = 0x0123456789ABCDEF
+    L.rocrand_set_seed.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong]
+    assert L.rocrand_set_seed(gen, seed) == 0
+    n = 4096
+    out = torch.zeros(n, dtype=torch.int32, device=dev)
+    L.rocrand_generate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    assert L.rocrand_generate(gen, ctypes.c_void_p(out.data_ptr()), n) == 0
+    torch.cuda.synchronize()
+    got = host(out).view(np.uint32)
+    L.rocrand_destroy_generator(gen)
+    want = np.concatenate([orc.philox4x32_10([i, 0, 0, 0], [seed & 0xFFFFFFFF, seed >> 32])
+                           for i in range(n // 4)])
+    assert_same("philox stream", got, want)
+
+
+def test_grouped_hand_case_b9(orc):
+    """A section whose amax is 10.5 (tensor scale 2^-8) holding the hand-worked
+    block [6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, -.25, -.75, 5.5, bf16(.1), -0, 1,
+    -6, 4.5]: every E2M1 tie, saturation and a -0 element (codes 7,0,2,2,4,4,6,6,
+    8,A,7,0,8,2,F,6)."""
+    dev = device()
+    announce("grouped hand case B9")
+    vals = [6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, -.25, -.75, 5.5, 0.1, -0.0, 1, -6, 4.5]
+    x = np.zeros((128, 128), np.float32)
+    x[0, :16] = vals
+    x[1, 16] = 10.5
+    x[2, :16] = 6.25
+    x[3, 32] = 2.0 ** -20
+    b = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    res, ref = compare_grouped(orc, bf16_dev(b, dev), [128], 0, 1)
+    codes = host(res.row_codes)[0, :8].tolist()
+    assert codes == [0x07, 0x22, 0x44, 0x66, 0xA8, 0x07, 0x28, 0x6F]
+    assert host(res.row_global)[0] == np.float32(2.0 ** -8)
