@@ -184,9 +184,19 @@ def alloc_nvfp4_outputs(total_rows: int, k: int, num_sections: int, flags: int, 
     return r
 
 
+WORKSPACE_ERROR_OFFSET = 8192      # byte offset of the error word in the workspace
+
+
 def alloc_workspace(total_rows: int, k: int, num_sections: int, flags: int, device) -> torch.Tensor:
     n = mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
     return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
+
+
+def workspace_ok(workspace: torch.Tensor) -> bool:
+    """After a finished call: True unless one of its waits hit the time limit."""
+    if workspace.numel() < WORKSPACE_ERROR_OFFSET + 4:
+        return True
+    return int(workspace[WORKSPACE_ERROR_OFFSET:WORKSPACE_ERROR_OFFSET + 4].view(torch.int32).item()) == 0
 
 
 class GroupedNVFP4:

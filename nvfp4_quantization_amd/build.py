@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["mxq_fp8.hip", "mxq_nvfp4.hip"]
 HOST_SOURCES = ["mxq_api.cpp"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Werror",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Werror", "-I", "/opt/rocm/include",
           "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
@@ -63,7 +63,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(OUT, src + ".o")
-        jobs.append([cc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))

@@ -117,12 +117,13 @@ def test_grouped_argument_errors(L):
 
 def test_workspace_size_query(L):
     q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
-    assert q(16384, 4096, 8, 4) == 0                              # FP8 only: no phase A
-    assert q(0, 4096, 8, 3) > 0
-    # covers the phase-A work-groups of any split of the rows
-    for total, k, S in [(16384, 4096, 8), (65536, 7168, 32), (128, 128, 1), (16384, 4096, 32)]:
-        chunks = (total // 512 + S) * (k // 128)
-        assert q(total, k, S, 3) >= chunks * 8
+    assert q(16384, 4096, 8, 4) == 0                              # FP8 only: no amax pass
+    # control words of one launch group plus one 8-byte partial per 128x512 block
+    for total, k, S in [(0, 4096, 8), (16384, 4096, 8), (65536, 7168, 32), (128, 128, 1), (16384, 4096, 256)]:
+        need = q(total, k, S, 3)
+        assert need % 256 == 0
+        assert need >= 8448 + 8 * (total // 128) * -(-(k // 128) // 4)
+        assert need < 8448 + 8 * (total // 128) * (k // 128) + 512
 
 
 def test_no_forbidden_calls_in_host_sources():

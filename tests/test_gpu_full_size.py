@@ -46,9 +46,11 @@ def test_full_dsa(orc):
 def _grouped_full(orc, w, dev):
     p = w.params
     x = w.tensors["x"]
-    res = mxq.GroupedNVFP4(x, p["split_sections"], p["sign_mask"], p["flags"], p["seed"],
-                           p["row_offsets"], p["col_offsets"])()
+    call = mxq.GroupedNVFP4(x, p["split_sections"], p["sign_mask"], p["flags"], p["seed"],
+                            p["row_offsets"], p["col_offsets"])
+    res = call()
     torch.cuda.synchronize()
+    assert mxq.workspace_ok(call.workspace)
     xb = bits16(x)
     ref = orc.group_rht_quant_nvfp4(xb, p["split_sections"], p["sign_mask"], p["flags"], p["seed"] or 0,
                                     p["row_offsets"], p["col_offsets"], threads=THREADS)
