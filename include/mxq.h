@@ -153,13 +153,12 @@ mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_p
  *
  * workspace: device memory of at least
  *   mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
- *   bytes (0 when only MXQ_FP8_ROWWISE is requested; otherwise about 8 KB plus
- *   8 bytes per 128 x 512 block of x), 256-byte aligned, with no initialization
- *   needed.  It holds the per-section counters, ready flags and partial maxima
- *   through which the work-groups of one call meet; the call clears what it uses
- *   first.  The 32-bit word at byte offset 8192 is nonzero after a call whose
- *   internal wait hit its time limit (outputs then undefined; every wait is
- *   bounded, so the call still terminates).
+ *   bytes (0 when only MXQ_FP8_ROWWISE is requested; otherwise 72 KB plus 8 bytes
+ *   per 128 x 128 tile of x), 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE.
+ *   It holds per-section counters, per-tile partial maxima and per-section scale
+ *   tables through which the two kernels of a call meet; every call leaves the
+ *   counters at zero again, so a workspace is zeroed once and then reused.  Calls
+ *   that share a workspace must be ordered (same stream, or synchronized).
  *
  * Requirements: k % 128 == 0, every m_s % 128 == 0 (else MXQ_ERR_MISALIGNED, with
  * no unfused fallback); 1 <= num_sections <= MXQ_MAX_SECTIONS; total_rows <= 2^31 -

@@ -184,19 +184,22 @@ def alloc_nvfp4_outputs(total_rows: int, k: int, num_sections: int, flags: int, 
     return r
 
 
-WORKSPACE_ERROR_OFFSET = 8192      # byte offset of the error word in the workspace
+WORKSPACE_COUNTERS = 32            # per-section counters at the start of the workspace
+WORKSPACE_COUNTER_STRIDE = 256     # bytes between two counters
 
 
 def alloc_workspace(total_rows: int, k: int, num_sections: int, flags: int, device) -> torch.Tensor:
+    """Zero-filled workspace of the size the library asks for (the grouped call
+    needs its counters at zero before the first use and leaves them at zero)."""
     n = mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
-    return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
+    return torch.zeros((max(n, 256),), dtype=torch.uint8, device=device)
 
 
-def workspace_ok(workspace: torch.Tensor) -> bool:
-    """After a finished call: True unless one of its waits hit the time limit."""
-    if workspace.numel() < WORKSPACE_ERROR_OFFSET + 4:
-        return True
-    return int(workspace[WORKSPACE_ERROR_OFFSET:WORKSPACE_ERROR_OFFSET + 4].view(torch.int32).item()) == 0
+def workspace_counters_clear(workspace: torch.Tensor) -> bool:
+    """After a finished call: True when every section counter is back at zero."""
+    n = min(workspace.numel(), WORKSPACE_COUNTERS * WORKSPACE_COUNTER_STRIDE)
+    words = workspace[:n].view(torch.int32)[:: WORKSPACE_COUNTER_STRIDE // 4]
+    return bool((words == 0).all().item())
 
 
 class GroupedNVFP4:

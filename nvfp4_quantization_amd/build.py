@@ -7,6 +7,10 @@ Compiled in-tree with hipcc; always rebuilds.  Flags:
                       unless written as an explicit fma (the kernels are bit-exact)
   -Xclang -target-feature -Xclang -packed-fp32-ops
                       no packed FP32 instructions (v_pk_add/mul/fma_f32)
+  -mllvm -pragma-unroll-threshold=1000000
+                      fully unroll every '#pragma unroll' loop, however large: a
+                      kept loop would index register arrays dynamically and move
+                      them to scratch memory
 FP32 denormals are kept and FP32 division is correctly rounded (hipcc defaults).
 """
 import os
@@ -27,7 +31,7 @@ HOST_SOURCES = ["mxq_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Werror", "-I", "/opt/rocm/include",
           "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+          "-munsafe-fp-atomics", "-mllvm", "-pragma-unroll-threshold=1000000"]
 
 
 def hipcc() -> str:

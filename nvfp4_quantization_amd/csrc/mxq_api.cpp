@@ -20,6 +20,7 @@ constexpr int64_t kMaxElems = 1ll << 40;
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -79,11 +80,10 @@ size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k, i
                                                 uint32_t flags) {
     if (total_rows < 0 || k <= 0 || num_sections <= 0) return 0;
     if (!(flags & (MXQ_ROWWISE | MXQ_COLUMNWISE))) return 0;
-    // control words of one launch group, then one 8-byte partial per A item
-    // (a 128-row x 512-column block) of the largest group, bounded by all rows
-    const int64_t a_items = (total_rows / 128) * ceil_div(ceil_div(k, 128), mxq::kATiles);
-    const int64_t bytes = mxq::kCtrlBytes + 8 * a_items;
-    return (size_t)((bytes + 255) / 256 * 256);
+    // counters and scale tables of one launch group, then one 8-byte partial per
+    // 128 x 128 tile of the largest group (bounded by all rows)
+    const int64_t tiles = (total_rows / 128) * ceil_div(k, 128);
+    return (size_t)round256(mxq::kPartialsOffset + 8 * tiles);
 }
 
 mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
@@ -135,10 +135,17 @@ mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
     }
     const int64_t n_ct = k / 128;
     if ((total_rows / 128) * n_ct * 2 * 64 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
-    const bool amax = row || col;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!row && !col) {
+        // the FP8 1x128 output alone needs no tensor scale: one plain FP8 launch
+        if (total_rows == 0) return MXQ_OK;
+        if (ceil_div(total_rows * (k / 128), 32) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+        mxq::Fp8Args a{x_bf16, fp8_rowwise->codes, fp8_rowwise->scales, total_rows, k, k, k, k / 128, 1};
+        return mxq::launch_quant_fp8_1x128(a, st) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+    }
 
     // ---- launch groups of up to kGroupSections sections
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
     int64_t row0 = 0;
     for (int64_t s0 = 0; s0 < num_sections; s0 += mxq::kGroupSections) {
         const int ns = (int)((num_sections - s0) < mxq::kGroupSections ? (num_sections - s0) : mxq::kGroupSections);
@@ -160,63 +167,27 @@ mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
             g.fp8_codes = fp8_rowwise->codes + row0 * k;
             g.fp8_scales = fp8_rowwise->scales + row0 * (k / 128);
         }
-        g.ctrl = static_cast<uint32_t*>(workspace);
-        g.partials = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + mxq::kCtrlBytes);
+        g.ctrl = reinterpret_cast<uint32_t*>(ws + mxq::kCtrlOffset);
+        g.tables = reinterpret_cast<float2*>(ws + mxq::kTablesOffset);
+        g.partials = reinterpret_cast<uint64_t*>(ws + mxq::kPartialsOffset);
         g.seed = sr ? sr->seed : 0;
-        g.flags = flags;
         g.sign_mask = rht_sign_mask;
         g.sr_row = sr_row ? 1u : 0u;
         g.sr_col = sr_col ? 1u : 0u;
         g.num_sections = ns;
         g.n_ctiles = (int32_t)n_ct;
-        g.n_agroups = (int32_t)ceil_div(n_ct, mxq::kATiles);
-        int64_t tt = 0, rows_group = 0, a_parts = 0;
-        int live[mxq::kGroupSections];
-        int n_live = 0;
+        int64_t tt = 0, rows_group = 0;
         for (int i = 0; i < ns; ++i) {
             const int64_t ms = split_sections[s0 + i];
             g.tt_start[i] = (int32_t)tt;
-            g.a_start[i] = (int32_t)a_parts;
             tt += ms / 128;
-            a_parts += (ms / 128) * g.n_agroups;
             rows_group += ms;
-            if (ms > 0) live[n_live++] = i;
             g.row_off[i] = sr_row ? sr->row_offsets[s0 + i] : 0;
             g.col_off[i] = sr_col ? sr->col_offsets[s0 + i] : 0;
         }
         g.tt_start[ns] = (int32_t)tt;
-        g.a_start[ns] = (int32_t)a_parts;
-        auto items_of = [&](int i) { return (int32_t)((g.tt_start[i + 1] - g.tt_start[i]) * n_ct); };
-        auto a_items_of = [&](int i) { return (int32_t)((g.tt_start[i + 1] - g.tt_start[i]) * g.n_agroups); };
-        // rounds: every A item first (section by section), then every B item.  A B
-        // item is dispatched only after all A items; by then those of its own
-        // section have long been running, so its wait is short, and the B items'
-        // ALU work overlaps the tail of the A items' reads.
-        int nr = 0;
-        int64_t start = 0;
-        if (amax) {
-            for (int r = 0; r < n_live; ++r) {
-                mxq::Nvfp4Round& R = g.rounds[nr++];
-                R.sec_b = -1;
-                R.sec_a = live[r];
-                R.n_b = 0;
-                R.n_a = a_items_of(live[r]);
-                R.start = (int32_t)start;
-                start += R.n_a;
-            }
-        }
-        for (int r = 0; r < n_live; ++r) {
-            mxq::Nvfp4Round& R = g.rounds[nr++];
-            R.sec_b = live[r];
-            R.sec_a = -1;
-            R.n_b = items_of(live[r]);
-            R.n_a = 0;
-            R.start = (int32_t)start;
-            start += R.n_b;
-        }
-        g.num_rounds = nr;
-        g.total_items = (int32_t)start;
-        if (mxq::launch_nvfp4_group(g, st) != hipSuccess) return MXQ_ERR_HIP;
+        g.total_tiles = (int32_t)(tt * n_ct);
+        if (mxq::launch_nvfp4_group(g, flags, st) != hipSuccess) return MXQ_ERR_HIP;
         row0 += rows_group;
     }
     return MXQ_OK;

@@ -28,29 +28,16 @@ struct DsaArgs {
 hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- grouped NVFP4
-// One launch group per at most kGroupSections sections (their tables travel in the
-// kernel arguments).  A group runs two kernels on the caller's stream:
-//   reset   one work-group: clears the group's control words and writes the floor
-//           tensor scales of empty sections;
-//   fused   one wave per work-group, work items in blockIdx order:
-//     A item  (section, 128-row tile, up to kATiles 128-column tiles): max |x| and
-//             max |H16 D x| of the block, stored as a partial; the section's last A
-//             item (a counter tells which) reduces the partials, publishes the two
-//             tensor scales and raises the section's ready flag;
-//     B item  (section, 128 x 128 tile): waits for the ready flag, then writes all
-//             outputs of its tile.
-// Items are listed round by round; the host puts every A item of a section before
-// all of its B items (all A items first, then all B items).
+// One launch group per at most kGroupSections sections.  A group runs two kernels
+// on the caller's stream, one wave per 128 x 128 tile in each:
+//   amax    max |x| and max |H16 D x| of the tile into a per-tile partial; the
+//           section's last tile (a counter tells which) folds the partials into
+//           the two tensor scales, writes the section's (d, 1/d) tables and resets
+//           the counter for the next call;
+//   quant   every output of the tile.
 constexpr int kGroupSections = 32;
 constexpr int kTileRows = 128;        // token tile
-constexpr int kTileCols = 128;        // column tile (one wave)
-constexpr int kATiles = 1;            // column tiles per A item
-
-struct Nvfp4Round {
-    int32_t sec_b, sec_a;             // section of the B / A items (-1: none)
-    int32_t n_b, n_a;                 // item counts
-    int32_t start;                    // first blockIdx of the round
-};
+constexpr int kTileCols = 128;        // column tile
 
 struct Nvfp4Group {
     const uint16_t* x;                // first row of the group
@@ -63,31 +50,30 @@ struct Nvfp4Group {
     uint8_t* col_scales;
     float* row_global;                // at the group's first section
     float* col_global;
-    uint32_t* ctrl;                   // workspace: control words
-    uint64_t* partials;               // workspace: one (row, column) amax pair per A item
+    uint32_t* ctrl;                   // workspace: per-section counters
+    float2* tables;                   // workspace: per-section (d, 1/d) tables
+    uint64_t* partials;               // workspace: one (row, column) amax pair per tile
     uint64_t seed;
-    uint32_t flags;
     uint32_t sign_mask;
     uint32_t sr_row, sr_col;
     int32_t num_sections;
     int32_t n_ctiles;                 // k / 128
-    int32_t n_agroups;                // ceil(n_ctiles / kATiles)
-    int32_t num_rounds;
-    int32_t total_items;
+    int32_t total_tiles;
     int32_t tt_start[kGroupSections + 1];    // first token tile of each section (group-relative)
-    int32_t a_start[kGroupSections + 1];     // first partial of each section
-    Nvfp4Round rounds[2 * kGroupSections];
     uint64_t row_off[kGroupSections];
     uint64_t col_off[kGroupSections];
 };
-hipError_t launch_nvfp4_group(const Nvfp4Group& g, hipStream_t stream);
+hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
 
-// Workspace layout: control words of section s at word kCtrlStride * s
-// ([0] A items done, [1] ready flag, [2] row tensor scale bits, [3] column tensor
-// scale bits), each section in its own 256-byte line; the error word after them
-// (a wait that timed out sets it); then the partials.
+// Workspace layout (byte offsets):
+//   kCtrlOffset    counter of section s at word kCtrlStride * s (own 256-byte line)
+//   kTablesOffset  section s, direction dir (0 row, 1 column), scale code c:
+//                  float2 at index (s * 2 + dir) * 128 + c = (d, +-1/d) (see the kernels)
+//   kPartialsOffset  one 8-byte partial per 128 x 128 tile
 constexpr int kCtrlStride = 64;
-constexpr int kCtrlErrorWord = kGroupSections * kCtrlStride;
-constexpr int64_t kCtrlBytes = (int64_t)(kGroupSections + 1) * kCtrlStride * 4;
+constexpr int64_t kCtrlOffset = 0;
+constexpr int64_t kTablesOffset = (int64_t)kGroupSections * kCtrlStride * 4;
+constexpr int64_t kTablesBytes = (int64_t)kGroupSections * 2 * 128 * 8;
+constexpr int64_t kPartialsOffset = kTablesOffset + kTablesBytes;
 
 }  // namespace mxq

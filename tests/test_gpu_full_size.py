@@ -50,7 +50,7 @@ def _grouped_full(orc, w, dev):
                             p["row_offsets"], p["col_offsets"])
     res = call()
     torch.cuda.synchronize()
-    assert mxq.workspace_ok(call.workspace)
+    assert mxq.workspace_counters_clear(call.workspace)
     xb = bits16(x)
     ref = orc.group_rht_quant_nvfp4(xb, p["split_sections"], p["sign_mask"], p["flags"], p["seed"] or 0,
                                     p["row_offsets"], p["col_offsets"], threads=THREADS)

@@ -135,7 +135,7 @@ def compare_grouped(orc, x_dev, sections, mask, flags, seed=None, ro=None, co=No
     call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, out=out)
     res = call()
     torch.cuda.synchronize()
-    assert mxq.workspace_ok(call.workspace), "a wait in the grouped kernel timed out"
+    assert mxq.workspace_counters_clear(call.workspace), "a section counter was left nonzero"
     ref = orc.group_rht_quant_nvfp4(bits16(x_dev), sections, mask, flags, seed or 0, ro, co, threads=threads)
     if flags & 1:
         assert_same("row_global", host(res.row_global), ref.row_global)
