@@ -33,6 +33,9 @@ def parse():
                     choices=["grouped_nvfp4_rht", "grouped_nvfp4_rht_sr", "large_moe_nvfp4_fp8",
                              "dsa_rotate_fp8", "fp8_1x128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="steady-state steps only, then one 256 MiB device copy (the counter calibration "
+                         "for rocprofv3 runs); prints the JSON line without the secondary figures")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows of the workload the oracle baseline runs on (0: the whole workload, "
                          "capped at 16384 rows)")
@@ -140,6 +143,17 @@ def main():
     wall = time.perf_counter() - t0
     ms = starts[0].elapsed_time(ends[K - 1]) / K            # throughput: whole run / steps
     per = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+
+    if args.profile:
+        del calls
+        a = torch.ones(1 << 27, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)                                        # 256 MiB read + 256 MiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": True, "workload": desc, "steps": K, "ms_per_step": round(ms, 5),
+                          "copy_calibration_bytes": 2 * a.numel()}), flush=True)
+        return
 
     # secondary figures: one call after reading a 1 GiB buffer (caches hold none of
     # the input and nothing dirty), and back-to-back calls on one set (input in cache)

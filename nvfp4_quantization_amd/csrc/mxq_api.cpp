@@ -168,7 +168,7 @@ mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
             g.fp8_scales = fp8_rowwise->scales + row0 * (k / 128);
         }
         g.ctrl = reinterpret_cast<uint32_t*>(ws + mxq::kCtrlOffset);
-        g.tables = reinterpret_cast<float2*>(ws + mxq::kTablesOffset);
+        g.tables = reinterpret_cast<float4*>(ws + mxq::kTablesOffset);
         g.partials = reinterpret_cast<uint64_t*>(ws + mxq::kPartialsOffset);
         g.seed = sr ? sr->seed : 0;
         g.sign_mask = rht_sign_mask;

@@ -51,7 +51,7 @@ struct Nvfp4Group {
     float* row_global;                // at the group's first section
     float* col_global;
     uint32_t* ctrl;                   // workspace: per-section counters
-    float2* tables;                   // workspace: per-section (d, 1/d) tables
+    float4* tables;                   // workspace: per-section scale tables
     uint64_t* partials;               // workspace: one (row, column) amax pair per tile
     uint64_t seed;
     uint32_t sign_mask;
@@ -68,12 +68,12 @@ hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, hipStream_t s
 // Workspace layout (byte offsets):
 //   kCtrlOffset    counter of section s at word kCtrlStride * s (own 256-byte line)
 //   kTablesOffset  section s, direction dir (0 row, 1 column), scale code c:
-//                  float2 at index (s * 2 + dir) * 128 + c = (d, +-1/d) (see the kernels)
+//                  float4 at index (s * 2 + dir) * 128 + c = (d, 1/d, multiplier, 0)
 //   kPartialsOffset  one 8-byte partial per 128 x 128 tile
 constexpr int kCtrlStride = 64;
 constexpr int64_t kCtrlOffset = 0;
 constexpr int64_t kTablesOffset = (int64_t)kGroupSections * kCtrlStride * 4;
-constexpr int64_t kTablesBytes = (int64_t)kGroupSections * 2 * 128 * 8;
+constexpr int64_t kTablesBytes = (int64_t)kGroupSections * 2 * 128 * 16;
 constexpr int64_t kPartialsOffset = kTablesOffset + kTablesBytes;
 
 }  // namespace mxq

@@ -20,19 +20,21 @@
 //                  every requested output.
 //
 // Scale tables: for each direction and E4M3 scale code c the quantizer divides by
-// d = fl(E4M3(c) * g).  The table holds (d, y = fl(1/d)), y negated when the plain
-// product fl(u * y) would pick a different E2M1 code than fl(u / d) for some BF16
-// u.  The two quotients differ by at most about one FP32 ulp, so a BF16 u can only
-// be decided differently when u / d lies within 2^-22 (relative) of one of the
-// seven E2M1 rounding boundaries 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; BF16 values
-// are 2^-8 apart, so only the two BF16 neighbours of each boundary times d can,
-// and those fourteen are checked with the exact division.  Where a wave's blocks
-// all use codes that pass, the codes come from one multiply per element;
-// elsewhere, and always with stochastic rounding (which needs the exact quotient),
-// from the exact division.  Column values enter unscaled: BF16(x/4) = BF16(x)/4
-// and fl((u/4)/d) = fl(u/(4d)) whenever x/4 is a normal number, and where it is
-// not, both quotients are far below the smallest E2M1 step with the same sign, so
-// the column tables hold (4d, y/4) and the 1/4 costs nothing per element.
+// d = fl(E4M3(c) * g).  The table holds (d, y = fl(1/d), ym): ym is a multiplier
+// whose plain product fl(u * ym) picks the same E2M1 code as fl(u / d) for every
+// BF16 u, or negative when there is none.  fl(u * ym) and fl(u / d) differ by a
+// few FP32 ulps at most, so a BF16 u can only be decided differently when u / d
+// lies within about 2^-21 (relative) of one of the seven E2M1 rounding boundaries
+// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; BF16 values are 2^-8 apart, so only the two
+// BF16 neighbours of each boundary times d can, and those fourteen are checked
+// against the exact division for ym = y and its nearest neighbours.  The codes of
+// a block come from one multiply per element when its scale code has a
+// multiplier, else (and always with stochastic rounding, which needs the exact
+// quotient) from the exact division.  Column values enter unscaled: BF16(x/4) =
+// BF16(x)/4 and fl((u/4)/d) = fl(u/(4d)) whenever x/4 is a normal number, and
+// where it is not, both quotients are far below the smallest E2M1 step with the
+// same sign, so the column tables are built for 4d and the 1/4 costs nothing per
+// element.
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -60,9 +62,9 @@ __device__ __forceinline__ uint32_t block_code(float a, float g, float yg) {
 
 __device__ __forceinline__ uint32_t e2m1_one(float q) { return e2m1_pack2<0>(0u, q, q) & 0xFu; }
 
-// True when fl(u * y) and fl(u / d) have the same E2M1 code for every BF16 u
-// (d > 0 finite, y = fl(1/d)); see the header comment.
-__device__ bool product_rounds_like_quotient(float d, float y) {
+// True when fl(u * ym) and fl(u / d) have the same E2M1 code for every BF16 u
+// (d > 0 finite, y = fl(1/d), ym within a few ulps of y); see the header comment.
+__device__ bool product_decides_like_quotient(float d, float y, float ym) {
     const float taus[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
     bool ok = true;
 #pragma unroll
@@ -71,10 +73,23 @@ __device__ bool product_rounds_like_quotient(float d, float y) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const float u = __builtin_bit_cast(float, lo + (uint32_t)j * 0x10000u);
-            ok &= e2m1_one(u * y) == e2m1_one(div_rn(u, d, y));
+            ok &= e2m1_one(u * ym) == e2m1_one(div_rn(u, d, y));
         }
     }
     return ok;
+}
+
+// The multiplier for the product path of divisor d: fl(1/d) or a neighbour a few
+// ulps away that decides every BF16 input like the exact quotient (exact
+// quotients that fall on rounding boundaries are common, because d and the
+// boundaries are short binary numbers); negative when none does.
+__device__ float product_multiplier(float d, float y) {
+    const int deltas[7] = {0, -1, 1, -2, 2, -3, 3};
+    for (int i = 0; i < 7; ++i) {
+        const float ym = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, y) + (uint32_t)deltas[i]);
+        if (product_decides_like_quotient(d, y, ym)) return ym;
+    }
+    return -y;
 }
 
 // Running max |x| over packed BF16 pairs, NaN ignored.
@@ -172,17 +187,6 @@ __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, co
     return c;
 }
 
-// 16 codes of one block with table entry dy = (d, +-y): by product when every
-// lane of the wave may (SR off), else by division / stochastic rounding.
-template <bool SR>
-__device__ __forceinline__ uint2 encode_block(const float (&u)[16], float2 dy, const u32x4& rnd) {
-    const float d = dy.x, y = __builtin_fabsf(dy.y);
-    if (SR) return make_uint2(encode8<Enc::Sr>(u, d, y, rnd, 0), encode8<Enc::Sr>(u + 8, d, y, rnd, 8));
-    if (__ballot(dy.y < 0.0f) == 0)
-        return make_uint2(encode8<Enc::Mul>(u, d, y, rnd, 0), encode8<Enc::Mul>(u + 8, d, y, rnd, 8));
-    return make_uint2(encode8<Enc::Div>(u, d, y, rnd, 0), encode8<Enc::Div>(u + 8, d, y, rnd, 8));
-}
-
 // ---------------------------------------------------------------- amax work
 // A quarter tile: rows 32q .. 32q+31; lane (h, c) holds rows 16h .. 16h+15 of it
 // and columns 4c .. 4c+3 (one 8-byte load per row).
@@ -253,6 +257,82 @@ __device__ __forceinline__ void amax_quarter(const uint2 (&v)[16], uint32_t sign
 // 16 cc .. 16 cc + 15 as p[t][half] (8 BF16 each).
 #define P(t, i) ((i) == 0 ? p[t][0].x : (i) == 1 ? p[t][0].y : (i) == 2 ? p[t][0].z : (i) == 3 ? p[t][0].w \
                : (i) == 4 ? p[t][1].x : (i) == 5 ? p[t][1].y : (i) == 6 ? p[t][1].z : p[t][1].w)
+
+// Hide the tile's provenance from the compiler (no instruction is emitted).
+// Otherwise it reuses values computed from the tile by an earlier pass in a later
+// one, keeping hundreds of them live across the passes.
+__device__ __forceinline__ void launder(uint4 (&p)[16][2]) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(p[t][h].x), "+v"(p[t][h].y), "+v"(p[t][h].z), "+v"(p[t][h].w));
+}
+
+struct BlockOut {
+    uint2 codes;          // 16 E2M1 codes
+    uint32_t scale;       // E4M3 scale byte
+    bool unsafe;          // (Enc::Mul) the scale code needs the exact division
+};
+
+// 16 codes of one block of values u with scale code sc (nan: the block holds a NaN).
+template <Enc E>
+__device__ __forceinline__ BlockOut encode_block(const float (&u)[16], uint32_t sc, bool nan, const float4* tab,
+                                                 const u32x4& rnd) {
+    const float4 e = tab[sc & 0x7Fu];
+    const float d = e.x, y = E == Enc::Mul ? __builtin_fabsf(e.z) : e.y;
+    BlockOut o;
+    o.codes = make_uint2(encode8<E>(u, d, y, rnd, 0), encode8<E>(u + 8, d, y, rnd, 8));
+    if (nan || sc == 0u) o.codes = make_uint2(0u, 0u);
+    o.scale = nan ? 0x7Fu : sc;
+    o.unsafe = e.z < 0.0f;
+    return o;
+}
+
+// Column j of the lane: rows 16 tb .. +15 after the sign flip and the butterfly,
+// rounded to BF16 (unscaled; the column tables carry the 1/4).
+template <Enc E>
+__device__ __forceinline__ BlockOut column_block(const uint4 (&p)[16][2], int j, uint32_t sign_mask, float g_c,
+                                                 float yg_c, const float4* tab_c, const u32x4& rnd) {
+    float v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const uint32_t w = P(t, j >> 1);
+        const uint32_t neg = sign_of_row(sign_mask, t);
+        v[t] = (j & 1) ? hi_signed(w, neg) : lo_signed(w, neg);
+    }
+    butterfly16(v);
+    const bool nan = v[0] != v[0];                   // a NaN input reaches every output
+    float mx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)                      // a shallow tree, not a 16-long chain
+        mx[i] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[4 * i]), __builtin_fabsf(v[4 * i + 1])),
+                                __builtin_fmaxf(__builtin_fabsf(v[4 * i + 2]), __builtin_fabsf(v[4 * i + 3])));
+    const float m = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), __builtin_fmaxf(mx[2], mx[3]));
+    // block amax of the column values BF16(v/4) = BF16(max |v|) / 4
+    const uint32_t sc = block_code(0.25f * round_bf16(m), g_c, yg_c);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) v[t] = round_bf16(v[t]);
+    return encode_block<E>(v, sc, nan, tab_c, rnd);
+}
+
+// Row t of the lane: columns 16 cc .. +15 (one row-wise block).
+template <Enc E>
+__device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, float g_r, float yg_r,
+                                              const float4* tab_r, const u32x4& rnd, uint32_t& m_out) {
+    float u[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        u[2 * i] = lo_bf16(P(t, i));
+        u[2 * i + 1] = hi_bf16(P(t, i));
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
+    const uint32_t m = fold_pk(acc);                 // max |x| (BF16 bits; above 0x7F80: a NaN)
+    m_out = m;
+    const uint32_t sc = block_code(bf16_mag(m), g_r, yg_r);
+    return encode_block<E>(u, sc, m > 0x7F80u, tab_r, rnd);
+}
 
 }  // namespace
 
@@ -330,15 +410,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int dir = e >> 7, code = e & 127;
         if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
         const float g = dir ? g_c : g_r;
-        float2 entry;
+        float4 entry;
         if (code == 0) {
-            entry = make_float2(g, 1.0f / g);
+            const float yg = 1.0f / g;
+            entry = make_float4(g, yg, yg, 0.0f);
         } else {
             float d = e4m3_value((uint32_t)code) * g;
             float y = 1.0f / d;
             if (dir) { d *= 4.0f; y *= 0.25f; }
-            const bool ok = code == 127 || product_rounds_like_quotient(d, y);
-            entry = make_float2(d, ok ? y : -y);
+            const float ym = code == 127 ? y : product_multiplier(d, y);
+            entry = make_float4(d, y, ym, 0.0f);
         }
         G.tables[(s * 2 + dir) * 128 + code] = entry;
     }
@@ -360,14 +441,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         p[t][1] = *reinterpret_cast<const uint4*>(base + t * k + 8);
     }
 
-    __shared__ float2 tab[2][128];
-    __shared__ uint2 lds_codes[kTileCols * 8];
-    __shared__ uint8_t lds_sc[kTileCols * 8];
+    __shared__ float4 tab[2][128];
+    // Column codes / scales of the tile by (column, 16-row block): 64 + 8 bytes per
+    // column, with one more slot after every 16 columns so that the 8 lane groups
+    // that write columns 16 apart use both halves of the LDS banks.
+    __shared__ uint2 lds_codes[kTileCols * 8 + 8 * 8];
+    __shared__ uint8_t lds_sc[kTileCols * 8 + 8 * 8];
     {
-        const float4* src = reinterpret_cast<const float4*>(G.tables + s * 256);
-        float4* dst = reinterpret_cast<float4*>(&tab[0][0]);
-        if (ROW) dst[lane] = src[lane];
-        if (COL) dst[64 + lane] = src[64 + lane];
+        const float4* src = G.tables + s * 256;
+        if (ROW) { tab[0][lane] = src[lane]; tab[0][64 + lane] = src[64 + lane]; }
+        if (COL) { tab[1][lane] = src[128 + lane]; tab[1][64 + lane] = src[192 + lane]; }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -378,43 +461,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int64_t row0 = (int64_t)T * kTileRows + tb * 16;           // group-relative
     const int64_t c0 = (int64_t)C * kTileCols + cc * 16;
     const int64_t r_local0 = (int64_t)T_local * kTileRows + tb * 16;  // section-local
+    const u32x4 no_rnd = {0, 0, 0, 0};
 
-    bool lane_nan = false;
     if (COL) {
         const float g_c = tab[1][0].x, yg_c = tab[1][0].y;
-        const int64_t b_local = r_local0 >> 4;                      // section-local 16-row block
+        const float4* tab_c = tab[1];
+        const uint32_t mask = G.sign_mask;
+        auto put = [&](int j, const BlockOut& o) {
+            lds_codes[(cc * 17 + j) * 8 + tb] = o.codes;
+            lds_sc[(cc * 17 + j) * 8 + tb] = (uint8_t)o.scale;
+        };
+        if (SR && G.sr_col) {
+            const int64_t b_local = r_local0 >> 4;                  // section-local 16-row block
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            float v[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const uint32_t w = P(t, j >> 1);
-                const uint32_t neg = sign_of_row(G.sign_mask, t);
-                v[t] = (j & 1) ? hi_signed(w, neg) : lo_signed(w, neg);
-            }
-            butterfly16(v);
-            const bool nan_block = v[0] != v[0];           // a NaN input reaches every output
-            lane_nan |= nan_block;
-            float mx = 0.0f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[t]));
-            // block amax of the column values BF16(v/4) = BF16(max |v|) / 4
-            const uint32_t sc = block_code(0.25f * round_bf16(mx), g_c, yg_c);
-            const float2 dy = tab[1][sc & 0x7Fu];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) v[t] = round_bf16(v[t]);
-            uint2 codes;
-            if (SR && G.sr_col) {
+            for (int j = 0; j < 16; ++j) {
                 const u32x4 rnd = block_random(G.seed, G.col_off[s], (uint64_t)((c0 + j) * (int64_t)(ms >> 4) + b_local));
-                codes = encode_block<true>(v, dy, rnd);
-            } else {
-                codes = encode_block<false>(v, dy, u32x4{0, 0, 0, 0});
+                put(j, column_block<Enc::Sr>(p, j, mask, g_c, yg_c, tab_c, rnd));
+                __builtin_amdgcn_sched_barrier(0);
             }
-            const bool zero = nan_block || sc == 0u;
-            const int col = cc * 16 + j;
-            lds_codes[col * 8 + tb] = zero ? make_uint2(0u, 0u) : codes;
-            lds_sc[col * 8 + tb] = (uint8_t)(nan_block ? 0x7Fu : sc);
-            __builtin_amdgcn_sched_barrier(0);   // one column at a time: bounds register pressure
+        } else {
+            // No branch in this loop, so the scheduler can overlap neighbouring
+            // columns; blocks whose scale code needs the exact division are redone.
+            uint32_t redo = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const BlockOut o = column_block<Enc::Mul>(p, j, mask, g_c, yg_c, tab_c, no_rnd);
+                put(j, o);
+                redo |= (uint32_t)o.unsafe << j;
+                if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two columns at a time: bounds registers
+            }
+            if (__ballot(redo != 0) != 0) {
+                launder(p);
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if ((redo >> j) & 1u) put(j, column_block<Enc::Div>(p, j, mask, g_c, yg_c, tab_c, no_rnd));
+            }
         }
         // the LDS region is this wave's own: order its writes before the reads below
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -425,28 +506,54 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         for (int it = 0; it < 8; ++it) {
             const int idx = it * 64 + lane;
             const int col = idx >> 2, part = idx & 3;
-            const uint4 v = *reinterpret_cast<const uint4*>(&lds_codes[col * 8 + part * 2]);
+            const uint4 v = *reinterpret_cast<const uint4*>(&lds_codes[(col + (col >> 4)) * 8 + part * 2]);
             *reinterpret_cast<uint4*>(codes_s + ((int64_t)C * kTileCols + col) * (ms >> 1) + T_local * 64 + part * 16) = v;
         }
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int col = it * 64 + lane;
-            const uint2 v = *reinterpret_cast<const uint2*>(&lds_sc[col * 8]);
+            const uint2 v = *reinterpret_cast<const uint2*>(&lds_sc[(col + (col >> 4)) * 8]);
             *reinterpret_cast<uint2*>(scales_s + ((int64_t)C * kTileCols + col) * (ms >> 4) + T_local * 8) = v;
         }
-        // Hide the tile's provenance from the compiler: otherwise it keeps values
-        // widened by the column pass alive for the row pass.
-#pragma unroll
-        for (int t = 0; t < 16; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(p[t][h].x), "+v"(p[t][h].y), "+v"(p[t][h].z), "+v"(p[t][h].w));
+        launder(p);
     }
 
-    if (ROW || FP8) {
+    if (ROW) {
         const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
-        // Without a NaN anywhere in the wave's tile (known from the column pass),
-        // max |x| of a block is the FP32 maximum of the widened values.
-        const bool fast_amax = COL && __ballot(lane_nan) == 0;
+        const float4* tab_r = tab[0];
+        auto put = [&](int t, const BlockOut& o) {
+            const int64_t row = row0 + t;
+            *reinterpret_cast<uint2*>(G.row_codes + row * (k >> 1) + (c0 >> 1)) = o.codes;
+            G.row_scales[row * (k >> 4) + (c0 >> 4)] = (uint8_t)o.scale;
+        };
+        uint32_t m;
+        if (SR && G.sr_row) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const u32x4 rnd = block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
+                put(t, row_block<Enc::Sr>(p, t, g_r, yg_r, tab_r, rnd, m));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            uint32_t redo = 0;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const BlockOut o = row_block<Enc::Mul>(p, t, g_r, yg_r, tab_r, no_rnd, m);
+                put(t, o);
+                redo |= (uint32_t)o.unsafe << t;
+                if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
+            }
+            if (__ballot(redo != 0) != 0) {
+                launder(p);
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    if ((redo >> t) & 1u) put(t, row_block<Enc::Div>(p, t, g_r, yg_r, tab_r, no_rnd, m));
+            }
+        }
+    }
+
+    if (FP8) {
+        // FP8 1x128 of each row: the group's max |x| without NaNs over 8 lanes
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int64_t row = row0 + t;
@@ -456,62 +563,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
                 u[2 * i] = lo_bf16(P(t, i));
                 u[2 * i + 1] = hi_bf16(P(t, i));
             }
-            uint32_t m;                                  // max |x| of the block, BF16 bits
-            if (fast_amax) {
-                float mx = 0.0f;
+            uint32_t acc = 0;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fabsf(u[i]));
-                m = __builtin_bit_cast(uint32_t, mx) >> 16;
-            } else {
-                uint32_t acc = 0;
+            for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
+            uint32_t mf = fold_pk(acc);
+            const bool nan = mf > 0x7F80u;
+            if (nan) {
+                mf = 0;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
-                m = fold_pk(acc);
+                for (int i = 0; i < 8; ++i) mf = absmax_pk_nonan(mf, P(t, i));
             }
-            const bool nan_block = m > 0x7F80u;
-            if (ROW) {
-                const uint32_t sc = block_code(bf16_mag(m), g_r, yg_r);
-                const float2 dy = tab[0][sc & 0x7Fu];
-                uint2 codes;
-                if (SR && G.sr_row) {
-                    const u32x4 rnd = block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
-                    codes = encode_block<true>(u, dy, rnd);
-                } else {
-                    codes = encode_block<false>(u, dy, u32x4{0, 0, 0, 0});
-                }
-                if (nan_block || sc == 0u) codes = make_uint2(0u, 0u);
-                *reinterpret_cast<uint2*>(G.row_codes + row * (k >> 1) + (c0 >> 1)) = codes;
-                G.row_scales[row * (k >> 4) + (c0 >> 4)] = (uint8_t)(nan_block ? 0x7Fu : sc);
-            }
-            if (FP8) {
-                // FP8 1x128 of the row: the group's max |x| without NaNs over 8 lanes
-                uint32_t mf = m;
-                if (nan_block) {
-                    mf = 0;
+            mf = group8_max_u32(mf);
+            const float amax = bf16_mag(mf);
+            const float sf = (amax > k_floor() ? amax : k_floor()) * k_inv448();
+            const float yf = 1.0f / sf;
+            uint32_t c4[4];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) mf = absmax_pk_nonan(mf, P(t, i));
+            for (int j = 0; j < 4; ++j) {
+                c4[j] = e4m3_pack4(div_rn(u[4 * j], sf, yf), div_rn(u[4 * j + 1], sf, yf),
+                                   div_rn(u[4 * j + 2], sf, yf), div_rn(u[4 * j + 3], sf, yf));
+                if (nan) {
+                    // a NaN element: the conversion gives 0xFF, the format's NaN code is 0x7F
+                    const uint32_t cj = c4[j];
+                    const uint32_t ff = cj & (cj >> 1) & (cj >> 2) & (cj >> 3) & (cj >> 4) & (cj >> 5) &
+                                        (cj >> 6) & (cj >> 7) & 0x01010101u;
+                    c4[j] = cj ^ (ff * 0x80u);
                 }
-                mf = group8_max_u32(mf);
-                const float amax = bf16_mag(mf);
-                const float sf = (amax > k_floor() ? amax : k_floor()) * k_inv448();
-                const float yf = 1.0f / sf;
-                uint32_t c4[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    c4[j] = e4m3_pack4(div_rn(u[4 * j], sf, yf), div_rn(u[4 * j + 1], sf, yf),
-                                       div_rn(u[4 * j + 2], sf, yf), div_rn(u[4 * j + 3], sf, yf));
-                    if (nan_block) {
-                        // a NaN element: the conversion gives 0xFF, the format's NaN code is 0x7F
-                        const uint32_t cj = c4[j];
-                        const uint32_t ff = cj & (cj >> 1) & (cj >> 2) & (cj >> 3) & (cj >> 4) & (cj >> 5) &
-                                            (cj >> 6) & (cj >> 7) & 0x01010101u;
-                        c4[j] = cj ^ (ff * 0x80u);
-                    }
-                }
-                *reinterpret_cast<uint4*>(G.fp8_codes + row * k + c0) = make_uint4(c4[0], c4[1], c4[2], c4[3]);
-                if (cc == 0) G.fp8_scales[row * (k >> 7) + C] = sf;
             }
-            __builtin_amdgcn_sched_barrier(0);       // one row at a time
+            *reinterpret_cast<uint4*>(G.fp8_codes + row * k + c0) = make_uint4(c4[0], c4[1], c4[2], c4[3]);
+            if (cc == 0) G.fp8_scales[row * (k >> 7) + C] = sf;
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }

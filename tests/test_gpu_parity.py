@@ -188,6 +188,43 @@ def test_grouped_large_moe_recipe_small(orc):
     compare_grouped(orc, w.tensors["x"].to(dev), w.params["split_sections"], w.params["sign_mask"], 7)
 
 
+def tie_matrix(rows, k, sections, mask, seed):
+    """Short binary values whose exact quotients often land on E2M1 rounding
+    boundaries: every section's max |x| is 2688 and the max |H16 D x| / 4 of every
+    section is 2688 too, so both tensor scales are exactly 1 and the divisors are
+    the E4M3 values themselves; some rows hold 3 (scale 0.5) and every boundary
+    times 0.5.  The kernels must then fall back from the product to the exact
+    division for scale codes where no multiplier decides like the quotient."""
+    rng = np.random.default_rng(seed)
+    mant = np.array([1, 1.5, 1.25, 1.75, 3, 3.5, 5, 6, 7, 0.75, 0.5, 0.25])
+    v = rng.choice(mant, size=(rows, k)) * 2.0 ** rng.integers(-6, 4, size=(rows, k))
+    v *= rng.choice([-1.0, 1.0], size=(rows, k))
+    ties = np.array([3.0, 0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5] * 2)
+    r0 = 0
+    for ms in sections:
+        if ms == 0:
+            continue
+        v[r0 + 5, 17] = 2688.0                              # row-wise section amax
+        signs = np.array([-1.0 if (mask >> t) & 1 else 1.0 for t in range(16)])
+        v[r0 + 32:r0 + 48, 40] = 672.0 * signs              # H16 D x = (10752, 0, ...)
+        for r in range(r0 + 64, r0 + 64 + 8):              # row blocks with exact ties everywhere
+            v[r, :16] = ties * rng.choice([-1.0, 1.0], size=16)
+        r0 += ms
+    f32 = v.astype(np.float32)
+    return (f32.view(np.uint32) >> 16).astype(np.uint16)    # exact: every value is short
+
+
+def test_grouped_exact_ties(orc):
+    dev = device()
+    announce("grouped exact ties")
+    sections = [256, 0, 384]
+    for mask in (0x0000, 0x6C93):
+        b = tie_matrix(640, 256, sections, mask, 77 + mask)
+        x = bf16_dev(b, dev)
+        compare_grouped(orc, x, sections, mask, 3)
+        compare_grouped(orc, x, sections, mask, 7)
+
+
 def test_grouped_edges(orc):
     dev = device()
     announce("grouped edges")
