@@ -7,6 +7,8 @@ Formats: OCP E4M3FN ("FLOAT8E4M3FN" in the onnxruntime QMoE PR, Description),
 E2M1 with E4M3 block scales (the NVFP4 format of the TransformerEngine NVFP4 PRs),
 bfloat16 (the activations' dtype in all pages)."""
 import numpy as np
+
+from tests.golden_util import num, rows
 import pytest
 import torch
 
@@ -143,8 +145,7 @@ def test_e2m1_hand_cases(orc):
 
 
 # ---------------------------------------------------------------- stochastic rounding
-@pytest.mark.parametrize("x,F,lo,hi", [(0.625, 64, 1, 2), (2.25, 64, 4, 5), (5.5, 192, 6, 7),
-                                       (1.0, 0, 2, 2), (0.3, 153, 0, 1)])
+@pytest.mark.parametrize("x,F,lo,hi", [(num(a), int(b), int(c), int(d)) for a, b, c, d in rows("e2m1_sr_counts.txt")])
 def test_sr_enumeration(orc, x, F, lo, hi):
     """Over all 256 random bytes the value rounds up exactly F times, F = floor(256 f)."""
     r = np.arange(256, dtype=np.uint8)

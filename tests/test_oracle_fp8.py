@@ -8,6 +8,8 @@ midpoints; the brute-force test below regenerates such cases.
 DSA (TensorRT-LLM PR #15158, Summary): torch.cat([qk_pe, qk_nope]) ->
 rotate_activation -> fp8_quantize_1x128."""
 import numpy as np
+
+from tests.golden_util import num, rows
 import pytest
 import torch
 
@@ -34,12 +36,13 @@ def torch_reference(x_bf16):
 
 
 def test_b1_unit_scale(orc):
+    fix = rows("fp8_unit_scale.txt")
+    vals = [num(r[0]) for r in fix]
     row = np.zeros((1, 128), np.float32)
-    vals = [448.0, 1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, -2.0 ** -10, 0.0]
     row[0, :len(vals)] = vals
     q, s = orc.quant_fp8_1x128(bf16(row))
     assert s[0, 0] == 1.0
-    assert q[0, :len(vals)].tolist() == [0x7E, 0x38, 0x3A, 0xB8, 0x00, 0x02, 0x80, 0x00]
+    assert q[0, :len(vals)].tolist() == [num(r[1]) for r in fix]
 
 
 def test_b2_b3(orc):
@@ -124,14 +127,14 @@ def test_division_mode_midpoints(orc):
 
 
 def test_b8_dsa_hand_case(orc):
+    fix = rows("dsa_wht128_fp8.txt")
     v = np.arange(1, 129, dtype=np.float32)
     pe, nope = bf16(v[None, :64]), bf16(v[None, 64:])
     q, s = orc.hadamard_quant_fp8(pe, nope)
-    assert s.view(np.uint32)[0] == 0x3FD00001
+    assert s.view(np.uint32)[0] == num(fix[0][1])
     expect = np.zeros(128, np.uint8)
-    expect[0] = 0x7E
-    for j, c in enumerate([0xC6, 0xCE, 0xD6, 0xDE, 0xE6, 0xEE, 0xF6]):
-        expect[1 << j] = c
+    for r in fix[1:]:
+        expect[int(r[1])] = num(r[2])
     assert q[0].tolist() == expect.tolist()
 
 

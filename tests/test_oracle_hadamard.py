@@ -9,6 +9,8 @@ Pins: scipy's Sylvester Hadamard matrix (library) on inputs whose sums are exact
 H.H^T = n.I, norm and inner-product preservation within BF16 rounding, and hand
 cases whose values follow from the definition."""
 import numpy as np
+
+from tests.golden_util import num, rows
 import pytest
 import scipy.linalg
 import torch
@@ -63,11 +65,9 @@ def test_c128_constant(orc):
 
 def test_b4_hand_cases(orc):
     x = np.arange(1, 17, dtype=np.float32)
-    y = orc.wht(x[None], sign_mask=0, c=0.25)[0]
-    assert y.tolist() == [34, -2, -4, 0, -8, 0, 0, 0, -16, 0, 0, 0, 0, 0, 0, 0]
-    y = orc.wht(x[None], sign_mask=0x8001, c=0.25)[0]
-    assert y.tolist() == [25.5, 5.5, 3.5, -8.5, -0.5, -8.5, -8.5, 7.5, -8.5, -8.5, -8.5, 7.5,
-                          -8.5, 7.5, 7.5, -8.5]
+    for r in rows("wht16_integers.txt"):
+        y = orc.wht(x[None], sign_mask=num(r[0]), c=0.25)[0]
+        assert y.tolist() == [num(t) for t in r[1:]]
 
 
 def test_b5_constant_block(orc):

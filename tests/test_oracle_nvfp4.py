@@ -10,6 +10,8 @@ The tensor-scale recipe g = max(A, 1e-10) * F(1/2688) per section and direction 
 a reading (the pages name an FP32 per-tensor scale but no formula); these tests pin
 the oracle's arithmetic of that reading with hand cases and invariants."""
 import numpy as np
+
+from tests.golden_util import num, rows
 import pytest
 import scipy.linalg
 import torch
@@ -40,29 +42,36 @@ def e4m3(codes):
 
 # ------------------------------------------------------------------ B9 hand cases
 def test_b9_block_cases(orc):
-    g = np.float32(2.0 ** -8)
-    assert orc.nvfp4_global_scale(10.5) == g
-    blk = np.zeros(16, np.float32)
-    blk[3] = 10.5
-    sc, _ = orc.nvfp4_block(blk, g)
-    assert sc == 0x7E                          # d = 448 * 2^-8 = 1.75
-    v = [6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, -.25, -.75, 5.5, f32_of_bf16(bf16([0.1]))[0], -0.0, 1, -6, 4.5]
-    sc, codes = orc.nvfp4_block(np.array(v, np.float32), g)
-    assert sc == 0x78                          # t = 256, d = 1.0
-    assert codes.tolist() == [7, 0, 2, 2, 4, 4, 6, 6, 8, 0xA, 7, 0, 8, 2, 0xF, 6]
+    fix = {}
+    for r in rows("nvfp4_blocks.txt"):
+        fix.setdefault(r[0], []).append(r[1:])
+    A, g_bits = num(fix["section"][0][0]), num(fix["section"][0][1])
+    g = orc.nvfp4_global_scale(A)
+    assert g.view(np.uint32) == g_bits
+    for a, sc_want in fix["block"]:
+        blk = np.zeros(16, np.float32)
+        blk[3] = num(a)
+        sc, codes = orc.nvfp4_block(blk, g)
+        assert sc == num(sc_want), a
+        if sc == 0:
+            assert not codes.any()                 # scale underflow: zero block
+    for a, d in fix["block_d"]:
+        blk = np.zeros(16, np.float32)
+        blk[0] = num(a)
+        sc, _ = orc.nvfp4_block(blk, g)
+        assert e4m3([sc])[0] * g == np.float32(num(d))
+    xs = [num(t) for t in fix["codes_x"][0]]
+    xs[11] = f32_of_bf16(bf16([xs[11]]))[0]       # BF16(0.1)
+    sc, codes = orc.nvfp4_block(np.array(xs, np.float32), g)
+    assert sc == 0x78                              # a = 6: t = 256, d = 1.0
+    assert codes.tolist() == [num(t) for t in fix["codes_c"][0]]
     packed = (codes[0::2] | (codes[1::2] << 4)).tolist()
-    assert packed == [0x07, 0x22, 0x44, 0x66, 0xA8, 0x07, 0x28, 0x6F]
+    assert packed == [num(t) for t in fix["packed"][0]]
     blk = np.zeros(16, np.float32)
     blk[0] = 6.25
     sc, codes = orc.nvfp4_block(blk, g)
-    assert sc == 0x78 and codes[0] == 7       # saturates at 6
-    blk[0] = 2.0 ** -20
-    sc, codes = orc.nvfp4_block(blk, g)
-    assert sc == 0 and not codes.any()        # scale underflow: zero block
-    blk[0] = 0.05
-    sc, codes = orc.nvfp4_block(blk, g)
-    assert sc == 0x41 and e4m3([sc])[0] * g == np.float32(0.0087890625)
-    assert orc.nvfp4_global_scale(0.0).view(np.uint32) == 0x29278B6D
+    assert sc == 0x78 and codes[0] == 7           # saturates at 6
+    assert orc.nvfp4_global_scale(0.0).view(np.uint32) == num(fix["empty_section_g"][0][0])
 
 
 def test_nan_block(orc):
