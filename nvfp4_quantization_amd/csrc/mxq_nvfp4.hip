@@ -159,6 +159,17 @@ __device__ __forceinline__ int section_of(const Nvfp4Group& G, int T) {
     return s;
 }
 
+// max |v_i| over 16 values: a tree of three-input maxima (depth 3, 8 operations).
+// NaNs are ignored (callers that care detect them separately).
+__device__ __forceinline__ float absmax16(const float (&v)[16]) {
+    auto m3 = [](float a, float b, float c) {
+        return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)), __builtin_fabsf(c));
+    };
+    const float a = m3(v[0], v[1], v[2]), b = m3(v[3], v[4], v[5]), c = m3(v[6], v[7], v[8]);
+    const float d = m3(v[9], v[10], v[11]), e = m3(v[12], v[13], v[14]);
+    return __builtin_fmaxf(m3(a, b, c), m3(d, e, v[15]));
+}
+
 // E2M1 codes of 8 values u[0..7] (element 2i in the low nibble of byte i):
 // nearest-even of u * y (MUL), of fl(u / d), or stochastic with random bytes
 // r0 .. r0+7 of rnd.
@@ -302,12 +313,7 @@ __device__ __forceinline__ BlockOut column_block(const uint4 (&p)[16][2], int j,
     }
     butterfly16(v);
     const bool nan = v[0] != v[0];                   // a NaN input reaches every output
-    float mx[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)                      // a shallow tree, not a 16-long chain
-        mx[i] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[4 * i]), __builtin_fabsf(v[4 * i + 1])),
-                                __builtin_fmaxf(__builtin_fabsf(v[4 * i + 2]), __builtin_fabsf(v[4 * i + 3])));
-    const float m = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), __builtin_fmaxf(mx[2], mx[3]));
+    const float m = absmax16(v);
     // block amax of the column values BF16(v/4) = BF16(max |v|) / 4
     const uint32_t sc = block_code(0.25f * round_bf16(m), g_c, yg_c);
 #pragma unroll
@@ -315,8 +321,11 @@ __device__ __forceinline__ BlockOut column_block(const uint4 (&p)[16][2], int j,
     return encode_block<E>(v, sc, nan, tab_c, rnd);
 }
 
-// Row t of the lane: columns 16 cc .. +15 (one row-wise block).
-template <Enc E>
+// Row t of the lane: columns 16 cc .. +15 (one row-wise block).  FAST: no NaN
+// anywhere in the wave's tile, so max |x| is the FP32 maximum of the widened values;
+// otherwise packed integer maxima of |x| bits, where a NaN shows as a value above
+// 0x7F80.
+template <Enc E, bool FAST>
 __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, float g_r, float yg_r,
                                               const float4* tab_r, const u32x4& rnd, uint32_t& m_out) {
     float u[16];
@@ -325,13 +334,76 @@ __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, fl
         u[2 * i] = lo_bf16(P(t, i));
         u[2 * i + 1] = hi_bf16(P(t, i));
     }
-    uint32_t acc = 0;
+    uint32_t m;                                      // max |x| (BF16 bits)
+    if (FAST) {
+        m = __builtin_bit_cast(uint32_t, absmax16(u)) >> 16;
+    } else {
+        uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
-    const uint32_t m = fold_pk(acc);                 // max |x| (BF16 bits; above 0x7F80: a NaN)
+        for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
+        m = fold_pk(acc);
+    }
     m_out = m;
     const uint32_t sc = block_code(bf16_mag(m), g_r, yg_r);
     return encode_block<E>(u, sc, m > 0x7F80u, tab_r, rnd);
+}
+
+// The row pass of a tile: 16 row blocks per lane.  FAST (the column pass ran and
+// reports NaN column blocks in nan): block maxima from the FP32 widened values,
+// then the lanes whose sub-tile holds a NaN redo all their rows with packed integer
+// maxima, where a NaN shows.
+template <bool SR, bool FAST>
+__device__ __forceinline__ void row_pass(const Nvfp4Group& G, uint4 (&p)[16][2], int s, int64_t row0, int64_t c0,
+                                         int64_t r_local0, float g_r, float yg_r, const float4* tab_r, bool nan) {
+    const int64_t k = G.k;
+    const u32x4 no_rnd = {0, 0, 0, 0};
+    auto put = [&](int t, const BlockOut& o) {
+        const int64_t row = row0 + t;
+        *reinterpret_cast<uint2*>(G.row_codes + row * (k >> 1) + (c0 >> 1)) = o.codes;
+        G.row_scales[row * (k >> 4) + (c0 >> 4)] = (uint8_t)o.scale;
+    };
+    auto rnd_of = [&](int t) {
+        return block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
+    };
+    uint32_t m;
+    if (SR && G.sr_row) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            put(t, row_block<Enc::Sr, FAST>(p, t, g_r, yg_r, tab_r, rnd_of(t), m));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        uint32_t redo = 0;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const BlockOut o = row_block<Enc::Mul, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m);
+            put(t, o);
+            redo |= (uint32_t)o.unsafe << t;
+            if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
+        }
+        if (__ballot(redo != 0) != 0) {
+            launder(p);
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                if ((redo >> t) & 1u) put(t, row_block<Enc::Div, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m));
+        }
+    }
+    if (FAST && __ballot(nan) != 0) {
+        // rare: the lane's rows again, loaded afresh one at a time, so that nothing of
+        // the main path stays live for this branch
+        asm volatile("" ::: "memory");
+        if (nan) {
+            const uint16_t* xr = G.x + row0 * k + c0;
+#pragma unroll 1
+            for (int t = 0; t < 16; ++t) {
+                uint4 q[16][2];
+                q[0][0] = *reinterpret_cast<const uint4*>(xr + t * k);
+                q[0][1] = *reinterpret_cast<const uint4*>(xr + t * k + 8);
+                if (SR && G.sr_row) put(t, row_block<Enc::Sr, false>(q, 0, g_r, yg_r, tab_r, rnd_of(t), m));
+                else put(t, row_block<Enc::Div, false>(q, 0, g_r, yg_r, tab_r, no_rnd, m));
+            }
+        }
+    }
 }
 
 }  // namespace
@@ -462,6 +534,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int64_t c0 = (int64_t)C * kTileCols + cc * 16;
     const int64_t r_local0 = (int64_t)T_local * kTileRows + tb * 16;  // section-local
     const u32x4 no_rnd = {0, 0, 0, 0};
+    bool lane_nan = !COL;                            // a NaN column block (unknown without the column pass)
 
     if (COL) {
         const float g_c = tab[1][0].x, yg_c = tab[1][0].y;
@@ -476,7 +549,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const u32x4 rnd = block_random(G.seed, G.col_off[s], (uint64_t)((c0 + j) * (int64_t)(ms >> 4) + b_local));
-                put(j, column_block<Enc::Sr>(p, j, mask, g_c, yg_c, tab_c, rnd));
+                const BlockOut o = column_block<Enc::Sr>(p, j, mask, g_c, yg_c, tab_c, rnd);
+                put(j, o);
+                lane_nan |= o.scale == 0x7Fu;
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
@@ -488,6 +563,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
                 const BlockOut o = column_block<Enc::Mul>(p, j, mask, g_c, yg_c, tab_c, no_rnd);
                 put(j, o);
                 redo |= (uint32_t)o.unsafe << j;
+                lane_nan |= o.scale == 0x7Fu;
                 if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two columns at a time: bounds registers
             }
             if (__ballot(redo != 0) != 0) {
@@ -521,35 +597,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     if (ROW) {
         const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
         const float4* tab_r = tab[0];
-        auto put = [&](int t, const BlockOut& o) {
-            const int64_t row = row0 + t;
-            *reinterpret_cast<uint2*>(G.row_codes + row * (k >> 1) + (c0 >> 1)) = o.codes;
-            G.row_scales[row * (k >> 4) + (c0 >> 4)] = (uint8_t)o.scale;
-        };
-        uint32_t m;
-        if (SR && G.sr_row) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const u32x4 rnd = block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
-                put(t, row_block<Enc::Sr>(p, t, g_r, yg_r, tab_r, rnd, m));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            uint32_t redo = 0;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const BlockOut o = row_block<Enc::Mul>(p, t, g_r, yg_r, tab_r, no_rnd, m);
-                put(t, o);
-                redo |= (uint32_t)o.unsafe << t;
-                if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
-            }
-            if (__ballot(redo != 0) != 0) {
-                launder(p);
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    if ((redo >> t) & 1u) put(t, row_block<Enc::Div>(p, t, g_r, yg_r, tab_r, no_rnd, m));
-            }
-        }
+        row_pass<SR, COL>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan);
     }
 
     if (FP8) {
