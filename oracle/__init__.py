@@ -68,6 +68,10 @@ def lib():
         L.oracle_group_rht_quant_nvfp4.restype = ctypes.c_int
         L.oracle_group_rht_quant_nvfp4.argtypes = [_p, _i64, _p, _i64, ctypes.c_uint16, ctypes.c_uint32,
                                                    _u64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.oracle_group_rht_quant_nvfp4_amax.restype = ctypes.c_int
+        L.oracle_group_rht_quant_nvfp4_amax.argtypes = [_p, _i64, _p, _i64, ctypes.c_uint16, ctypes.c_uint32,
+                                                        _u64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                                        _p, _p, _p, _p]
         for name in ("oracle_e4m3_encode_n", "oracle_e2m1_encode_n", "oracle_f32_to_bf16_n"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [_p, _i64, _p]
@@ -213,12 +217,18 @@ class NVFP4Outputs:
         self.col_global = np.zeros(num_sections if col else 0, np.float32)
         self.fp8_codes = np.zeros(total_rows * k if f8 else 0, np.uint8)
         self.fp8_scales = np.zeros(total_rows * k // 128 if f8 else 0, np.float32)
+        # measured section maxima (row values, column values), always filled
+        self.row_amax = np.zeros(num_sections, np.float32)
+        self.col_amax = np.zeros(num_sections, np.float32)
 
 
 def group_rht_quant_nvfp4(x_bf16, split_sections, sign_mask, flags, seed=0,
-                          row_offsets=None, col_offsets=None, threads=1):
+                          row_offsets=None, col_offsets=None, threads=1, amax_in=None):
     """The whole grouped call.  threads > 1 runs independent sections and column
-    ranges of the same oracle functions on worker threads (ctypes releases the GIL)."""
+    ranges of the same oracle functions on worker threads (ctypes releases the GIL).
+    amax_in: None, or (row maxima, column maxima) per section supplied by the caller
+    (either may be None) that replace the measured maxima in the tensor scales.  The
+    measured maxima are returned in out.row_amax / out.col_amax."""
     x = _c(x_bf16, np.uint16)
     total, k = x.shape
     sections = _c(split_sections, np.int64)
@@ -227,20 +237,25 @@ def group_rht_quant_nvfp4(x_bf16, split_sections, sign_mask, flags, seed=0,
     out = NVFP4Outputs(total, k, S, flags)
     ro = None if row_offsets is None else _c(row_offsets, np.uint64)
     co = None if col_offsets is None else _c(col_offsets, np.uint64)
+    ain_r = ain_c = None
+    if amax_in is not None:
+        ain_r = None if amax_in[0] is None else _c(amax_in[0], np.float32)
+        ain_c = None if amax_in[1] is None else _c(amax_in[1], np.float32)
     if threads <= 1:
-        rc = lib().oracle_group_rht_quant_nvfp4(
+        rc = lib().oracle_group_rht_quant_nvfp4_amax(
             _ptr(x), k, _ptr(sections), S, sign_mask, flags, seed, _ptr(ro), _ptr(co),
             _ptr(out.row_codes), _ptr(out.row_scales), _ptr(out.row_global),
             _ptr(out.col_codes), _ptr(out.col_scales), _ptr(out.col_global),
-            _ptr(out.fp8_codes), _ptr(out.fp8_scales))
+            _ptr(out.fp8_codes), _ptr(out.fp8_scales),
+            _ptr(ain_r), _ptr(ain_c), _ptr(out.row_amax), _ptr(out.col_amax))
         if rc != 0:
             raise ValueError(f"oracle rejected the call ({rc})")
         return out
-    _threaded_group(x, sections, sign_mask, flags, seed, ro, co, out, threads)
+    _threaded_group(x, sections, sign_mask, flags, seed, ro, co, out, threads, ain_r, ain_c)
     return out
 
 
-def _threaded_group(x, sections, sign_mask, flags, seed, ro, co, out, threads):
+def _threaded_group(x, sections, sign_mask, flags, seed, ro, co, out, threads, ain_r=None, ain_c=None):
     total, k = x.shape
     L = lib()
     starts = np.concatenate([[0], np.cumsum(sections)[:-1]]).astype(np.int64)
@@ -264,8 +279,10 @@ def _threaded_group(x, sections, sign_mask, flags, seed, ro, co, out, threads):
         for s, ar, ac in ex.map(lambda j: amax_job(*j), jobs):
             amax_r[s] = max(amax_r[s], ar)
             amax_c[s] = max(amax_c[s], ac)
-    g_r = np.array([nvfp4_global_scale(a) for a in amax_r], np.float32)
-    g_c = np.array([nvfp4_global_scale(a) for a in amax_c], np.float32)
+    out.row_amax[:] = amax_r
+    out.col_amax[:] = amax_c
+    g_r = np.array([nvfp4_global_scale(a) for a in (amax_r if ain_r is None else ain_r)], np.float32)
+    g_c = np.array([nvfp4_global_scale(a) for a in (amax_c if ain_c is None else ain_c)], np.float32)
     if flags & ROWWISE:
         out.row_global[:] = g_r
     if flags & COLUMNWISE:

@@ -375,13 +375,15 @@ void oracle_nvfp4_section(const uint16_t* x, int64_t rows, int64_t k, uint16_t s
     }
 }
 
-int oracle_group_rht_quant_nvfp4(const uint16_t* x, int64_t k,
-                                 const int64_t* split_sections, int64_t num_sections,
-                                 uint16_t sign_mask, uint32_t flags, uint64_t seed,
-                                 const uint64_t* row_offsets, const uint64_t* col_offsets,
-                                 uint8_t* row_codes, uint8_t* row_scales, float* row_global,
-                                 uint8_t* col_codes, uint8_t* col_scales, float* col_global,
-                                 uint8_t* fp8_codes, float* fp8_scales)
+int oracle_group_rht_quant_nvfp4_amax(const uint16_t* x, int64_t k,
+                                      const int64_t* split_sections, int64_t num_sections,
+                                      uint16_t sign_mask, uint32_t flags, uint64_t seed,
+                                      const uint64_t* row_offsets, const uint64_t* col_offsets,
+                                      uint8_t* row_codes, uint8_t* row_scales, float* row_global,
+                                      uint8_t* col_codes, uint8_t* col_scales, float* col_global,
+                                      uint8_t* fp8_codes, float* fp8_scales,
+                                      const float* amax_row_in, const float* amax_col_in,
+                                      float* amax_row_out, float* amax_col_out)
 {
     if (k <= 0 || k % 128 != 0) return 1;
     int64_t R = 0; /* first row of the current section */
@@ -391,8 +393,11 @@ int oracle_group_rht_quant_nvfp4(const uint16_t* x, int64_t k,
         const uint16_t* xs = x + R * k;
         float ar = 0.0f, ac = 0.0f;
         oracle_nvfp4_section_amax(xs, m, k, sign_mask, &ar, &ac);
-        float gr = oracle_nvfp4_global_scale(ar);
-        float gc = oracle_nvfp4_global_scale(ac);
+        if (amax_row_out) amax_row_out[s] = ar;
+        if (amax_col_out) amax_col_out[s] = ac;
+        /* a caller-supplied amax replaces the measured one in the tensor scale */
+        float gr = oracle_nvfp4_global_scale(amax_row_in ? amax_row_in[s] : ar);
+        float gc = oracle_nvfp4_global_scale(amax_col_in ? amax_col_in[s] : ac);
         if (flags & ORACLE_ROWWISE)    row_global[s] = gr;
         if (flags & ORACLE_COLUMNWISE) col_global[s] = gc;
         oracle_nvfp4_section(xs, m, k, sign_mask, flags, gr, gc,
@@ -408,6 +413,20 @@ int oracle_group_rht_quant_nvfp4(const uint16_t* x, int64_t k,
         R += m;
     }
     return 0;
+}
+
+int oracle_group_rht_quant_nvfp4(const uint16_t* x, int64_t k,
+                                 const int64_t* split_sections, int64_t num_sections,
+                                 uint16_t sign_mask, uint32_t flags, uint64_t seed,
+                                 const uint64_t* row_offsets, const uint64_t* col_offsets,
+                                 uint8_t* row_codes, uint8_t* row_scales, float* row_global,
+                                 uint8_t* col_codes, uint8_t* col_scales, float* col_global,
+                                 uint8_t* fp8_codes, float* fp8_scales)
+{
+    return oracle_group_rht_quant_nvfp4_amax(x, k, split_sections, num_sections, sign_mask, flags, seed,
+                                             row_offsets, col_offsets, row_codes, row_scales, row_global,
+                                             col_codes, col_scales, col_global, fp8_codes, fp8_scales,
+                                             NULL, NULL, NULL, NULL);
 }
 
 /* ------------------------------------------------------------------------ */

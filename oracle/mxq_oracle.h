@@ -133,6 +133,21 @@ int oracle_group_rht_quant_nvfp4(const uint16_t* x, int64_t k,
                                  uint8_t* col_codes, uint8_t* col_scales, float* col_global,
                                  uint8_t* fp8_codes, float* fp8_scales);
 
+/* The grouped call with a caller-supplied amax (next-step scaling, a single pass
+ * over x in the library): amax_row_in / amax_col_in (NULL: measure) replace the
+ * section maxima in the tensor scales, g = fl(max(A_in, F(1e-10)) * F(1/2688)); the
+ * measured maxima (the values the plain call would use) go to amax_row_out /
+ * amax_col_out when not NULL. */
+int oracle_group_rht_quant_nvfp4_amax(const uint16_t* x, int64_t k,
+                                      const int64_t* split_sections, int64_t num_sections,
+                                      uint16_t sign_mask, uint32_t flags, uint64_t seed,
+                                      const uint64_t* row_offsets, const uint64_t* col_offsets,
+                                      uint8_t* row_codes, uint8_t* row_scales, float* row_global,
+                                      uint8_t* col_codes, uint8_t* col_scales, float* col_global,
+                                      uint8_t* fp8_codes, float* fp8_scales,
+                                      const float* amax_row_in, const float* amax_col_in,
+                                      float* amax_row_out, float* amax_col_out);
+
 /* ---- element-wise loops over arrays (for exhaustive codec sweeps) ---------- */
 void oracle_e4m3_encode_n(const float* v, int64_t n, uint8_t* out);
 void oracle_e2m1_encode_n(const float* v, int64_t n, uint8_t* out);

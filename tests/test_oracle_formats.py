@@ -7,10 +7,9 @@ Formats: OCP E4M3FN ("FLOAT8E4M3FN" in the onnxruntime QMoE PR, Description),
 E2M1 with E4M3 block scales (the NVFP4 format of the TransformerEngine NVFP4 PRs),
 bfloat16 (the activations' dtype in all pages)."""
 import numpy as np
-
-from tests.golden_util import num, rows
 import pytest
 import torch
+from tests.golden_util import num, rows
 
 
 def f32(bits):

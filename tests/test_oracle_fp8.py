@@ -8,10 +8,9 @@ midpoints; the brute-force test below regenerates such cases.
 DSA (TensorRT-LLM PR #15158, Summary): torch.cat([qk_pe, qk_nope]) ->
 rotate_activation -> fp8_quantize_1x128."""
 import numpy as np
-
-from tests.golden_util import num, rows
 import pytest
 import torch
+from tests.golden_util import num, rows
 
 
 def bf16(v):

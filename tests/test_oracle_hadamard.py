@@ -9,11 +9,10 @@ Pins: scipy's Sylvester Hadamard matrix (library) on inputs whose sums are exact
 H.H^T = n.I, norm and inner-product preservation within BF16 rounding, and hand
 cases whose values follow from the definition."""
 import numpy as np
-
-from tests.golden_util import num, rows
 import pytest
 import scipy.linalg
 import torch
+from tests.golden_util import num, rows
 
 C128_BITS = 0x3DB504F3
 

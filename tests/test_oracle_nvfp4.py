@@ -10,11 +10,12 @@ The tensor-scale recipe g = max(A, 1e-10) * F(1/2688) per section and direction 
 a reading (the pages name an FP32 per-tensor scale but no formula); these tests pin
 the oracle's arithmetic of that reading with hand cases and invariants."""
 import numpy as np
-
-from tests.golden_util import num, rows
 import pytest
 import scipy.linalg
 import torch
+
+from nvfp4_quantization_amd import synth
+from tests.golden_util import num, rows
 
 
 def bf16(v):
@@ -274,3 +275,80 @@ def test_threaded_oracle_equals_single_thread(orc):
     for name in ("row_codes", "row_scales", "row_global", "col_codes", "col_scales", "col_global",
                  "fp8_codes", "fp8_scales"):
         assert np.array_equal(getattr(a, name), getattr(b, name)), name
+
+
+# ------------------------------------------------------------------ caller-supplied amax
+def _small_group(seed=41):
+    w = synth.grouped_nvfp4(total_rows=640, k=256, parts=4, seed=seed)
+    x = w.tensors["x"].view(torch.int16).numpy().view(np.uint16)
+    return x, w.params["split_sections"], w.params["sign_mask"]
+
+
+def test_given_measured_amax_reproduces_plain_call(orc):
+    """Supplying the maxima the plain call measures changes nothing."""
+    x, sec, mask = _small_group()
+    a = orc.group_rht_quant_nvfp4(x, sec, mask, 3)
+    b = orc.group_rht_quant_nvfp4(x, sec, mask, 3, amax_in=(a.row_amax, a.col_amax))
+    for n in ("row_codes", "row_scales", "row_global", "col_codes", "col_scales", "col_global"):
+        assert np.array_equal(getattr(a, n), getattr(b, n)), n
+
+
+def test_measured_amax_matches_closed_form(orc):
+    """Row amax = max |x|; column amax = max |BF16(0.25 * H16 D x)| with H16 the
+    Sylvester matrix, on small-integer inputs where every sum is exact in FP32."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(7)
+    v = rng.integers(-40, 41, size=(256, 128)).astype(np.float32)
+    x = (v.view(np.uint32) >> 16).astype(np.uint16)
+    mask = 0x35A1
+    out = orc.group_rht_quant_nvfp4(x, [128, 128], mask, 3, threads=2)
+    D = np.array([-1.0 if (mask >> t) & 1 else 1.0 for t in range(16)])
+    H = hadamard(16).astype(np.float64)
+    for s in range(2):
+        xs = v[128 * s:128 * (s + 1)].astype(np.float64)
+        assert out.row_amax[s] == np.abs(xs).max()
+        blocks = xs.reshape(8, 16, 128)                       # [block][t][column]
+        y = 0.25 * np.einsum("it,btc->bic", H, D[None, :, None] * blocks)
+        # y is exact in FP32 (integers / 4); the column values are its BF16 roundings
+        want = torch.tensor(np.float32(np.abs(y).max())).to(torch.bfloat16).float().item()
+        assert out.col_amax[s] == np.float32(want)
+
+
+def test_small_given_amax_saturates(orc):
+    """A supplied amax below the data's: blocks above it take the top scale 0x7E and
+    their largest elements the top code 6 (saturation, never NaN)."""
+    x, sec, mask = _small_group(43)
+    a = orc.group_rht_quant_nvfp4(x, sec, mask, 1)
+    b = orc.group_rht_quant_nvfp4(x, sec, mask, 1, amax_in=(a.row_amax / 4, None))
+    assert (b.row_scales <= 0x7E).all() and (b.row_scales != 0x7F).all()
+    assert (b.row_scales == 0x7E).sum() > (a.row_scales == 0x7E).sum()
+    f = x.view(np.uint16).astype(np.uint32) << 16
+    xf = f.view(np.float32).reshape(x.shape)
+    r, c = np.unravel_index(np.argmax(np.abs(xf[:sec[0]])), xf[:sec[0]].shape)
+    code = (b.row_codes[r * x.shape[1] // 2 + c // 2] >> (4 * (c & 1))) & 7
+    assert code == 7
+
+
+def test_large_given_amax_keeps_error_bound(orc):
+    """A supplied amax above the data's only coarsens the scales: dequantized values
+    stay within half a code step of the inputs."""
+    x, sec, mask = _small_group(44)
+    a = orc.group_rht_quant_nvfp4(x, sec, mask, 1)
+    b = orc.group_rht_quant_nvfp4(x, sec, mask, 1, amax_in=(a.row_amax * 3, None))
+    assert (b.row_global > a.row_global).all()
+    # every block keeps a nonzero scale and codes that dequantize close to x
+    k = x.shape[1]
+    xf = ((x.astype(np.uint32) << 16).view(np.float32)).reshape(-1, k)
+    R0 = 0
+    for s, m in enumerate(sec):
+        g = b.row_global[s]
+        for r in range(R0, R0 + m, 37):
+            for kb in range(0, k // 16, 5):
+                sc = b.row_scales[r * (k // 16) + kb]
+                d = np.float32(e4m3([sc])[0]) * g
+                for t in range(16):
+                    c = kb * 16 + t
+                    code = (b.row_codes[r * k // 2 + c // 2] >> (4 * (c & 1))) & 0xF
+                    val = [0, .5, 1, 1.5, 2, 3, 4, 6][code & 7] * (-1 if code & 8 else 1) * d
+                    assert abs(val - xf[r, c]) <= 1.0 * d + 1e-30
+        R0 += m
