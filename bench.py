@@ -228,8 +228,9 @@ def main():
 # HBM bytes per call from the committed counter summaries (rocprofv3 --pmc), used
 # only while the kernel sources they were taken on are unchanged.
 TRAFFIC_SUMMARIES = {"grouped_nvfp4_rht": "profiles/grouped_nvfp4_rht_16384x4096_hbm_traffic.md"}
-KERNEL_SOURCES = ["nvfp4_quantization_amd/csrc/mxq_nvfp4.hip", "nvfp4_quantization_amd/csrc/mxq_device.hpp",
-                  "nvfp4_quantization_amd/csrc/mxq_internal.hpp"]
+KERNEL_SOURCES = ["nvfp4_quantization_amd/csrc/mxq_nvfp4.hip", "nvfp4_quantization_amd/csrc/mxq_nvfp4_impl.hpp",
+                  "nvfp4_quantization_amd/csrc/mxq_nvfp4_quant_rne.hip",
+                  "nvfp4_quantization_amd/csrc/mxq_device.hpp", "nvfp4_quantization_amd/csrc/mxq_internal.hpp"]
 
 
 def kernel_source_digest() -> str:

@@ -196,6 +196,39 @@ mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
                                      const mxq_fp8_out* fp8_rowwise,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The grouped call with caller-supplied section maxima (a single pass over x) and
+ * the measured maxima out, for scaling the next step by this step's maxima.
+ *
+ * amax (may be NULL: as mxq_group_rht_quant_nvfp4):
+ *   row_in, col_in    device float[num_sections]: the A of the tensor scales,
+ *                     g = fl(max(A, F(1e-10)) * F(1/2688)), instead of the measured
+ *                     maxima; given for every requested NVFP4 direction or for none
+ *                     (else MXQ_ERR_INVALID_ARGUMENT).  Blocks above the supplied A
+ *                     saturate (scale 0x7E, codes at +-6).
+ *   row_out, col_out  device float[num_sections] or NULL: the measured maxima of this
+ *                     call (max |x| without NaNs; max |BF16(H16 D x / 4)| without NaNs),
+ *                     written for the requested directions; an empty section gives 0.
+ * With supplied maxima the amax pass is skipped: the workspace only carries the scale
+ * tables, and the maxima out are gathered with atomic maxima while quantizing.
+ * Reading of TransformerEngine PR #2564 (the workspace / size-query pattern) for a
+ * delayed-scaling variant of the same cast; everything else as above.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const float* row_in;
+    const float* col_in;
+    float*       row_out;
+    float*       col_out;
+} mxq_amax;
+
+mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k,
+                                               const int64_t* split_sections, int64_t num_sections,
+                                               uint16_t rht_sign_mask, uint32_t flags, const mxq_sr* sr,
+                                               const mxq_nvfp4_out* rowwise,
+                                               const mxq_nvfp4_out* columnwise,
+                                               const mxq_fp8_out* fp8_rowwise, const mxq_amax* amax,
+                                               void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

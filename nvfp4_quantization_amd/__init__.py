@@ -24,7 +24,8 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_MISALIGNED",
           3: "MXQ_ERR_WORKSPACE_TOO_SMALL", 4: "MXQ_ERR_UNSUPPORTED", 5: "MXQ_ERR_HIP"}
 
 EXPORTED = ("mxq_status_string", "mxq_version", "mxq_quant_fp8_1x128", "mxq_hadamard_quant_fp8",
-            "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4")
+            "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4",
+            "mxq_group_rht_quant_nvfp4_with_amax")
 
 
 class MxqError(RuntimeError):
@@ -43,6 +44,11 @@ class _FP8Out(ctypes.Structure):
 
 class _SR(ctypes.Structure):
     _fields_ = [("seed", ctypes.c_uint64), ("row_offsets", ctypes.c_void_p), ("col_offsets", ctypes.c_void_p)]
+
+
+class _Amax(ctypes.Structure):
+    _fields_ = [("row_in", ctypes.c_void_p), ("col_in", ctypes.c_void_p),
+                ("row_out", ctypes.c_void_p), ("col_out", ctypes.c_void_p)]
 
 
 _lib = None
@@ -69,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_rht_quant_nvfp4.restype = ctypes.c_int
         L.mxq_group_rht_quant_nvfp4.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
                                                 p, p, p, p, ctypes.c_size_t, p]
+        L.mxq_group_rht_quant_nvfp4_with_amax.restype = ctypes.c_int
+        L.mxq_group_rht_quant_nvfp4_with_amax.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
+                                                          p, p, p, p, p, ctypes.c_size_t, p]
         _lib = L
     return _lib
 
@@ -160,6 +169,8 @@ class NVFP4Result:
     col_global: Optional[torch.Tensor] = None     # [S] float32
     fp8_codes: Optional[torch.Tensor] = None      # [total][k] uint8
     fp8_scales: Optional[torch.Tensor] = None     # [total][k/128] float32
+    row_amax: Optional[torch.Tensor] = None       # [S] float32, measured (when asked for)
+    col_amax: Optional[torch.Tensor] = None       # [S] float32, measured (when asked for)
 
 
 def mxq_group_rht_quant_nvfp4_workspace_size(total_rows: int, k: int, num_sections: int, flags: int) -> int:
@@ -209,7 +220,11 @@ class GroupedNVFP4:
     def __init__(self, x: torch.Tensor, split_sections: Sequence[int], rht_sign_mask: int, flags: int,
                  seed: Optional[int] = None, row_offsets: Optional[Sequence[int]] = None,
                  col_offsets: Optional[Sequence[int]] = None, out: Optional[NVFP4Result] = None,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, amax_in: Optional[tuple] = None,
+                 amax_out: bool = False):
+        """amax_in: None, or (row maxima, column maxima) device float32 [S] tensors (None
+        for a direction not requested) that replace the measured section maxima;
+        amax_out: also return the measured maxima (out.row_amax / out.col_amax)."""
         x = _bf16_bits(x)
         if not x.is_contiguous():
             raise ValueError("x must be contiguous [total_rows][k]")
@@ -229,6 +244,16 @@ class GroupedNVFP4:
                               o.col_global.data_ptr() if o.col_global is not None else None)
         self._fp8 = _FP8Out(o.fp8_codes.data_ptr() if o.fp8_codes is not None else None,
                             o.fp8_scales.data_ptr() if o.fp8_scales is not None else None)
+        self._amax = None
+        if amax_in is not None or amax_out:
+            f32 = dict(dtype=torch.float32, device=x.device)
+            if amax_out:
+                o.row_amax = torch.zeros((S,), **f32) if flags & MXQ_ROWWISE else None
+                o.col_amax = torch.zeros((S,), **f32) if flags & MXQ_COLUMNWISE else None
+            self._amax_in = [None if a is None else a.contiguous().float() for a in (amax_in or (None, None))]
+            self._amax = _Amax(*[None if a is None else a.data_ptr() for a in self._amax_in],
+                               o.row_amax.data_ptr() if o.row_amax is not None else None,
+                               o.col_amax.data_ptr() if o.col_amax is not None else None)
         self._sr = None
         if seed is not None and (row_offsets is not None or col_offsets is not None):
             self._ro = (ctypes.c_uint64 * S)(*row_offsets) if row_offsets is not None else None
@@ -238,12 +263,20 @@ class GroupedNVFP4:
                            ctypes.addressof(self._co) if self._co is not None else None)
 
     def __call__(self, stream=None) -> NVFP4Result:
-        st = lib().mxq_group_rht_quant_nvfp4(
-            _ptr(self.x), self.k, ctypes.addressof(self.sections), self.S, self.mask, self.flags,
-            ctypes.addressof(self._sr) if self._sr is not None else None,
-            ctypes.addressof(self._row), ctypes.addressof(self._col), ctypes.addressof(self._fp8),
-            _ptr(self.workspace), self.workspace.numel(), _stream(stream))
-        _check(st, "mxq_group_rht_quant_nvfp4")
+        if self._amax is None:
+            st = lib().mxq_group_rht_quant_nvfp4(
+                _ptr(self.x), self.k, ctypes.addressof(self.sections), self.S, self.mask, self.flags,
+                ctypes.addressof(self._sr) if self._sr is not None else None,
+                ctypes.addressof(self._row), ctypes.addressof(self._col), ctypes.addressof(self._fp8),
+                _ptr(self.workspace), self.workspace.numel(), _stream(stream))
+            _check(st, "mxq_group_rht_quant_nvfp4")
+        else:
+            st = lib().mxq_group_rht_quant_nvfp4_with_amax(
+                _ptr(self.x), self.k, ctypes.addressof(self.sections), self.S, self.mask, self.flags,
+                ctypes.addressof(self._sr) if self._sr is not None else None,
+                ctypes.addressof(self._row), ctypes.addressof(self._col), ctypes.addressof(self._fp8),
+                ctypes.addressof(self._amax), _ptr(self.workspace), self.workspace.numel(), _stream(stream))
+            _check(st, "mxq_group_rht_quant_nvfp4_with_amax")
         return self.out
 
 

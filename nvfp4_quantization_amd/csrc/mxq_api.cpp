@@ -92,6 +92,17 @@ mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
                                      const mxq_nvfp4_out* rowwise, const mxq_nvfp4_out* columnwise,
                                      const mxq_fp8_out* fp8_rowwise,
                                      void* workspace, size_t workspace_bytes, void* stream) {
+    return mxq_group_rht_quant_nvfp4_with_amax(x_bf16, k, split_sections, num_sections, rht_sign_mask, flags, sr,
+                                               rowwise, columnwise, fp8_rowwise, nullptr, workspace,
+                                               workspace_bytes, stream);
+}
+
+mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k,
+                                               const int64_t* split_sections, int64_t num_sections,
+                                               uint16_t rht_sign_mask, uint32_t flags, const mxq_sr* sr,
+                                               const mxq_nvfp4_out* rowwise, const mxq_nvfp4_out* columnwise,
+                                               const mxq_fp8_out* fp8_rowwise, const mxq_amax* amax,
+                                               void* workspace, size_t workspace_bytes, void* stream) {
     // ---- checks (nothing is enqueued before all of them pass)
     if (k <= 0 || !split_sections || num_sections < 1) return MXQ_ERR_INVALID_ARGUMENT;
     if (num_sections > MXQ_MAX_SECTIONS) return MXQ_ERR_UNSUPPORTED;
@@ -124,6 +135,12 @@ mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
                 !aligned(columnwise->global_scales, 4)))
         return MXQ_ERR_MISALIGNED;
     if (fp8 && total_rows > 0 && (!aligned(fp8_rowwise->codes, 16) || !aligned(fp8_rowwise->scales, 4)))
+        return MXQ_ERR_MISALIGNED;
+    // caller-supplied maxima: all or none of the requested NVFP4 directions
+    const bool given = amax && (amax->row_in || amax->col_in);
+    if (given && ((row && !amax->row_in) || (col && !amax->col_in))) return MXQ_ERR_INVALID_ARGUMENT;
+    if (amax && (!aligned(amax->row_in, 4) || !aligned(amax->col_in, 4) || !aligned(amax->row_out, 4) ||
+                 !aligned(amax->col_out, 4)))
         return MXQ_ERR_MISALIGNED;
     const bool sr_row = row && sr && sr->row_offsets;
     const bool sr_col = col && sr && sr->col_offsets;
@@ -186,6 +203,14 @@ mxq_status mxq_group_rht_quant_nvfp4(const uint16_t* x_bf16, int64_t k,
             g.col_off[i] = sr_col ? sr->col_offsets[s0 + i] : 0;
         }
         g.tt_start[ns] = (int32_t)tt;
+        if (given) {
+            g.amax_in_row = row ? amax->row_in + s0 : nullptr;
+            g.amax_in_col = col ? amax->col_in + s0 : nullptr;
+        }
+        if (amax) {
+            g.amax_out_row = (row && amax->row_out) ? amax->row_out + s0 : nullptr;
+            g.amax_out_col = (col && amax->col_out) ? amax->col_out + s0 : nullptr;
+        }
         g.total_tiles = (int32_t)(tt * n_ct);
         if (mxq::launch_nvfp4_group(g, flags, st) != hipSuccess) return MXQ_ERR_HIP;
         row0 += rows_group;

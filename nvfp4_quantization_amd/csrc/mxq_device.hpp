@@ -13,8 +13,8 @@
 //  * The E4M3 / E2M1 / BF16 conversions use gfx950's hardware conversions.  Over
 //    all 2^32 FP32 inputs they equal nearest-even with saturation for every
 //    finite input below 464 (E4M3) and every non-NaN input (E2M1, BF16); the
-//    kernels never pass a NaN or a value >= 464 to the E4M3 conversion except on
-//    the NaN path, which rewrites the result.
+//    kernels clamp to 448 (or never exceed 464) before the E4M3 conversion, and
+//    pass a NaN to it only on the NaN path, which rewrites the result.
 #pragma once
 
 #include <hip/hip_runtime.h>

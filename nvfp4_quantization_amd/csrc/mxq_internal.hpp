@@ -29,7 +29,8 @@ hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- grouped NVFP4
 // One launch group per at most kGroupSections sections.  A group runs two kernels
-// on the caller's stream, one wave per 128 x 128 tile in each:
+// on the caller's stream, one wave per 128 x 128 tile in each (with a caller-supplied
+// amax, a small per-section kernel that builds the tables replaces the first):
 //   amax    max |x| and max |H16 D x| of the tile into a per-tile partial; the
 //           section's last tile (a counter tells which) folds the partials into
 //           the two tensor scales, writes the section's (d, 1/d) tables and resets
@@ -62,8 +63,20 @@ struct Nvfp4Group {
     int32_t tt_start[kGroupSections + 1];    // first token tile of each section (group-relative)
     uint64_t row_off[kGroupSections];
     uint64_t col_off[kGroupSections];
+    // caller-supplied section maxima (at the group's first section; both null: measure)
+    const float* amax_in_row;
+    const float* amax_in_col;
+    // measured section maxima out (at the group's first section; null: not wanted)
+    float* amax_out_row;
+    float* amax_out_col;
 };
 hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
+// The quant kernel's variant families (one translation unit each): nearest-even or
+// stochastic rounding, with or without measured maxima out (supplied maxima).
+hipError_t launch_quant_rne(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
+hipError_t launch_quant_sr(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
+hipError_t launch_quant_rne_aout(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
+hipError_t launch_quant_sr_aout(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
 
 // Workspace layout (byte offsets):
 //   kCtrlOffset    counter of section s at word kCtrlStride * s (own 256-byte line)

@@ -1,651 +1,11 @@
 // mxq_nvfp4.hip -- grouped NVFP4 quantization with a 16-point RHT on the
-// column-wise operand (gfx950).
-//
-// The method: TransformerEngine PR #2564 "[NVFP4][MOE] Bug Fix for NVFP4 Grouped
-// Quant" (Greptile summary: grouped row-wise + column-wise RHT cast fusion, the
-// workspace supplied by the caller) and the review comments of PR #2555 on
-// quantizer.cpp (RHT only for the column-wise operand; the RHT(x^T) intermediate
-// has the input dtype; a separate column-wise RNG).
-//
-// The FP32 tensor scale of a section needs the section's amax before any code is
-// final, so a call runs two kernels per group of sections, one wave per 128 x 128
-// tile in each:
-//
-//   k_nvfp4_amax   max |x| and max |H16 D x| of the tile (a per-tile partial).
-//                  The last tile of a section to finish (an agent-scope counter
-//                  tells which) folds the section's partials into the two tensor
-//                  scales, writes the section's scale tables and puts the counter
-//                  back to zero, so the workspace is ready for the next call.
-//   k_nvfp4_quant  re-reads the tile (usually from the Infinity Cache) and writes
-//                  every requested output.
-//
-// Scale tables: for each direction and E4M3 scale code c the quantizer divides by
-// d = fl(E4M3(c) * g).  The table holds (d, y = fl(1/d), ym): ym is a multiplier
-// whose plain product fl(u * ym) picks the same E2M1 code as fl(u / d) for every
-// BF16 u, or negative when there is none.  fl(u * ym) and fl(u / d) differ by a
-// few FP32 ulps at most, so a BF16 u can only be decided differently when u / d
-// lies within about 2^-21 (relative) of one of the seven E2M1 rounding boundaries
-// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; BF16 values are 2^-8 apart, so only the two
-// BF16 neighbours of each boundary times d can, and those fourteen are checked
-// against the exact division for ym = y and its nearest neighbours.  The codes of
-// a block come from one multiply per element when its scale code has a
-// multiplier, else (and always with stochastic rounding, which needs the exact
-// quotient) from the exact division.  Column values enter unscaled: BF16(x/4) =
-// BF16(x)/4 and fl((u/4)/d) = fl(u/(4d)) whenever x/4 is a normal number, and
-// where it is not, both quotients are far below the smallest E2M1 step with the
-// same sign, so the column tables are built for 4d and the 1/4 costs nothing per
-// element.
-#include "mxq_device.hpp"
-#include "mxq_internal.hpp"
+// column-wise operand (gfx950): the amax, supplied-amax and empty-group kernels and
+// the launch plan; the quant kernel variants are instantiated in
+// mxq_nvfp4_quant_*.hip.  The method and the kernels' design are described in
+// mxq_nvfp4_impl.hpp.
+#include "mxq_nvfp4_impl.hpp"
 
 namespace mxq {
-
-namespace {
-
-__device__ __forceinline__ uint64_t ws_load64(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ws_store64(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Tensor scale g = fl(max(A, F(1e-10)) * F(1/2688)).
-__device__ __forceinline__ float tensor_scale(float amax) {
-    return (amax > k_floor() ? amax : k_floor()) * k_inv2688();
-}
-
-// E4M3 block-scale code of a 1x16 block with amax a (a BF16 value):
-// E4M3(fl(fl(a * F(1/6)) / g)), yg = fl(1/g).
-__device__ __forceinline__ uint32_t block_code(float a, float g, float yg) {
-    return e4m3_code(div_rn(a * k_inv6(), g, yg));
-}
-
-__device__ __forceinline__ uint32_t e2m1_one(float q) { return e2m1_pack2<0>(0u, q, q) & 0xFu; }
-
-// True when fl(u * ym) and fl(u / d) have the same E2M1 code for every BF16 u
-// (d > 0 finite, y = fl(1/d), ym within a few ulps of y); see the header comment.
-__device__ bool product_decides_like_quotient(float d, float y, float ym) {
-    const float taus[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < 7; ++i) {
-        const uint32_t lo = __builtin_bit_cast(uint32_t, taus[i] * d) & 0xFFFF0000u;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float u = __builtin_bit_cast(float, lo + (uint32_t)j * 0x10000u);
-            ok &= e2m1_one(u * ym) == e2m1_one(div_rn(u, d, y));
-        }
-    }
-    return ok;
-}
-
-// The multiplier for the product path of divisor d: fl(1/d) or a neighbour a few
-// ulps away that decides every BF16 input like the exact quotient (exact
-// quotients that fall on rounding boundaries are common, because d and the
-// boundaries are short binary numbers); negative when none does.
-__device__ float product_multiplier(float d, float y) {
-    const int deltas[7] = {0, -1, 1, -2, 2, -3, 3};
-    for (int i = 0; i < 7; ++i) {
-        const float ym = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, y) + (uint32_t)deltas[i]);
-        if (product_decides_like_quotient(d, y, ym)) return ym;
-    }
-    return -y;
-}
-
-// Running max |x| over packed BF16 pairs, NaN ignored.
-__device__ __forceinline__ uint32_t absmax_nonan_pairs(uint32_t acc, uint32_t w) {
-    return absmax_pk_nonan(acc, w);
-}
-
-__device__ __forceinline__ u32x4 block_random(uint64_t seed, uint64_t off, uint64_t beta) {
-    u32x4 c = {(uint32_t)off, (uint32_t)(off >> 32), (uint32_t)beta, (uint32_t)(beta >> 32)};
-    return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
-}
-
-// Butterfly h = 1, 2, 4, 8 over 16 values.
-__device__ __forceinline__ void butterfly16(float (&v)[16]) {
-#pragma unroll
-    for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i & h) continue;
-            const float x0 = v[i], x1 = v[i + h];
-            v[i] = x0 + x1;
-            v[i + h] = x0 - x1;
-        }
-    }
-}
-
-// BF16 element of a packed pair widened to FP32 with its sign flipped when
-// neg = 0x80000000 (adding the top bit flips it).
-__device__ __forceinline__ float lo_signed(uint32_t p, uint32_t neg) {
-    return __builtin_bit_cast(float, (p << 16) + neg);
-}
-__device__ __forceinline__ float hi_signed(uint32_t p, uint32_t neg) {
-    return __builtin_bit_cast(float, (p & 0xFFFF0000u) ^ neg);
-}
-__device__ __forceinline__ uint32_t sign_of_row(uint32_t mask, int t) { return ((mask >> t) & 1u) << 31; }
-
-// FP32 value of BF16(v) (nearest-even), one conversion.
-__device__ __forceinline__ float round_bf16(float v) { return __builtin_bit_cast(float, pack_bf16(0.0f, v)); }
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v = __builtin_fmaxf(v, shfl_xor_f32(v, o));
-    return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t w = shfl_xor_u32(v, o);
-        v = w > v ? w : v;
-    }
-    return v;
-}
-__device__ __forceinline__ uint32_t group8_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-        uint32_t w = shfl_xor_u32(v, o);
-        v = w > v ? w : v;
-    }
-    return v;
-}
-
-// Section of token tile T (uniform): the last section starting at or before T
-// (empty sections start where the next one does, so they are skipped).
-__device__ __forceinline__ int section_of(const Nvfp4Group& G, int T) {
-    int s = 0;
-    for (int i = 1; i < G.num_sections; ++i) s = G.tt_start[i] <= T ? i : s;
-    return s;
-}
-
-// max |v_i| over 16 values: a tree of three-input maxima (depth 3, 8 operations).
-// NaNs are ignored (callers that care detect them separately).
-__device__ __forceinline__ float absmax16(const float (&v)[16]) {
-    auto m3 = [](float a, float b, float c) {
-        return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)), __builtin_fabsf(c));
-    };
-    const float a = m3(v[0], v[1], v[2]), b = m3(v[3], v[4], v[5]), c = m3(v[6], v[7], v[8]);
-    const float d = m3(v[9], v[10], v[11]), e = m3(v[12], v[13], v[14]);
-    return __builtin_fmaxf(m3(a, b, c), m3(d, e, v[15]));
-}
-
-// E2M1 codes of 8 values u[0..7] (element 2i in the low nibble of byte i):
-// nearest-even of u * y (MUL), of fl(u / d), or stochastic with random bytes
-// r0 .. r0+7 of rnd.
-enum class Enc { Mul, Div, Sr };
-template <Enc E>
-__device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, const u32x4& rnd, int r0) {
-    uint32_t c = 0;
-    if (E == Enc::Mul) {
-        c = e2m1_pack2<0>(c, u[0] * y, u[1] * y);
-        c = e2m1_pack2<1>(c, u[2] * y, u[3] * y);
-        c = e2m1_pack2<2>(c, u[4] * y, u[5] * y);
-        c = e2m1_pack2<3>(c, u[6] * y, u[7] * y);
-    } else if (E == Enc::Div) {
-        c = e2m1_pack2<0>(c, div_rn(u[0], d, y), div_rn(u[1], d, y));
-        c = e2m1_pack2<1>(c, div_rn(u[2], d, y), div_rn(u[3], d, y));
-        c = e2m1_pack2<2>(c, div_rn(u[4], d, y), div_rn(u[5], d, y));
-        c = e2m1_pack2<3>(c, div_rn(u[6], d, y), div_rn(u[7], d, y));
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t c0 = e2m1_sr(div_rn(u[2 * i], d, y), rbyte(rnd, r0 + 2 * i));
-            const uint32_t c1 = e2m1_sr(div_rn(u[2 * i + 1], d, y), rbyte(rnd, r0 + 2 * i + 1));
-            c |= (c0 | (c1 << 4)) << (8 * i);
-        }
-    }
-    return c;
-}
-
-// ---------------------------------------------------------------- amax work
-// A quarter tile: rows 32q .. 32q+31; lane (h, c) holds rows 16h .. 16h+15 of it
-// and columns 4c .. 4c+3 (one 8-byte load per row).
-__device__ __forceinline__ void load_quarter(uint2 (&v)[16], const uint16_t* base, int64_t k, int q) {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) v[t] = *reinterpret_cast<const uint2*>(base + (int64_t)(32 * q + t) * k);
-}
-
-// Row max |x| of the lane's 64 rows x 4 columns of a tile, NaN ignored (the rare
-// path: the quarters are loaded again).
-__device__ uint32_t lane_absmax_nonan(const uint16_t* base, int64_t k) {
-    uint32_t m = 0;
-#pragma unroll 1
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll 1
-        for (int t = 0; t < 16; ++t) {
-            const uint2 w = *reinterpret_cast<const uint2*>(base + (int64_t)(32 * q + t) * k);
-            m = absmax_nonan_pairs(absmax_nonan_pairs(m, w.x), w.y);
-        }
-    }
-    return m;
-}
-
-// mr: running max |x| as BF16 bits (ROW without COL: packed integer maxima,
-// NaN ignored); rmax: running FP32 max |x| (ROW with COL, from the widened values
-// the butterfly needs anyway; a NaN input can spoil it, which nan reports);
-// mc: running max |H16 D x|.
-template <bool ROW, bool COL>
-__device__ __forceinline__ void amax_quarter(const uint2 (&v)[16], uint32_t sign_mask, uint32_t& mr, float& rmax,
-                                             float& mc, bool& nan) {
-    if (ROW && !COL) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) m = absmax_pk(absmax_pk(m, v[t].x), v[t].y);
-        m = fold_pk(m);
-        if (m > 0x7F80u) {                           // a NaN: take the maximum without it
-            m = 0;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) m = absmax_nonan_pairs(absmax_nonan_pairs(m, v[t].x), v[t].y);
-        }
-        mr = m > mr ? m : mr;
-    }
-    if (COL) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float f[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const uint32_t w = j < 2 ? v[t].x : v[t].y;
-                const uint32_t neg = sign_of_row(sign_mask, t);
-                f[t] = (j & 1) ? hi_signed(w, neg) : lo_signed(w, neg);
-            }
-            if (ROW) {
-#pragma unroll
-                for (int t = 0; t < 16; ++t) rmax = __builtin_fmaxf(rmax, __builtin_fabsf(f[t]));
-            }
-            butterfly16(f);
-            nan |= f[0] != f[0];                    // a NaN input reaches every output
-            // NaN outputs are quiet, and max ignores them
-#pragma unroll
-            for (int t = 0; t < 16; ++t) mc = __builtin_fmaxf(mc, __builtin_fabsf(f[t]));
-        }
-    }
-}
-
-// ---------------------------------------------------------------- quant work
-// Tile in registers: lane (tb, cc) holds rows 16 tb .. 16 tb + 15 and columns
-// 16 cc .. 16 cc + 15 as p[t][half] (8 BF16 each).
-#define P(t, i) ((i) == 0 ? p[t][0].x : (i) == 1 ? p[t][0].y : (i) == 2 ? p[t][0].z : (i) == 3 ? p[t][0].w \
-               : (i) == 4 ? p[t][1].x : (i) == 5 ? p[t][1].y : (i) == 6 ? p[t][1].z : p[t][1].w)
-
-// Hide the tile's provenance from the compiler (no instruction is emitted).
-// Otherwise it reuses values computed from the tile by an earlier pass in a later
-// one, keeping hundreds of them live across the passes.
-__device__ __forceinline__ void launder(uint4 (&p)[16][2]) {
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(p[t][h].x), "+v"(p[t][h].y), "+v"(p[t][h].z), "+v"(p[t][h].w));
-}
-
-struct BlockOut {
-    uint2 codes;          // 16 E2M1 codes
-    uint32_t scale;       // E4M3 scale byte
-    bool unsafe;          // (Enc::Mul) the scale code needs the exact division
-};
-
-// 16 codes of one block of values u with scale code sc (nan: the block holds a NaN).
-template <Enc E>
-__device__ __forceinline__ BlockOut encode_block(const float (&u)[16], uint32_t sc, bool nan, const float4* tab,
-                                                 const u32x4& rnd) {
-    const float4 e = tab[sc & 0x7Fu];
-    const float d = e.x, y = E == Enc::Mul ? __builtin_fabsf(e.z) : e.y;
-    BlockOut o;
-    o.codes = make_uint2(encode8<E>(u, d, y, rnd, 0), encode8<E>(u + 8, d, y, rnd, 8));
-    if (nan || sc == 0u) o.codes = make_uint2(0u, 0u);
-    o.scale = nan ? 0x7Fu : sc;
-    o.unsafe = e.z < 0.0f;
-    return o;
-}
-
-// Column j of the lane: rows 16 tb .. +15 after the sign flip and the butterfly,
-// rounded to BF16 (unscaled; the column tables carry the 1/4).
-template <Enc E>
-__device__ __forceinline__ BlockOut column_block(const uint4 (&p)[16][2], int j, uint32_t sign_mask, float g_c,
-                                                 float yg_c, const float4* tab_c, const u32x4& rnd) {
-    float v[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const uint32_t w = P(t, j >> 1);
-        const uint32_t neg = sign_of_row(sign_mask, t);
-        v[t] = (j & 1) ? hi_signed(w, neg) : lo_signed(w, neg);
-    }
-    butterfly16(v);
-    const bool nan = v[0] != v[0];                   // a NaN input reaches every output
-    const float m = absmax16(v);
-    // block amax of the column values BF16(v/4) = BF16(max |v|) / 4
-    const uint32_t sc = block_code(0.25f * round_bf16(m), g_c, yg_c);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) v[t] = round_bf16(v[t]);
-    return encode_block<E>(v, sc, nan, tab_c, rnd);
-}
-
-// Row t of the lane: columns 16 cc .. +15 (one row-wise block).  FAST: no NaN
-// anywhere in the wave's tile, so max |x| is the FP32 maximum of the widened values;
-// otherwise packed integer maxima of |x| bits, where a NaN shows as a value above
-// 0x7F80.
-template <Enc E, bool FAST>
-__device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, float g_r, float yg_r,
-                                              const float4* tab_r, const u32x4& rnd, uint32_t& m_out) {
-    float u[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        u[2 * i] = lo_bf16(P(t, i));
-        u[2 * i + 1] = hi_bf16(P(t, i));
-    }
-    uint32_t m;                                      // max |x| (BF16 bits)
-    if (FAST) {
-        m = __builtin_bit_cast(uint32_t, absmax16(u)) >> 16;
-    } else {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
-        m = fold_pk(acc);
-    }
-    m_out = m;
-    const uint32_t sc = block_code(bf16_mag(m), g_r, yg_r);
-    return encode_block<E>(u, sc, m > 0x7F80u, tab_r, rnd);
-}
-
-// The row pass of a tile: 16 row blocks per lane.  FAST (the column pass ran and
-// reports NaN column blocks in nan): block maxima from the FP32 widened values,
-// then the lanes whose sub-tile holds a NaN redo all their rows with packed integer
-// maxima, where a NaN shows.
-template <bool SR, bool FAST>
-__device__ __forceinline__ void row_pass(const Nvfp4Group& G, uint4 (&p)[16][2], int s, int64_t row0, int64_t c0,
-                                         int64_t r_local0, float g_r, float yg_r, const float4* tab_r, bool nan) {
-    const int64_t k = G.k;
-    const u32x4 no_rnd = {0, 0, 0, 0};
-    auto put = [&](int t, const BlockOut& o) {
-        const int64_t row = row0 + t;
-        *reinterpret_cast<uint2*>(G.row_codes + row * (k >> 1) + (c0 >> 1)) = o.codes;
-        G.row_scales[row * (k >> 4) + (c0 >> 4)] = (uint8_t)o.scale;
-    };
-    auto rnd_of = [&](int t) {
-        return block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
-    };
-    uint32_t m;
-    if (SR && G.sr_row) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            put(t, row_block<Enc::Sr, FAST>(p, t, g_r, yg_r, tab_r, rnd_of(t), m));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-        uint32_t redo = 0;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const BlockOut o = row_block<Enc::Mul, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m);
-            put(t, o);
-            redo |= (uint32_t)o.unsafe << t;
-            if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
-        }
-        if (__ballot(redo != 0) != 0) {
-            launder(p);
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                if ((redo >> t) & 1u) put(t, row_block<Enc::Div, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m));
-        }
-    }
-    if (FAST && __ballot(nan) != 0) {
-        // rare: the lane's rows again, loaded afresh one at a time, so that nothing of
-        // the main path stays live for this branch
-        asm volatile("" ::: "memory");
-        if (nan) {
-            const uint16_t* xr = G.x + row0 * k + c0;
-#pragma unroll 1
-            for (int t = 0; t < 16; ++t) {
-                uint4 q[16][2];
-                q[0][0] = *reinterpret_cast<const uint4*>(xr + t * k);
-                q[0][1] = *reinterpret_cast<const uint4*>(xr + t * k + 8);
-                if (SR && G.sr_row) put(t, row_block<Enc::Sr, false>(q, 0, g_r, yg_r, tab_r, rnd_of(t), m));
-                else put(t, row_block<Enc::Div, false>(q, 0, g_r, yg_r, tab_r, no_rnd, m));
-            }
-        }
-    }
-}
-
-}  // namespace
-
-// ---------------------------------------------------------------- the kernels
-template <bool ROW, bool COL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_nvfp4_amax(const Nvfp4Group G) {
-    const int lane = threadIdx.x;
-    const int b = blockIdx.x;
-    const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
-    const int s = section_of(G, T);
-    const uint16_t* base = G.x + ((int64_t)T * kTileRows + (lane >> 5) * 16) * G.k + (int64_t)C * kTileCols + (lane & 31) * 4;
-
-    uint32_t mr = 0;
-    float rmax = 0.0f, mc = 0.0f;
-    bool nan = false;
-    uint2 q0[16], q1[16];
-    load_quarter(q0, base, G.k, 0);
-    load_quarter(q1, base, G.k, 1);
-    amax_quarter<ROW, COL>(q0, G.sign_mask, mr, rmax, mc, nan);
-    load_quarter(q0, base, G.k, 2);
-    amax_quarter<ROW, COL>(q1, G.sign_mask, mr, rmax, mc, nan);
-    load_quarter(q1, base, G.k, 3);
-    amax_quarter<ROW, COL>(q0, G.sign_mask, mr, rmax, mc, nan);
-    amax_quarter<ROW, COL>(q1, G.sign_mask, mr, rmax, mc, nan);
-    if (ROW && COL) mr = __builtin_bit_cast(uint32_t, rmax) >> 16;
-    mr = wave_max_u32(mr);
-    mc = wave_max_f32(mc);
-    if (ROW && COL) {
-        // pin the main path's results before the rare branch, so that none of its
-        // work is scheduled after it
-        asm volatile("" : "+v"(mr), "+v"(mc));
-        if (__ballot(nan) != 0) mr = wave_max_u32(lane_absmax_nonan(base, G.k));
-    }
-
-    if (b == 0) {
-        // empty sections: the tensor scale of an all-zero section
-        for (int i = lane; i < G.num_sections; i += 64) {
-            if (G.tt_start[i + 1] != G.tt_start[i]) continue;
-            if (ROW) G.row_global[i] = tensor_scale(0.0f);
-            if (COL) G.col_global[i] = tensor_scale(0.0f);
-        }
-    }
-
-    const int first = G.tt_start[s] * G.n_ctiles;                 // first tile of the section
-    const int n = (G.tt_start[s + 1] - G.tt_start[s]) * G.n_ctiles;
-    uint32_t* counter = G.ctrl + kCtrlStride * s;
-    uint32_t last = 0;
-    if (lane == 0) {
-        ws_store64(G.partials + b, (uint64_t)(mr << 16) | ((uint64_t)__builtin_bit_cast(uint32_t, mc) << 32));
-        __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): the partial is stored
-        last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(n - 1);
-    }
-    if (!__shfl((int)last, 0, 64)) return;
-
-    // The section's last tile: every partial is in.
-    uint32_t ar = 0, ac = 0;
-    for (int i = lane; i < n; i += 64) {
-        const uint64_t v = ws_load64(G.partials + first + i);
-        ar = (uint32_t)v > ar ? (uint32_t)v : ar;
-        ac = (uint32_t)(v >> 32) > ac ? (uint32_t)(v >> 32) : ac;
-    }
-    ar = wave_max_u32(ar);
-    ac = wave_max_u32(ac);
-    // max |BF16(y/4)| over the section = BF16(max |y| / 4) (rounding is monotone)
-    const float g_r = tensor_scale(__builtin_bit_cast(float, ar));
-    const float g_c = tensor_scale(lo_bf16(pack_bf16(__builtin_bit_cast(float, ac) * 0.25f, 0.0f)));
-    if (lane == 0) {
-        if (ROW) G.row_global[s] = g_r;
-        if (COL) G.col_global[s] = g_c;
-        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
-    }
-    // Scale tables; entry 0 (scale code 0 never divides) holds (g, fl(1/g)).
-#pragma unroll
-    for (int e = lane; e < 256; e += 64) {
-        const int dir = e >> 7, code = e & 127;
-        if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
-        const float g = dir ? g_c : g_r;
-        float4 entry;
-        if (code == 0) {
-            const float yg = 1.0f / g;
-            entry = make_float4(g, yg, yg, 0.0f);
-        } else {
-            float d = e4m3_value((uint32_t)code) * g;
-            float y = 1.0f / d;
-            if (dir) { d *= 4.0f; y *= 0.25f; }
-            const float ym = code == 127 ? y : product_multiplier(d, y);
-            entry = make_float4(d, y, ym, 0.0f);
-        }
-        G.tables[(s * 2 + dir) * 128 + code] = entry;
-    }
-}
-
-template <bool ROW, bool COL, bool FP8, bool SR>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_nvfp4_quant(const Nvfp4Group G) {
-    const int lane = threadIdx.x;
-    const int b = blockIdx.x;
-    const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
-    const int s = section_of(G, T);
-    const int tb = lane >> 3, cc = lane & 7;
-    const int64_t k = G.k;
-    const uint16_t* base = G.x + ((int64_t)T * kTileRows + tb * 16) * k + (int64_t)C * kTileCols + cc * 16;
-    uint4 p[16][2];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        p[t][0] = *reinterpret_cast<const uint4*>(base + t * k);
-        p[t][1] = *reinterpret_cast<const uint4*>(base + t * k + 8);
-    }
-
-    __shared__ float4 tab[2][128];
-    // Column codes / scales of the tile by (column, 16-row block): 64 + 8 bytes per
-    // column, with one more slot after every 16 columns so that the 8 lane groups
-    // that write columns 16 apart use both halves of the LDS banks.
-    __shared__ uint2 lds_codes[kTileCols * 8 + 8 * 8];
-    __shared__ uint8_t lds_sc[kTileCols * 8 + 8 * 8];
-    {
-        const float4* src = G.tables + s * 256;
-        if (ROW) { tab[0][lane] = src[lane]; tab[0][64 + lane] = src[64 + lane]; }
-        if (COL) { tab[1][lane] = src[128 + lane]; tab[1][64 + lane] = src[192 + lane]; }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-
-    const int tt0 = G.tt_start[s];
-    const int ms = (G.tt_start[s + 1] - tt0) * kTileRows;           // section rows
-    const int T_local = T - tt0;
-    const int64_t row0 = (int64_t)T * kTileRows + tb * 16;           // group-relative
-    const int64_t c0 = (int64_t)C * kTileCols + cc * 16;
-    const int64_t r_local0 = (int64_t)T_local * kTileRows + tb * 16;  // section-local
-    const u32x4 no_rnd = {0, 0, 0, 0};
-    bool lane_nan = !COL;                            // a NaN column block (unknown without the column pass)
-
-    if (COL) {
-        const float g_c = tab[1][0].x, yg_c = tab[1][0].y;
-        const float4* tab_c = tab[1];
-        const uint32_t mask = G.sign_mask;
-        auto put = [&](int j, const BlockOut& o) {
-            lds_codes[(cc * 17 + j) * 8 + tb] = o.codes;
-            lds_sc[(cc * 17 + j) * 8 + tb] = (uint8_t)o.scale;
-        };
-        if (SR && G.sr_col) {
-            const int64_t b_local = r_local0 >> 4;                  // section-local 16-row block
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const u32x4 rnd = block_random(G.seed, G.col_off[s], (uint64_t)((c0 + j) * (int64_t)(ms >> 4) + b_local));
-                const BlockOut o = column_block<Enc::Sr>(p, j, mask, g_c, yg_c, tab_c, rnd);
-                put(j, o);
-                lane_nan |= o.scale == 0x7Fu;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            // No branch in this loop, so the scheduler can overlap neighbouring
-            // columns; blocks whose scale code needs the exact division are redone.
-            uint32_t redo = 0;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const BlockOut o = column_block<Enc::Mul>(p, j, mask, g_c, yg_c, tab_c, no_rnd);
-                put(j, o);
-                redo |= (uint32_t)o.unsafe << j;
-                lane_nan |= o.scale == 0x7Fu;
-                if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two columns at a time: bounds registers
-            }
-            if (__ballot(redo != 0) != 0) {
-                launder(p);
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if ((redo >> j) & 1u) put(j, column_block<Enc::Div>(p, j, mask, g_c, yg_c, tab_c, no_rnd));
-            }
-        }
-        // the LDS region is this wave's own: order its writes before the reads below
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        uint8_t* codes_s = G.col_codes + k * (int64_t)tt0 * kTileRows / 2;
-        uint8_t* scales_s = G.col_scales + k * (int64_t)tt0 * kTileRows / 16;
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int idx = it * 64 + lane;
-            const int col = idx >> 2, part = idx & 3;
-            const uint4 v = *reinterpret_cast<const uint4*>(&lds_codes[(col + (col >> 4)) * 8 + part * 2]);
-            *reinterpret_cast<uint4*>(codes_s + ((int64_t)C * kTileCols + col) * (ms >> 1) + T_local * 64 + part * 16) = v;
-        }
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int col = it * 64 + lane;
-            const uint2 v = *reinterpret_cast<const uint2*>(&lds_sc[(col + (col >> 4)) * 8]);
-            *reinterpret_cast<uint2*>(scales_s + ((int64_t)C * kTileCols + col) * (ms >> 4) + T_local * 8) = v;
-        }
-        launder(p);
-    }
-
-    if (ROW) {
-        const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
-        const float4* tab_r = tab[0];
-        row_pass<SR, COL>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan);
-    }
-
-    if (FP8) {
-        // FP8 1x128 of each row: the group's max |x| without NaNs over 8 lanes
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int64_t row = row0 + t;
-            float u[16];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                u[2 * i] = lo_bf16(P(t, i));
-                u[2 * i + 1] = hi_bf16(P(t, i));
-            }
-            uint32_t acc = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
-            uint32_t mf = fold_pk(acc);
-            const bool nan = mf > 0x7F80u;
-            if (nan) {
-                mf = 0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) mf = absmax_pk_nonan(mf, P(t, i));
-            }
-            mf = group8_max_u32(mf);
-            const float amax = bf16_mag(mf);
-            const float sf = (amax > k_floor() ? amax : k_floor()) * k_inv448();
-            const float yf = 1.0f / sf;
-            uint32_t c4[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c4[j] = e4m3_pack4(div_rn(u[4 * j], sf, yf), div_rn(u[4 * j + 1], sf, yf),
-                                   div_rn(u[4 * j + 2], sf, yf), div_rn(u[4 * j + 3], sf, yf));
-                if (nan) {
-                    // a NaN element: the conversion gives 0xFF, the format's NaN code is 0x7F
-                    const uint32_t cj = c4[j];
-                    const uint32_t ff = cj & (cj >> 1) & (cj >> 2) & (cj >> 3) & (cj >> 4) & (cj >> 5) &
-                                        (cj >> 6) & (cj >> 7) & 0x01010101u;
-                    c4[j] = cj ^ (ff * 0x80u);
-                }
-            }
-            *reinterpret_cast<uint4*>(G.fp8_codes + row * k + c0) = make_uint4(c4[0], c4[1], c4[2], c4[3]);
-            if (cc == 0) G.fp8_scales[row * (k >> 7) + C] = sf;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-}
-
-#undef P
 
 // A group without rows: only the floor tensor scales of its (empty) sections.
 template <bool ROW, bool COL>
@@ -653,25 +13,33 @@ __global__ __launch_bounds__(64) void k_nvfp4_empty(const Nvfp4Group G) {
     for (int i = threadIdx.x; i < G.num_sections; i += 64) {
         if (ROW) G.row_global[i] = tensor_scale(0.0f);
         if (COL) G.col_global[i] = tensor_scale(0.0f);
+        if (ROW && G.amax_out_row) G.amax_out_row[i] = 0.0f;
+        if (COL && G.amax_out_col) G.amax_out_col[i] = 0.0f;
     }
 }
 
 namespace {
 template <bool ROW, bool COL, bool FP8>
 hipError_t launch_sel(const Nvfp4Group& g, hipStream_t stream) {
-    if (g.total_tiles == 0) {
+    const bool given = g.amax_in_row || g.amax_in_col;
+    if (given) {
+        hipLaunchKernelGGL((k_nvfp4_given<ROW, COL>), dim3(g.num_sections), dim3(64), 0, stream, g);
+    } else if (g.total_tiles == 0) {
         hipLaunchKernelGGL((k_nvfp4_empty<ROW, COL>), dim3(1), dim3(64), 0, stream, g);
         return hipGetLastError();
     }
-    const unsigned grid = (unsigned)g.total_tiles;
-    hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL>), dim3(grid), dim3(64), 0, stream, g);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.total_tiles == 0) return e;
+    const unsigned grid = (unsigned)g.total_tiles;
+    if (!given) {
+        hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL>), dim3(grid), dim3(64), 0, stream, g);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
-    if (g.sr_row || g.sr_col)
-        hipLaunchKernelGGL((k_nvfp4_quant<ROW, COL, FP8, true>), dim3(grid), dim3(64), 0, stream, g);
-    else
-        hipLaunchKernelGGL((k_nvfp4_quant<ROW, COL, FP8, false>), dim3(grid), dim3(64), 0, stream, g);
-    return hipGetLastError();
+    const uint32_t flags = (ROW ? 1u : 0u) | (COL ? 2u : 0u) | (FP8 ? 4u : 0u);
+    const bool sr = g.sr_row || g.sr_col, aout = given && (g.amax_out_row || g.amax_out_col);
+    if (sr) return aout ? launch_quant_sr_aout(g, flags, stream) : launch_quant_sr(g, flags, stream);
+    return aout ? launch_quant_rne_aout(g, flags, stream) : launch_quant_rne(g, flags, stream);
 }
 }  // namespace
 
@@ -689,3 +57,4 @@ hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, hipStream_t s
 }
 
 }  // namespace mxq
+

@@ -136,3 +136,25 @@ def test_no_forbidden_calls_in_host_sources():
     for bad in ("hipMalloc", "hipFree", "hipMemset", "hipDeviceSynchronize", "hipStreamSynchronize",
                 "getenv", "malloc(", "new "):
         assert bad not in code, bad
+
+
+def grouped_amax(L, amax, flags=3):
+    S = 2
+    arr = (ctypes.c_int64 * S)(128, 256)
+    r = mxq._NVFP4Out(A, A, A)
+    c = mxq._NVFP4Out(A, A, A)
+    f = mxq._FP8Out(A, A)
+    a = mxq._Amax(*amax)
+    return L.mxq_group_rht_quant_nvfp4_with_amax(
+        A, 256, ctypes.addressof(arr), S, 0, flags, None, ctypes.addressof(r), ctypes.addressof(c),
+        ctypes.addressof(f), ctypes.addressof(a), A, 1 << 30, None)
+
+
+def test_grouped_amax_argument_errors(L):
+    """Supplied maxima come for every requested NVFP4 direction or for none, 4-byte
+    aligned; every rejected call returns before anything is enqueued."""
+    assert grouped_amax(L, (A, None, None, None)) == INVALID       # column maxima missing
+    assert grouped_amax(L, (None, A, None, None)) == INVALID       # row maxima missing
+    assert grouped_amax(L, (A + 2, A, None, None)) == MISALIGNED
+    assert grouped_amax(L, (None, None, A + 1, None)) == MISALIGNED
+    assert grouped_amax(L, (A, A, None, None), flags=0) == INVALID

@@ -378,3 +378,74 @@ def test_grouped_hand_case_b9(orc):
     codes = host(res.row_codes)[0, :8].tolist()
     assert codes == [0x07, 0x22, 0x44, 0x66, 0xA8, 0x07, 0x28, 0x6F]
     assert host(res.row_global)[0] == np.float32(2.0 ** -8)
+
+
+# ============================================================== supplied amax (single pass)
+def compare_grouped_amax(orc, x_dev, sections, mask, flags, amax_in, seed=None, ro=None, co=None):
+    """The call with supplied maxima (device tensors, or None) and measured maxima out,
+    against the oracle given the same maxima."""
+    dev = x_dev.device
+    ain = None
+    if amax_in is not None:
+        ain = tuple(None if a is None else torch.tensor(np.asarray(a, np.float32), device=dev) for a in amax_in)
+    call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, amax_in=ain, amax_out=True)
+    res = call()
+    torch.cuda.synchronize()
+    ref = orc.group_rht_quant_nvfp4(bits16(x_dev), sections, mask, flags, seed or 0, ro, co, threads=8,
+                                    amax_in=amax_in)
+    names = []
+    if flags & 1:
+        names += ["row_global", "row_scales", "row_codes", "row_amax"]
+    if flags & 2:
+        names += ["col_global", "col_scales", "col_codes", "col_amax"]
+    if flags & 4:
+        names += ["fp8_scales", "fp8_codes"]
+    for n in names:
+        assert_same(n, host(getattr(res, n)), getattr(ref, n))
+    return res, ref
+
+
+@pytest.mark.parametrize("flags", [3, 1, 2, 7])
+def test_grouped_measured_amax_out(orc, flags):
+    """The plain (two-pass) call reports the maxima its tensor scales used."""
+    dev = device()
+    announce(f"grouped amax out flags={flags}")
+    w = synth.grouped_nvfp4(total_rows=1024, k=512, parts=4, seed=51)
+    compare_grouped_amax(orc, w.tensors["x"].to(dev), w.params["split_sections"], w.params["sign_mask"],
+                         flags, None)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.25, 3.0])
+def test_grouped_supplied_amax(orc, scale):
+    """Single pass with supplied maxima: the measured ones (scale 1: the outputs of
+    the plain call), smaller ones (saturation) and larger ones."""
+    dev = device()
+    announce(f"grouped supplied amax x{scale}")
+    w = synth.grouped_nvfp4(total_rows=1280, k=640, parts=5, seed=52)
+    x = w.tensors["x"].to(dev)
+    sec, mask = w.params["split_sections"], w.params["sign_mask"]
+    meas = orc.group_rht_quant_nvfp4(bits16(x), sec, mask, 3, threads=8)
+    amax_in = (meas.row_amax * np.float32(scale), meas.col_amax * np.float32(scale))
+    res, _ = compare_grouped_amax(orc, x, sec, mask, 3, amax_in)
+    if scale == 1.0:
+        plain = mxq.mxq_group_rht_quant_nvfp4(x, sec, mask, 3)
+        torch.cuda.synchronize()
+        for n in ("row_codes", "row_scales", "row_global", "col_codes", "col_scales", "col_global"):
+            assert torch.equal(getattr(res, n), getattr(plain, n)), n
+
+
+def test_grouped_supplied_amax_sr_fp8_edges(orc):
+    """Supplied maxima with stochastic rounding, the FP8 output, empty sections and
+    NaN / -0 / subnormal edge values."""
+    dev = device()
+    announce("grouped supplied amax: SR + FP8 + edges")
+    b = edge_matrix(512, 256, 53)
+    b[100:116, 40] = 0x7FC0
+    x = bf16_dev(b, dev)
+    sec = [128, 0, 256, 128, 0]
+    rng = np.random.default_rng(54)
+    amax_in = (rng.uniform(0.5, 40, 5).astype(np.float32), rng.uniform(0.5, 40, 5).astype(np.float32))
+    compare_grouped_amax(orc, x, sec, 0x3C5A, 7, amax_in, seed=99, ro=[1, 2, 3, 4, 5], co=[6, 7, 8, 9, 10])
+    compare_grouped_amax(orc, x, sec, 0x3C5A, 3, amax_in)
+    compare_grouped_amax(orc, x, sec, 0x3C5A, 2, (None, amax_in[1]))
+    compare_grouped_amax(orc, x[:0], [0, 0], 0, 3, (np.ones(2, np.float32), np.ones(2, np.float32)))
