@@ -229,6 +229,25 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
                                                const mxq_fp8_out* fp8_rowwise, const mxq_amax* amax,
                                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Launch marks (measurement).  Not an operation of the method: a hook through
+ * which a harness times each kernel of a grouped NVFP4 call on the call's own
+ * stream, so that per-kernel times come from the same run as the call's time.
+ *
+ * before, between, after: hipEvent_t handles owned by the caller (created on the
+ * device the calls run on), or all NULL to turn the marks off.  While set, every
+ * grouped NVFP4 call made from the calling thread records `before` ahead of its
+ * first kernel, `between` after the kernel that forms the tensor scales (the
+ * amax kernel, or the table kernel when maxima are supplied) and `after` behind
+ * the quantize kernel; with more than one launch group per call (more than 32
+ * sections) the marks of the last group are the ones left.  The setting is per
+ * thread and lasts until changed; the library never creates, waits on or
+ * destroys the events.  Returns MXQ_ERR_INVALID_ARGUMENT when some but not all
+ * of the three are NULL; a failed record makes the grouped call return
+ * MXQ_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_set_launch_marks(void* before, void* between, void* after);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,10 @@ struct Nvfp4Group {
     float* amax_out_col;
 };
 hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
+// Launch marks of the calling thread (mxq_set_launch_marks): records mark i
+// (0 before the first kernel, 1 between the scale and quantize kernels, 2 after)
+// on the stream when marks are set; hipSuccess otherwise.
+hipError_t launch_mark(int i, hipStream_t stream);
 // The quant kernel's variant families (one translation unit each): nearest-even or
 // stochastic rounding, with or without measured maxima out (supplied maxima).
 hipError_t launch_quant_rne(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);

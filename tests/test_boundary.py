@@ -158,3 +158,11 @@ def test_grouped_amax_argument_errors(L):
     assert grouped_amax(L, (A + 2, A, None, None)) == MISALIGNED
     assert grouped_amax(L, (None, None, A + 1, None)) == MISALIGNED
     assert grouped_amax(L, (A, A, None, None), flags=0) == INVALID
+
+
+def test_launch_marks_arguments(L):
+    """Launch marks are three events or none; a partial set is refused and leaves
+    the marks off."""
+    assert L.mxq_set_launch_marks(A, None, None) == INVALID
+    assert L.mxq_set_launch_marks(None, A, A) == INVALID
+    assert L.mxq_set_launch_marks(None, None, None) == 0

@@ -449,3 +449,30 @@ def test_grouped_supplied_amax_sr_fp8_edges(orc):
     compare_grouped_amax(orc, x, sec, 0x3C5A, 3, amax_in)
     compare_grouped_amax(orc, x, sec, 0x3C5A, 2, (None, amax_in[1]))
     compare_grouped_amax(orc, x[:0], [0, 0], 0, 3, (np.ones(2, np.float32), np.ones(2, np.float32)))
+
+
+def test_grouped_launch_marks(orc):
+    """Launch marks time the two kernels of a call on its stream and change none of
+    its outputs; turned off, the next call records nothing."""
+    dev = device()
+    announce("grouped launch marks")
+    w = synth.grouped_nvfp4(total_rows=1024, k=512, parts=3, seed=41)
+    x = w.tensors["x"].to(dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in ev:
+        e.record(stream)
+    torch.cuda.synchronize()
+    try:
+        mxq.mxq_set_launch_marks(*ev)
+        compare_grouped(orc, x, w.params["split_sections"], w.params["sign_mask"], 3)
+    finally:
+        mxq.mxq_set_launch_marks()
+    assert ev[0].elapsed_time(ev[1]) > 0.0 and ev[1].elapsed_time(ev[2]) > 0.0
+    late = torch.cuda.Event(enable_timing=True)
+    late.record(stream)
+    compare_grouped(orc, x, w.params["split_sections"], w.params["sign_mask"], 3)
+    torch.cuda.synchronize()
+    assert ev[2].elapsed_time(late) > 0.0          # the unmarked call moved no mark
+    with pytest.raises(ValueError):
+        mxq.mxq_set_launch_marks(ev[0], None, None)
