@@ -54,6 +54,8 @@ def lib():
         L.oracle_quant_fp8_1x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64]
         L.oracle_hadamard_quant_fp8.restype = None
         L.oracle_hadamard_quant_fp8.argtypes = [_p, _i64, ctypes.c_int32, _p, _i64, _i64, _p, _p]
+        L.oracle_hadamard_quant_nvfp4.restype = None
+        L.oracle_hadamard_quant_nvfp4.argtypes = [_p, _i64, ctypes.c_int32, _p, _i64, _i64, _p, _p, _p, _p, _p]
         L.oracle_nvfp4_global_scale.restype = ctypes.c_float
         L.oracle_nvfp4_global_scale.argtypes = [ctypes.c_float]
         L.oracle_nvfp4_block.restype = None
@@ -175,6 +177,30 @@ def hadamard_quant_fp8(pe, nope):
     lib().oracle_hadamard_quant_fp8(_ptr(pe), max(d_pe, 1), d_pe, _ptr(nope), max(128 - d_pe, 1),
                                     m, _ptr(q), _ptr(s))
     return q, s
+
+
+class DsaNVFP4Outputs:
+    """codes [m][64] uint8, scales [m][8] uint8 (E4M3), global_scale float32, amax float32
+    (the measured A)."""
+
+    def __init__(self, codes, scales, global_scale, amax):
+        self.codes, self.scales, self.global_scale, self.amax = codes, scales, global_scale, amax
+
+
+def hadamard_quant_nvfp4(pe, nope, amax_in=None):
+    """pe: [m][d_pe], nope: [m][128-d_pe] uint16.  amax_in: None (measure) or the A to use."""
+    pe = _c(pe, np.uint16)
+    nope = _c(nope, np.uint16)
+    m, d_pe = pe.shape
+    assert nope.shape == (m, 128 - d_pe)
+    codes = np.empty((m, 64), np.uint8)
+    scales = np.empty((m, 8), np.uint8)
+    g = np.zeros(1, np.float32)
+    a = np.zeros(1, np.float32)
+    ain = None if amax_in is None else np.array([amax_in], np.float32)
+    lib().oracle_hadamard_quant_nvfp4(_ptr(pe), max(d_pe, 1), d_pe, _ptr(nope), max(128 - d_pe, 1), m,
+                                      _ptr(ain), _ptr(codes), _ptr(scales), _ptr(g), _ptr(a))
+    return DsaNVFP4Outputs(codes, scales, np.float32(g[0]), np.float32(a[0]))
 
 
 # ---- NVFP4 ----------------------------------------------------------------------

@@ -456,3 +456,45 @@ void oracle_wht_n(const float* in, int64_t count, int n, uint32_t sign_mask, flo
 {
     for (int64_t i = 0; i < count; ++i) oracle_wht(in + i * n, n, sign_mask, c, out + i * n);
 }
+
+/* ------------------------------------------------------------------------ */
+/* DSA rotate + NVFP4 row-wise                                               */
+/* ------------------------------------------------------------------------ */
+/* The rotated values of row r: v = cat(pe[r][0:d_pe], nope[r][0:128-d_pe]),
+ * y = WHT_128(v; no signs, F(1/sqrt(128))), each y_i a BF16 value. */
+static void dsa_rotated_row(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                            const uint16_t* nope, int64_t ld_nope, int64_t r, float* y)
+{
+    float v[128];
+    for (int i = 0; i < d_pe; ++i)   v[i] = oracle_bf16_to_f32(pe[r * ld_pe + i]);
+    for (int i = d_pe; i < 128; ++i) v[i] = oracle_bf16_to_f32(nope[r * ld_nope + (i - d_pe)]);
+    oracle_wht(v, 128, 0u, F_C128(), y);
+}
+
+void oracle_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                 const uint16_t* nope, int64_t ld_nope, int64_t m,
+                                 const float* amax_in, uint8_t* codes, uint8_t* scales,
+                                 float* global_scale, float* amax_out)
+{
+    float y[128];
+    /* pass 1: A = max |y| over every rotated value of the tensor, NaN ignored */
+    float A = 0.0f;
+    for (int64_t r = 0; r < m; ++r) {
+        dsa_rotated_row(pe, ld_pe, d_pe, nope, ld_nope, r, y);
+        float a = oracle_amax(y, 128);
+        if (a > A) A = a;
+    }
+    if (amax_out) *amax_out = A;
+    float g = oracle_nvfp4_global_scale(amax_in ? *amax_in : A);
+    *global_scale = g;
+    /* pass 2: each 1x16 block of each row with the tensor scale g */
+    for (int64_t r = 0; r < m; ++r) {
+        dsa_rotated_row(pe, ld_pe, d_pe, nope, ld_nope, r, y);
+        for (int b = 0; b < 8; ++b) {
+            uint8_t c16[16];
+            oracle_nvfp4_block(y + 16 * b, g, NULL, &scales[r * 8 + b], c16);
+            for (int i = 0; i < 8; ++i)
+                codes[r * 64 + b * 8 + i] = (uint8_t)(c16[2 * i] | (c16[2 * i + 1] << 4));
+        }
+    }
+}

@@ -79,6 +79,18 @@ void oracle_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
                                const uint16_t* nope, int64_t ld_nope, int64_t m,
                                uint8_t* q, float* scales);
 
+/* DSA-indexer rotate + NVFP4 row-wise (the FP4 counterpart of the call above):
+ * y = WHT_128(cat(pe[r][0:d_pe], nope[r][0:128-d_pe]); no signs, F(1/sqrt(128))),
+ * rounded to BF16; one tensor scale g = fl(max(A, F(1e-10)) * F(1/2688)) with A the
+ * max |y| over the whole tensor (NaN ignored), or *amax_in when amax_in is not
+ * NULL; then every 1x16 block of every row encoded with g as oracle_nvfp4_block.
+ * codes [m][64] (even element in the low nibble), scales [m][8] E4M3,
+ * *global_scale = g, *amax_out = the measured A (when not NULL). */
+void oracle_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                 const uint16_t* nope, int64_t ld_nope, int64_t m,
+                                 const float* amax_in, uint8_t* codes, uint8_t* scales,
+                                 float* global_scale, float* amax_out);
+
 /* ---- NVFP4 -------------------------------------------------------------------- */
 /* g = fl(max(A, F(1e-10)) * F(1/2688)) */
 float oracle_nvfp4_global_scale(float amax);
