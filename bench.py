@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="grouped_nvfp4_rht",
                     choices=["grouped_nvfp4_rht", "grouped_nvfp4_rht_sr", "large_moe_nvfp4_fp8",
-                             "dsa_rotate_fp8", "fp8_1x128"])
+                             "dsa_rotate_fp8", "dsa_rotate_nvfp4", "fp8_1x128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="steady-state steps only, then one 256 MiB device copy (the counter calibration "
@@ -60,7 +60,7 @@ def main():
 
     # ---------------------------------------------------------------- workload
     wl = args.workload
-    grouped = wl not in ("fp8_1x128", "dsa_rotate_fp8")
+    grouped = wl not in ("fp8_1x128", "dsa_rotate_fp8", "dsa_rotate_nvfp4")
     if wl == "fp8_1x128":
         w = synth.plain_fp8(device=dev)
         x = w.tensors["x"]
@@ -89,6 +89,18 @@ def main():
         in_bytes = m * 128 * 2
         alg_bytes = in_bytes + m * 128 + m * 4
         desc = f"dsa cat+WHT128+fp8_1x128, {m} rows (4096 tokens x 64 heads) bf16"
+    elif wl == "dsa_rotate_nvfp4":
+        w = synth.dsa_rotate_fp8(device=dev)
+        pe, nope = w.tensors["pe"], w.tensors["nope"]
+        m = pe.shape[0]
+        dsa_ws = torch.zeros((mxq.mxq_hadamard_quant_nvfp4_workspace_size(m),), dtype=torch.uint8, device=dev)
+
+        def make_call():
+            return mxq.HadamardNVFP4(pe.clone(), nope.clone(), workspace=dsa_ws)
+        call = make_call()
+        in_bytes = m * 128 * 2
+        alg_bytes = in_bytes + m * 64 + m * 8 + 4
+        desc = f"dsa cat+WHT128+nvfp4 row-wise (one tensor scale, measured), {m} rows (4096 tokens x 64 heads) bf16"
     else:
         gen = {"grouped_nvfp4_rht": synth.grouped_nvfp4, "grouped_nvfp4_rht_sr": synth.grouped_nvfp4_sr,
                "large_moe_nvfp4_fp8": synth.large_moe}[wl]
@@ -147,7 +159,12 @@ def main():
 
     # per-kernel times of K more steady-state calls, from launch marks the library
     # records on the call's stream around each of its kernels
-    kern = kernel_times(mxq, torch, calls, n_sets, K, stream) if grouped else None
+    kern = None
+    if grouped:
+        kern = kernel_times(mxq, torch, calls, n_sets, K, stream, ("k_nvfp4_amax", "k_nvfp4_quant"))
+    elif wl == "dsa_rotate_nvfp4":
+        kern = kernel_times(mxq, torch, calls, n_sets, K, stream,
+                            ("k_dsa_nvfp4_amax+k_dsa_nvfp4_scale", "k_dsa_nvfp4_quant"))
 
     if args.profile:
         del calls
@@ -200,10 +217,10 @@ def main():
 
     value = in_bytes / (ms * 1e-3) / 1e9
     achieved = alg_bytes / (ms * 1e-3) / 1e9              # the whole call (every kernel)
-    if grouped:
+    if kern is not None:
         # the dominant kernel: the one with the longest average launch
         dom = max(kern, key=kern.get)
-        dom_bytes = {"k_nvfp4_amax": in_bytes, "k_nvfp4_quant": alg_bytes}[dom]
+        dom_bytes = alg_bytes if dom.endswith("_quant") else in_bytes
         dom_gbs = dom_bytes / (kern[dom] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl, dom),
@@ -213,7 +230,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     line = {
-        "metric": "input GB/s and % of HBM peak, grouped NVFP4 RHT quant (row+col), 1 MI355X",
+        "metric": ("input GB/s and % of HBM peak, grouped NVFP4 RHT quant (row+col), 1 MI355X"
+                   if wl == "grouped_nvfp4_rht" else f"input GB/s and % of HBM peak, {wl}, 1 MI355X"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -260,10 +278,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def kernel_times(mxq, torch, calls, n_sets, K, stream):
-    """Average duration (us) of each kernel of a grouped call over K steady-state
-    calls, between HIP events the library records on the call's stream just before,
-    between and after its two kernels."""
+def kernel_times(mxq, torch, calls, n_sets, K, stream, names):
+    """Average duration (us) of each of the two kernels (`names`) of an NVFP4 call
+    over K steady-state calls, between HIP events the library records on the call's
+    stream just before, between and after them."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for trio in ev:
         for e in trio:
@@ -278,7 +296,7 @@ def kernel_times(mxq, torch, calls, n_sets, K, stream):
     torch.cuda.synchronize()
     first = sum(a.elapsed_time(b) for a, b, _ in ev) / K
     second = sum(b.elapsed_time(c) for _, b, c in ev) / K
-    return {"k_nvfp4_amax": round(first * 1e3, 2), "k_nvfp4_quant": round(second * 1e3, 2)}
+    return {names[0]: round(first * 1e3, 2), names[1]: round(second * 1e3, 2)}
 
 
 def measured_traffic(wl, kernel):

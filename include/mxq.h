@@ -2,10 +2,12 @@
  * mxq.h -- C ABI of the mxq block-quantization library for AMD Instinct MI355X
  * (gfx950).
  *
- * Three entry points quantize BF16 activations on the GPU:
+ * Four entry points quantize BF16 activations on the GPU:
  *   mxq_quant_fp8_1x128        FP8 E4M3 with one FP32 scale per 1x128 group
  *   mxq_hadamard_quant_fp8     cat[qk_pe, qk_nope] -> normalized 128-point
  *                              Walsh-Hadamard rotation -> FP8 1x128
+ *   mxq_hadamard_quant_nvfp4   the same rotation -> NVFP4 row-wise (1x16 blocks,
+ *                              one FP32 tensor scale, measured or supplied)
  *   mxq_group_rht_quant_nvfp4  grouped (MoE split sections) NVFP4, row-wise and
  *                              column-wise after a 16-point random-sign Hadamard
  *                              transform, optionally with an FP8 1x128 row-wise
@@ -19,8 +21,9 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous: MXQ_OK means the work was enqueued.
  *  - The library never allocates, frees, memsets, synchronizes or reads the
- *    environment; it keeps no global state and is re-entrant.  Calls in flight at
- *    the same time need distinct workspaces.
+ *    environment; it keeps no global state (the per-thread launch marks, a
+ *    measurement hook, aside) and is re-entrant.  Calls in flight at the same time
+ *    need distinct workspaces.
  *  - All argument checks run on the host before anything is enqueued; on an error
  *    nothing is launched and no output is touched.  A failed launch returns
  *    MXQ_ERR_HIP (outputs are then undefined).  There is no fallback path: an
@@ -109,6 +112,41 @@ mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int
 mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
                                   const uint16_t* nope, int64_t ld_nope, int64_t m,
                                   uint8_t* q_e4m3, float* scales, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * DSA-indexer rotate + NVFP4 (row-wise 1x16).  The FP4 counterpart of the call
+ * above: TensorRT-LLM PR #15158 (Summary) names the FP4 path's missing rotation and
+ * its need for a standalone FP4 quantize-only kernel.  For each row r:
+ *   y = BF16(fl(WHT_128(cat(pe[r][0:d_pe], nope[r][0:128-d_pe])) * F(1/sqrt(128))))
+ *   (as mxq_hadamard_quant_fp8), then the row-wise NVFP4 encode of
+ *   mxq_group_rht_quant_nvfp4 with ONE tensor scale for the whole call:
+ *   g = fl(max(A, F(1e-10)) * F(1/2688)), A = max |y| over every row (NaN ignored)
+ *   or *amax_in; per 1x16 block t = fl(fl(a * F(1/6)) / g), sc = E4M3(t),
+ *   d = fl(E4M3(sc) * g), codes E2M1(fl(y / d)) (nearest-even, saturating); a block
+ *   of a row holding a NaN gets scale 0x7F and zero codes.
+ *
+ *   pe, nope, d_pe, ld_pe, ld_nope: as mxq_hadamard_quant_fp8
+ *   amax_in       device float[1], or NULL: measure A (two passes over the input)
+ *   amax_out      device float[1], or NULL: the measured A of this call (0 for m = 0)
+ *   codes         device [m][64]: codes of y[r][2i] (low nibble) and y[r][2i+1]
+ *   block_scales  device [m][8] E4M3
+ *   global_scale  device float[1]: g (also written for m = 0: the floor scale, or
+ *                 the scale of *amax_in)
+ *   workspace     device memory of mxq_hadamard_quant_nvfp4_workspace_size(m)
+ *                 bytes (2 KB of scale table + 4 bytes per 64 rows, rounded up to
+ *                 256), 256-byte aligned, no initialization needed.  Calls that
+ *                 share it must be ordered.  May be NULL when m = 0.
+ * Requirements: as mxq_hadamard_quant_fp8; codes and block_scales 16-byte aligned,
+ * global_scale, amax_in, amax_out 4-byte aligned; m <= 2^31 - 128.  Errors are
+ * returned before anything is enqueued.
+ * ------------------------------------------------------------------------- */
+size_t mxq_hadamard_quant_nvfp4_workspace_size(int64_t m);
+
+mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                    const uint16_t* nope, int64_t ld_nope, int64_t m,
+                                    const float* amax_in, float* amax_out,
+                                    uint8_t* codes, uint8_t* block_scales, float* global_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Grouped NVFP4 quantization with a 16-point random Hadamard transform (RHT) on
@@ -236,11 +274,12 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
  *
  * before, between, after: hipEvent_t handles owned by the caller (created on the
  * device the calls run on), or all NULL to turn the marks off.  While set, every
- * grouped NVFP4 call made from the calling thread records `before` ahead of its
- * first kernel, `between` after the kernel that forms the tensor scales (the
- * amax kernel, or the table kernel when maxima are supplied) and `after` behind
- * the quantize kernel; with more than one launch group per call (more than 32
- * sections) the marks of the last group are the ones left.  The setting is per
+ * NVFP4 call (mxq_group_rht_quant_nvfp4*, mxq_hadamard_quant_nvfp4) made from the
+ * calling thread records `before` ahead of its first kernel, `between` after the
+ * kernel that forms the tensor scales (the amax kernel, or the table kernel when
+ * maxima are supplied) and `after` behind the quantize kernel; with more than one
+ * launch group per grouped call (more than 32 sections) the marks of the last
+ * group are the ones left; a call without rows records `before` only.  The setting is per
  * thread and lasts until changed; the library never creates, waits on or
  * destroys the events.  Returns MXQ_ERR_INVALID_ARGUMENT when some but not all
  * of the three are NULL; a failed record makes the grouped call return

@@ -25,7 +25,8 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_MISALIGNED",
 
 EXPORTED = ("mxq_status_string", "mxq_version", "mxq_quant_fp8_1x128", "mxq_hadamard_quant_fp8",
             "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4",
-            "mxq_group_rht_quant_nvfp4_with_amax", "mxq_set_launch_marks")
+            "mxq_group_rht_quant_nvfp4_with_amax", "mxq_set_launch_marks",
+            "mxq_hadamard_quant_nvfp4_workspace_size", "mxq_hadamard_quant_nvfp4")
 
 
 class MxqError(RuntimeError):
@@ -78,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_rht_quant_nvfp4_with_amax.restype = ctypes.c_int
         L.mxq_group_rht_quant_nvfp4_with_amax.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
                                                           p, p, p, p, p, ctypes.c_size_t, p]
+        L.mxq_hadamard_quant_nvfp4_workspace_size.restype = ctypes.c_size_t
+        L.mxq_hadamard_quant_nvfp4_workspace_size.argtypes = [i64]
+        L.mxq_hadamard_quant_nvfp4.restype = ctypes.c_int
+        L.mxq_hadamard_quant_nvfp4.argtypes = [p, i64, ctypes.c_int32, p, i64, i64, p, p, p, p, p, p,
+                                               ctypes.c_size_t, p]
         L.mxq_set_launch_marks.restype = ctypes.c_int
         L.mxq_set_launch_marks.argtypes = [p, p, p]
         _lib = L
@@ -97,6 +103,13 @@ def _stream(stream) -> ctypes.c_void_p:
 def _check(status: int, what: str):
     if status != 0:
         raise MxqError(status, what)
+
+
+def _row_stride(t: Optional[torch.Tensor]) -> int:
+    """Row stride in elements of a 2-D tensor (its width when it holds nothing)."""
+    if t is None:
+        return 0
+    return t.stride(0) if t.numel() > 0 else t.shape[1]
 
 
 def _bf16_bits(t: torch.Tensor) -> torch.Tensor:
@@ -172,11 +185,71 @@ def mxq_hadamard_quant_fp8(pe: Optional[torch.Tensor], nope: Optional[torch.Tens
         q = torch.empty((m, 128), dtype=torch.uint8, device=ref.device)
     if scales is None:
         scales = torch.empty((m,), dtype=torch.float32, device=ref.device)
-    ld_pe = pe.stride(0) if pe is not None else 0
-    ld_nope = nope.stride(0) if nope is not None else 0
+    ld_pe = _row_stride(pe)
+    ld_nope = _row_stride(nope)
     _check(lib().mxq_hadamard_quant_fp8(_ptr(pe), ld_pe, d_pe, _ptr(nope), ld_nope, m, _ptr(q), _ptr(scales),
                                         _stream(stream)), "mxq_hadamard_quant_fp8")
     return q, scales
+
+
+# ---------------------------------------------------------------------------- DSA rotate + NVFP4
+@dataclass
+class DsaNVFP4Result:
+    codes: torch.Tensor                           # [m][64] uint8, even element in the low nibble
+    scales: torch.Tensor                          # [m][8] uint8 (E4M3)
+    global_scale: torch.Tensor                    # [1] float32
+    amax: Optional[torch.Tensor] = None           # [1] float32, the measured max |y| (when asked for)
+
+
+def mxq_hadamard_quant_nvfp4_workspace_size(m: int) -> int:
+    return int(lib().mxq_hadamard_quant_nvfp4_workspace_size(m))
+
+
+class HadamardNVFP4:
+    """A prepared DSA rotate + NVFP4 call: outputs and a workspace are allocated
+    once; each call runs the quantizer on `pe`, `nope` as they are then.
+    pe: [m][d_pe], nope: [m][128-d_pe] BF16 with unit column stride (either may be
+    None when empty).  amax_in: None (measure), a float, or a device float32 tensor
+    of one element.  amax_out: also return the measured max |y|."""
+
+    def __init__(self, pe: Optional[torch.Tensor], nope: Optional[torch.Tensor], amax_in=None,
+                 amax_out: bool = False, workspace: Optional[torch.Tensor] = None):
+        ref = pe if pe is not None else nope
+        self.m = ref.shape[0]
+        self.d_pe = pe.shape[1] if pe is not None else 0
+        for t in (pe, nope):
+            if t is not None and t.numel() > 0 and t.stride(1) != 1:
+                raise ValueError("pe / nope need unit column stride")
+        self.pe = _bf16_bits(pe) if pe is not None else None
+        self.nope = _bf16_bits(nope) if nope is not None else None
+        dev = ref.device
+        self.out = DsaNVFP4Result(torch.empty((self.m, 64), dtype=torch.uint8, device=dev),
+                                  torch.empty((self.m, 8), dtype=torch.uint8, device=dev),
+                                  torch.empty((1,), dtype=torch.float32, device=dev),
+                                  torch.empty((1,), dtype=torch.float32, device=dev) if amax_out else None)
+        if amax_in is not None and not isinstance(amax_in, torch.Tensor):
+            amax_in = torch.tensor([float(amax_in)], dtype=torch.float32, device=dev)
+        self.amax_in = amax_in
+        need = mxq_hadamard_quant_nvfp4_workspace_size(self.m)
+        if workspace is None:
+            workspace = torch.zeros((max(need, 256),), dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+
+    def __call__(self, stream=None) -> DsaNVFP4Result:
+        o = self.out
+        _check(lib().mxq_hadamard_quant_nvfp4(
+            _ptr(self.pe), _row_stride(self.pe), self.d_pe, _ptr(self.nope), _row_stride(self.nope), self.m,
+            _ptr(self.amax_in), _ptr(o.amax), _ptr(o.codes), _ptr(o.scales), _ptr(o.global_scale),
+            _ptr(self.workspace), self.workspace.numel(), _stream(stream)), "mxq_hadamard_quant_nvfp4")
+        return o
+
+
+def mxq_hadamard_quant_nvfp4(pe: Optional[torch.Tensor], nope: Optional[torch.Tensor], amax_in=None,
+                             amax_out: bool = False, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> DsaNVFP4Result:
+    """cat[pe, nope] -> normalized 128-point WHT -> BF16 -> NVFP4 row-wise (1x16 blocks,
+    one tensor scale over the call)."""
+    return HadamardNVFP4(pe, nope, amax_in, amax_out, workspace)(stream)
 
 
 # ---------------------------------------------------------------------------- grouped NVFP4

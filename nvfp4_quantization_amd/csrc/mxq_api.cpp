@@ -93,6 +93,52 @@ mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_p
     return mxq::launch_hadamard_quant_fp8(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
+size_t mxq_hadamard_quant_nvfp4_workspace_size(int64_t m) {
+    if (m <= 0 || m > kMaxRows) return 0;
+    return (size_t)round256(mxq::kDsaPartialsOffset + 4 * ceil_div(m, 64));
+}
+
+mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                    const uint16_t* nope, int64_t ld_nope, int64_t m,
+                                    const float* amax_in, float* amax_out,
+                                    uint8_t* codes, uint8_t* block_scales, float* global_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (m < 0 || d_pe < 0 || d_pe > 128) return MXQ_ERR_INVALID_ARGUMENT;
+    if (d_pe % 8 != 0) return MXQ_ERR_MISALIGNED;
+    if (d_pe > 0 && ld_pe < d_pe) return MXQ_ERR_INVALID_ARGUMENT;
+    if (d_pe < 128 && ld_nope < 128 - d_pe) return MXQ_ERR_INVALID_ARGUMENT;
+    if ((d_pe > 0 && ld_pe % 8 != 0) || (d_pe < 128 && ld_nope % 8 != 0)) return MXQ_ERR_MISALIGNED;
+    if (!global_scale) return MXQ_ERR_INVALID_ARGUMENT;
+    if (!aligned(global_scale, 4) || !aligned(amax_in, 4) || !aligned(amax_out, 4)) return MXQ_ERR_MISALIGNED;
+    if (m > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    if (m > 0) {
+        if ((d_pe > 0 && !pe) || (d_pe < 128 && !nope) || !codes || !block_scales || !workspace)
+            return MXQ_ERR_INVALID_ARGUMENT;
+        if ((d_pe > 0 && !aligned(pe, 16)) || (d_pe < 128 && !aligned(nope, 16)) || !aligned(codes, 16) ||
+            !aligned(block_scales, 16) || !aligned(workspace, 256))
+            return MXQ_ERR_MISALIGNED;
+        if (workspace_bytes < mxq_hadamard_quant_nvfp4_workspace_size(m)) return MXQ_ERR_WORKSPACE_TOO_SMALL;
+    }
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    mxq::DsaNvfp4Args a{};
+    a.pe = pe;
+    a.nope = nope;
+    a.ld_pe = ld_pe;
+    a.ld_nope = ld_nope;
+    a.m = m;
+    a.d_pe = d_pe;
+    a.n_wg = (int32_t)ceil_div(m, 64);
+    a.codes = codes;
+    a.scales = block_scales;
+    a.global_scale = global_scale;
+    a.amax_in = amax_in;
+    a.amax_out = amax_out;
+    a.table = m > 0 ? reinterpret_cast<float4*>(ws + mxq::kDsaTableOffset) : nullptr;
+    a.partials = m > 0 ? reinterpret_cast<float*>(ws + mxq::kDsaPartialsOffset) : nullptr;
+    return mxq::launch_hadamard_quant_nvfp4(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK
+                                                                                              : MXQ_ERR_HIP;
+}
+
 size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k, int64_t num_sections,
                                                 uint32_t flags) {
     if (total_rows < 0 || k <= 0 || num_sections <= 0) return 0;

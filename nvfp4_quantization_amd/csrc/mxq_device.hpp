@@ -144,4 +144,60 @@ __device__ __forceinline__ float shfl_xor_f32(float v, int m) {
     return __shfl_xor(v, m, 64);
 }
 
+// The value of another lane of the same quad (4 consecutive lanes): DPP quad_perm
+// control PERM (0xB1: lane ^ 1, 0x4E: lane ^ 2).
+template <int PERM>
+__device__ __forceinline__ float quad_swap(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), PERM, 0xF, 0xF, true));
+}
+
+// The 128-point Walsh-Hadamard butterfly of v = cat(pe[r][0:d_pe], nope[r][0:128-d_pe])
+// held by 4 consecutive lanes: lane `quarter` loads elements 32q .. 32q+31 (d_pe a
+// multiple of 8, so an 8-element load never straddles pe and nope) and ends with
+// outputs 32q .. 32q+31 before the constant: stages h = 1..16 run inside the lane,
+// h = 32 and 64 pair lanes quarter ^ 1 and quarter ^ 2.  A lane that is not live
+// works on zeros (its partners' rows are its own, so it changes no live output).
+__device__ __forceinline__ void wht128_quarter(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                               const uint16_t* nope, int64_t ld_nope, int64_t r, bool live,
+                                               int quarter, float (&v)[32]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e0 = (quarter * 4 + q) * 8;
+        uint4 w = {0, 0, 0, 0};
+        if (live) {
+            const uint16_t* src = e0 < d_pe ? pe + r * ld_pe + e0 : nope + r * ld_nope + (e0 - d_pe);
+            w = *reinterpret_cast<const uint4*>(src);
+        }
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[q * 8 + 2 * i] = lo_bf16(ww[i]);
+            v[q * 8 + 2 * i + 1] = hi_bf16(ww[i]);
+        }
+    }
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (i & h) continue;
+            const float x0 = v[i], x1 = v[i + h];
+            v[i] = x0 + x1;
+            v[i + h] = x0 - x1;
+        }
+    }
+    // the upper lane of a pair forms other - v, the lower v + other: both are
+    // fma(v, +-1, other), exact products with one rounding (signed zeros included);
+    // the partner's value comes over the quad's data-parallel crossbar (DPP)
+    {
+        const float sgn = (quarter & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(v[i], sgn, quad_swap<0xB1>(v[i]));   // lane ^ 1
+    }
+    {
+        const float sgn = (quarter & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(v[i], sgn, quad_swap<0x4E>(v[i]));   // lane ^ 2
+    }
+}
+
 }  // namespace mxq

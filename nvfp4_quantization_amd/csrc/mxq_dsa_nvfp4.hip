@@ -1,0 +1,150 @@
+// mxq_dsa_nvfp4.hip -- DSA-indexer rotate + NVFP4 row-wise (gfx950).
+//
+// TensorRT-LLM PR #15158 (Summary; discussion): the indexer concatenates qk_pe and
+// qk_nope, rotates the 128 values with the orthonormal Hadamard transform and then
+// quantizes; its FP4 path lacks the rotation for want of a standalone FP4 quantizer.
+// This is that quantizer: y = BF16(WHT_128(cat(pe, nope)) / sqrt(128)) per row, then
+// the row-wise NVFP4 encode of the grouped path (TransformerEngine PR #2564 / #2555:
+// 1x16 E2M1 blocks with E4M3 block scales) with one FP32 tensor scale over the whole
+// rotated tensor, g = fl(max(A, F(1e-10)) * F(1/2688)), A measured or supplied.
+//
+// A row is held by 4 consecutive lanes, 32 values each (wht128_quarter), so every
+// 1x16 block lies inside one lane: its maximum, scale code and 16 codes need no
+// exchange.  The encode is the grouped path's: block_code, then one multiply per
+// element by the table's multiplier (exact division where the table has none).
+#include "mxq_nvfp4_impl.hpp"
+
+namespace mxq {
+
+namespace {
+
+constexpr int kDsaRows = 64;          // rows per 256-thread work-group
+
+// Maximum of a non-negative, NaN-free per-thread value over the 256-thread
+// work-group (red: 4 floats of LDS), returned to every thread.
+__device__ __forceinline__ float wg_max(float v, float* red) {
+    v = wave_max_f32(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+// The lane's 32 butterfly outputs split into its two 1x16 blocks.
+__device__ __forceinline__ void halves(const float (&v)[32], float (&h0)[16], float (&h1)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        h0[i] = v[i];
+        h1[i] = v[16 + i];
+    }
+}
+
+}  // namespace
+
+// Phase A: max |y| of the work-group's 64 rows into its partial (a plain store:
+// the scale kernel that folds the partials runs after this kernel has ended).
+__global__ __launch_bounds__(256) void k_dsa_nvfp4_amax(const DsaNvfp4Args a) {
+    __shared__ float red[4];
+    const int quarter = threadIdx.x & 3;
+    const int64_t r = (int64_t)blockIdx.x * kDsaRows + (threadIdx.x >> 2);
+    const bool live = r < a.m;
+    float v[32];
+    wht128_quarter(a.pe, a.ld_pe, a.d_pe, a.nope, a.ld_nope, r, live, quarter, v);
+    // max |BF16(fl(v C))| = BF16(fl(max |v| C)) (both roundings are monotone); a
+    // NaN input reaches all 128 outputs of its row, which is then left out
+    float h0[16], h1[16];
+    halves(v, h0, h1);
+    const float m = __builtin_fmaxf(absmax16(h0), absmax16(h1));
+    const float lane = v[0] != v[0] ? 0.0f : round_bf16(m * k_inv_sqrt128());
+    const float wg = wg_max(lane, red);
+    if (threadIdx.x == 0) a.partials[blockIdx.x] = wg;
+}
+
+// The tensor scale and the scale table: A is the supplied amax, or the maximum of
+// the partials (measured), or 0 for a tensor without rows.  With a supplied amax
+// the measured-amax output is zeroed here and raised by the quantize kernel.
+__global__ __launch_bounds__(256) void k_dsa_nvfp4_scale(const DsaNvfp4Args a) {
+    __shared__ float red[4];
+    float A = 0.0f;
+    if (a.amax_in) {
+        A = *a.amax_in;
+    } else if (a.m > 0) {
+        float p = 0.0f;
+        for (int i = threadIdx.x; i < a.n_wg; i += 256) p = __builtin_fmaxf(p, a.partials[i]);
+        A = wg_max(p, red);
+    }
+    const float g = tensor_scale(A);
+    if (a.m > 0 && threadIdx.x < 128) a.table[threadIdx.x] = table_entry((int)threadIdx.x, g, false);
+    if (threadIdx.x == 0) {
+        *a.global_scale = g;
+        if (a.amax_out) *a.amax_out = a.amax_in ? 0.0f : A;
+    }
+}
+
+// Phase B: rotate again and encode.  AOUT: the amax was supplied and the measured
+// one is wanted out (an atomic maximum per work-group).
+template <bool AOUT>
+__global__ __launch_bounds__(256) void k_dsa_nvfp4_quant(const DsaNvfp4Args a) {
+    __shared__ float4 tab[128];
+    __shared__ float red[4];
+    if (threadIdx.x < 128) tab[threadIdx.x] = a.table[threadIdx.x];
+    __syncthreads();
+    const float g = tab[0].x, yg = tab[0].y;
+    const int quarter = threadIdx.x & 3;
+    const int64_t r = (int64_t)blockIdx.x * kDsaRows + (threadIdx.x >> 2);
+    const bool live = r < a.m;
+    float v[32];
+    wht128_quarter(a.pe, a.ld_pe, a.d_pe, a.nope, a.ld_nope, r, live, quarter, v);
+    const bool nan = v[0] != v[0];                   // the whole row is NaN
+    const float c = k_inv_sqrt128();
+    const u32x4 no_rnd = {0, 0, 0, 0};
+    float h[2][16];
+    halves(v, h[0], h[1]);
+    BlockOut o[2];
+    float lane_max = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const float ab = round_bf16(absmax16(h[b]) * c);             // block max |y|
+        const uint32_t sc = block_code(ab, g, yg);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) h[b][i] = round_bf16(h[b][i] * c);
+        o[b] = encode_block<Enc::Mul>(h[b], sc, nan, tab, no_rnd);
+        lane_max = __builtin_fmaxf(lane_max, ab);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+        if (o[b].unsafe) o[b] = encode_block<Enc::Div>(h[b], o[b].scale, nan, tab, no_rnd);
+    if (live) {
+        *reinterpret_cast<uint4*>(a.codes + r * 64 + quarter * 16) =
+            make_uint4(o[0].codes.x, o[0].codes.y, o[1].codes.x, o[1].codes.y);
+        *reinterpret_cast<uint16_t*>(a.scales + r * 8 + quarter * 2) = (uint16_t)(o[0].scale | (o[1].scale << 8));
+    }
+    if (AOUT) {
+        const float wg = wg_max(live && !nan ? lane_max : 0.0f, red);
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(a.amax_out), __builtin_bit_cast(uint32_t, wg),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+hipError_t launch_hadamard_quant_nvfp4(const DsaNvfp4Args& a, hipStream_t stream) {
+    const bool given = a.amax_in != nullptr;
+    hipError_t e = launch_mark(0, stream);
+    if (e != hipSuccess) return e;
+    if (!given && a.m > 0) {
+        hipLaunchKernelGGL(k_dsa_nvfp4_amax, dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_dsa_nvfp4_scale, dim3(1), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess || a.m == 0) return e;
+    if ((e = launch_mark(1, stream)) != hipSuccess) return e;
+    if (given && a.amax_out)
+        hipLaunchKernelGGL((k_dsa_nvfp4_quant<true>), dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_dsa_nvfp4_quant<false>), dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_mark(2, stream);
+}
+
+}  // namespace mxq

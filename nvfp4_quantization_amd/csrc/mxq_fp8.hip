@@ -81,40 +81,7 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
     const bool live = r < a.m;
 
     float v[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e0 = (quarter * 4 + q) * 8;
-        uint4 w = {0, 0, 0, 0};
-        if (live) {
-            const uint16_t* src = e0 < a.d_pe ? a.pe + r * a.ld_pe + e0 : a.nope + r * a.ld_nope + (e0 - a.d_pe);
-            w = *reinterpret_cast<const uint4*>(src);
-        }
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[q * 8 + 2 * i] = lo_bf16(ww[i]);
-            v[q * 8 + 2 * i + 1] = hi_bf16(ww[i]);
-        }
-    }
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if (i & h) continue;
-            const float x0 = v[i], x1 = v[i + h];
-            v[i] = x0 + x1;
-            v[i + h] = x0 - x1;
-        }
-    }
-#pragma unroll
-    for (int lanebit = 1; lanebit <= 2; lanebit <<= 1) {
-        const bool upper = (quarter & lanebit) != 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float other = shfl_xor_f32(v[i], lanebit);
-            v[i] = upper ? other - v[i] : v[i] + other;
-        }
-    }
+    wht128_quarter(a.pe, a.ld_pe, a.d_pe, a.nope, a.ld_nope, r, live, quarter, v);
     uint32_t w[16];
     const float c = k_inv_sqrt128();
 #pragma unroll

@@ -27,6 +27,31 @@ struct DsaArgs {
 };
 hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- DSA rotate + NVFP4
+// With a measured tensor amax three kernels: the first rotates 64 rows per
+// 256-thread work-group and stores the work-group's max |y| as a partial; a
+// one-work-group kernel folds the partials into the tensor scale and writes the
+// scale table; the last rotates again and encodes.  With a supplied amax the first
+// is left out.
+struct DsaNvfp4Args {
+    const uint16_t* pe;
+    const uint16_t* nope;
+    int64_t ld_pe, ld_nope, m;
+    int32_t d_pe;
+    int32_t n_wg;                     // work-groups of the row kernels
+    uint8_t* codes;                   // [m][64]
+    uint8_t* scales;                  // [m][8]
+    float* global_scale;              // [1]
+    const float* amax_in;             // [1] or null: measure
+    float* amax_out;                  // [1] or null
+    float4* table;                    // workspace: 128 scale-table entries
+    float* partials;                  // workspace: one max per work-group
+};
+hipError_t launch_hadamard_quant_nvfp4(const DsaNvfp4Args& a, hipStream_t stream);
+// Workspace layout of the DSA NVFP4 call (byte offsets).
+constexpr int64_t kDsaTableOffset = 0;
+constexpr int64_t kDsaPartialsOffset = kDsaTableOffset + 128 * 16;
+
 // ---------------------------------------------------------------- grouped NVFP4
 // One launch group per at most kGroupSections sections.  A group runs two kernels
 // on the caller's stream, one wave per 128 x 128 tile in each (with a caller-supplied

@@ -437,26 +437,29 @@ __device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2]
     return amax;
 }
 
-// Scale tables of section s; entry 0 (scale code 0 never divides) holds (g, fl(1/g)).
+// Scale-table entry of scale code `code` for tensor scale g: (d, fl(1/d), ym, 0)
+// with d = fl(E4M3(code) * g), or (4d, fl(1/d)/4, ...) for column values that enter
+// unscaled (quarter); entry 0 (scale code 0 never divides) holds (g, fl(1/g)).
+__device__ __forceinline__ float4 table_entry(int code, float g, bool quarter) {
+    if (code == 0) {
+        const float yg = 1.0f / g;
+        return make_float4(g, yg, yg, 0.0f);
+    }
+    float d = e4m3_value((uint32_t)code) * g;
+    float y = 1.0f / d;
+    if (quarter) { d *= 4.0f; y *= 0.25f; }
+    const float ym = code == 127 ? y : product_multiplier(d, y);
+    return make_float4(d, y, ym, 0.0f);
+}
+
+// Scale tables of section s (row-wise, then column-wise).
 template <bool ROW, bool COL>
 __device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g_r, float g_c) {
 #pragma unroll
     for (int e = threadIdx.x; e < 256; e += 64) {
         const int dir = e >> 7, code = e & 127;
         if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
-        const float g = dir ? g_c : g_r;
-        float4 entry;
-        if (code == 0) {
-            const float yg = 1.0f / g;
-            entry = make_float4(g, yg, yg, 0.0f);
-        } else {
-            float d = e4m3_value((uint32_t)code) * g;
-            float y = 1.0f / d;
-            if (dir) { d *= 4.0f; y *= 0.25f; }
-            const float ym = code == 127 ? y : product_multiplier(d, y);
-            entry = make_float4(d, y, ym, 0.0f);
-        }
-        G.tables[(s * 2 + dir) * 128 + code] = entry;
+        G.tables[(s * 2 + dir) * 128 + code] = table_entry(code, dir ? g_c : g_r, dir == 1);
     }
 }
 

@@ -166,3 +166,40 @@ def test_launch_marks_arguments(L):
     assert L.mxq_set_launch_marks(A, None, None) == INVALID
     assert L.mxq_set_launch_marks(None, A, A) == INVALID
     assert L.mxq_set_launch_marks(None, None, None) == 0
+
+
+def dsa4(L, pe=A, ld_pe=64, d_pe=64, nope=A, ld_nope=64, m=8, amax_in=None, amax_out=None, codes=A, scales=A,
+         g=A, ws=A, ws_bytes=1 << 20):
+    return L.mxq_hadamard_quant_nvfp4(pe, ld_pe, d_pe, nope, ld_nope, m, amax_in, amax_out, codes, scales, g,
+                                      ws, ws_bytes, None)
+
+
+def test_dsa_nvfp4_argument_errors(L):
+    """The DSA rotate + NVFP4 call checks everything on the host; a call without
+    rows needs no workspace but still writes the tensor scale."""
+    assert dsa4(L, d_pe=60, ld_pe=60, ld_nope=68) == MISALIGNED
+    assert dsa4(L, d_pe=136) == INVALID
+    assert dsa4(L, ld_nope=32) == INVALID
+    assert dsa4(L, pe=None) == INVALID
+    assert dsa4(L, codes=None) == INVALID
+    assert dsa4(L, g=None) == INVALID
+    assert dsa4(L, g=A + 2) == MISALIGNED
+    assert dsa4(L, amax_in=A + 1) == MISALIGNED
+    assert dsa4(L, amax_out=A + 2) == MISALIGNED
+    assert dsa4(L, scales=A + 8) == MISALIGNED
+    assert dsa4(L, ws=None) == INVALID
+    assert dsa4(L, ws=A + 128) == MISALIGNED
+    assert dsa4(L, m=-1) == INVALID
+    assert dsa4(L, m=1 << 31) == UNSUPPORTED
+    need = L.mxq_hadamard_quant_nvfp4_workspace_size(8)
+    assert dsa4(L, ws_bytes=need - 1) == 3                        # MXQ_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_dsa_nvfp4_workspace_size(L):
+    """128 table entries, then 4 bytes per 64 rows, rounded to 256."""
+    q = L.mxq_hadamard_quant_nvfp4_workspace_size
+    assert q(0) == 0 and q(-5) == 0
+    assert q(1) == 2048 + 256
+    assert q(64 * 64) == 2048 + 256
+    assert q(64 * 64 + 1) == 2048 + 512
+    assert q(262144) == 2048 + 4 * 4096

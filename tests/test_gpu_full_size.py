@@ -43,6 +43,20 @@ def test_full_dsa(orc):
     assert_same("scales", host(s), np.concatenate([p[1] for p in parts]))
 
 
+def test_full_dsa_nvfp4(orc):
+    dev = device()
+    announce("full size: DSA rotate+NVFP4 4096 tokens x 64 heads")
+    w = synth.dsa_rotate_fp8(device=dev)
+    call = mxq.HadamardNVFP4(w.tensors["pe"], w.tensors["nope"], amax_out=True)
+    res = call()
+    torch.cuda.synchronize()
+    ref = orc.hadamard_quant_nvfp4(bits16(w.tensors["pe"]), bits16(w.tensors["nope"]))
+    assert_same("global_scale", host(res.global_scale), np.array([ref.global_scale], np.float32))
+    assert_same("amax", host(res.amax), np.array([ref.amax], np.float32))
+    assert_same("scales", host(res.scales), ref.scales)
+    assert_same("codes", host(res.codes), ref.codes)
+
+
 def _grouped_full(orc, w, dev):
     p = w.params
     x = w.tensors["x"]

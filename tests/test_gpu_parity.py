@@ -130,6 +130,92 @@ def test_dsa_strided_and_edges(orc):
     assert_same("scales", host(s), rs)
 
 
+# ============================================================== DSA rotate + NVFP4
+def compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_in=None, amax_out=False, call=None):
+    """The DSA rotate + NVFP4 call on device tensors pe / nope against the oracle on
+    their host bit patterns pe_np / nope_np, every byte."""
+    if call is None:
+        call = mxq.HadamardNVFP4(pe, nope, amax_in=amax_in, amax_out=amax_out)
+    res = call()
+    torch.cuda.synchronize()
+    ref = orc.hadamard_quant_nvfp4(pe_np, nope_np, amax_in=amax_in)
+    assert_same("global_scale", host(res.global_scale), np.array([ref.global_scale], np.float32))
+    assert_same("scales", host(res.scales), ref.scales)
+    assert_same("codes", host(res.codes), ref.codes)
+    if amax_out:
+        assert_same("amax", host(res.amax), np.array([ref.amax], np.float32))
+    return res, ref
+
+
+@pytest.mark.parametrize("tokens,heads,d_pe", [(64, 8, 64), (7, 9, 64), (32, 4, 0), (32, 4, 128), (16, 5, 8),
+                                               (625, 32, 64)])
+def test_dsa_nvfp4_random(orc, tokens, heads, d_pe):
+    dev = device()
+    announce(f"dsa nvfp4 tokens={tokens} heads={heads} d_pe={d_pe}")
+    w = synth.dsa_rotate_fp8(tokens=tokens, heads=heads, d_pe=d_pe, seed=300 + tokens)
+    pe = w.tensors["pe"].to(dev) if d_pe > 0 else None
+    nope = w.tensors["nope"].to(dev) if d_pe < 128 else None
+    compare_dsa4(orc, bits16(w.tensors["pe"]), bits16(w.tensors["nope"]), pe, nope, amax_out=True)
+
+
+def test_dsa_nvfp4_strided_and_edges(orc):
+    """NaN rows, zero / -0 / subnormal rows, exact ties, rows 2^-30 .. 2^30 apart (the
+    small ones underflow to scale code 0 under the one tensor scale), and pe / nope
+    as column slices of wider rows."""
+    dev = device()
+    announce("dsa nvfp4 strided + edges")
+    m = 100
+    b = edge_matrix(m, 128, 19)
+    big = np.zeros((m, 256), np.uint16)
+    big[:, :64] = b[:, :64]
+    big[:, 128:192] = b[:, 64:]
+    t = bf16_dev(big, dev)
+    compare_dsa4(orc, b[:, :64], b[:, 64:], t[:, :64], t[:, 128:192], amax_out=True)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.25, 4.0])
+def test_dsa_nvfp4_supplied_amax(orc, scale):
+    """A supplied amax (the measured one times `scale`): one pass, saturating blocks
+    above it; the measured amax comes out as well."""
+    dev = device()
+    announce(f"dsa nvfp4 supplied amax x{scale}")
+    w = synth.dsa_rotate_fp8(tokens=48, heads=8, seed=77)
+    pe_np, nope_np = bits16(w.tensors["pe"]), bits16(w.tensors["nope"])
+    A = orc.hadamard_quant_nvfp4(pe_np, nope_np).amax
+    amax_in = np.float32(A * np.float32(scale))
+    compare_dsa4(orc, pe_np, nope_np, w.tensors["pe"].to(dev), w.tensors["nope"].to(dev),
+                 amax_in=float(amax_in), amax_out=True)
+
+
+def test_dsa_nvfp4_empty(orc):
+    """No rows: only the tensor scale (the floor, or the supplied amax's) and a zero
+    measured amax."""
+    dev = device()
+    announce("dsa nvfp4 empty")
+    z = np.zeros((0, 64), np.uint16)
+    for amax_in in (None, 2.5):
+        res = mxq.mxq_hadamard_quant_nvfp4(bf16_dev(z, dev), bf16_dev(z, dev), amax_in=amax_in, amax_out=True)
+        torch.cuda.synchronize()
+        ref = orc.hadamard_quant_nvfp4(z, z, amax_in=amax_in)
+        assert_same("global_scale", host(res.global_scale), np.array([ref.global_scale], np.float32))
+        assert_same("amax", host(res.amax), np.zeros(1, np.float32))
+
+
+def test_dsa_nvfp4_reuse(orc):
+    """One prepared call run twice, then a smaller input through the same workspace
+    (left over partials and table from the larger call): every run matches."""
+    dev = device()
+    announce("dsa nvfp4 reuse")
+    w = synth.dsa_rotate_fp8(tokens=100, heads=8, seed=78)
+    pe, nope = w.tensors["pe"].to(dev), w.tensors["nope"].to(dev)
+    pe_np, nope_np = bits16(w.tensors["pe"]), bits16(w.tensors["nope"])
+    call = mxq.HadamardNVFP4(pe, nope, amax_out=True)
+    compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_out=True, call=call)
+    compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_out=True, call=call)
+    small = mxq.HadamardNVFP4(pe[:300], nope[:300], workspace=call.workspace)
+    compare_dsa4(orc, pe_np[:300], nope_np[:300], pe[:300], nope[:300], call=small)
+
+
 # ============================================================== grouped NVFP4
 def compare_grouped(orc, x_dev, sections, mask, flags, seed=None, ro=None, co=None, out=None, threads=8):
     call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, out=out)
