@@ -54,6 +54,14 @@ def lib():
         L.oracle_quant_fp8_1x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64]
         L.oracle_hadamard_quant_fp8.restype = None
         L.oracle_hadamard_quant_fp8.argtypes = [_p, _i64, ctypes.c_int32, _p, _i64, _i64, _p, _p]
+        L.oracle_exp.restype = ctypes.c_float
+        L.oracle_exp.argtypes = [ctypes.c_float]
+        L.oracle_silu.restype = ctypes.c_float
+        L.oracle_silu.argtypes = [ctypes.c_float]
+        L.oracle_exp_n.argtypes = [_p, _i64, _p]
+        L.oracle_silu_n.argtypes = [_p, _i64, _p]
+        L.oracle_swiglu_quant_fp8.restype = None
+        L.oracle_swiglu_quant_fp8.argtypes = [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64]
         L.oracle_hadamard_quant_nvfp4.restype = None
         L.oracle_hadamard_quant_nvfp4.argtypes = [_p, _i64, ctypes.c_int32, _p, _i64, _i64, _p, _p, _p, _p, _p]
         L.oracle_nvfp4_global_scale.restype = ctypes.c_float
@@ -176,6 +184,49 @@ def hadamard_quant_fp8(pe, nope):
     s = np.empty((m,), np.float32)
     lib().oracle_hadamard_quant_fp8(_ptr(pe), max(d_pe, 1), d_pe, _ptr(nope), max(128 - d_pe, 1),
                                     m, _ptr(q), _ptr(s))
+    return q, s
+
+
+def fp8_group(x):
+    """FP8 1x128 of one group of 128 float32 values: (scale, codes [128])."""
+    x = _c(x, np.float32)
+    assert x.size == 128
+    codes = np.empty(128, np.uint8)
+    s = lib().oracle_fp8_group(_ptr(x), _ptr(codes))
+    return np.float32(s), codes
+
+
+def exp(x):
+    """EXP over an array of float32 values."""
+    x = _c(x, np.float32)
+    out = np.empty_like(x)
+    lib().oracle_exp_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def silu(x):
+    """SILU over an array of float32 values."""
+    x = _c(x, np.float32)
+    out = np.empty_like(x)
+    lib().oracle_silu_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def swiglu_quant_fp8(gate, up, scale_transposed=False):
+    """gate, up: [m][n] uint16 (BF16 bits), n % 128 == 0.  Returns (codes [m][n],
+    scales [m][n/128] or [n/128][m] when scale_transposed)."""
+    gate = _c(gate, np.uint16)
+    up = _c(up, np.uint16)
+    m, n = gate.shape
+    assert up.shape == (m, n) and n % 128 == 0
+    q = np.empty((m, n), np.uint8)
+    if scale_transposed:
+        s = np.empty((n // 128, m), np.float32)
+        sr, sg = 1, m
+    else:
+        s = np.empty((m, n // 128), np.float32)
+        sr, sg = n // 128, 1
+    lib().oracle_swiglu_quant_fp8(_ptr(gate), n, _ptr(up), n, m, n, _ptr(q), n, _ptr(s), sr, sg)
     return q, s
 
 

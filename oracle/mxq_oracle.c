@@ -498,3 +498,68 @@ void oracle_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d_pe
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* SwiGLU -> FP8 1x128                                                       */
+/* ------------------------------------------------------------------------ */
+/* 2^j for an integer j in [-126, 127] (a normal binary32). */
+static float pow2i(int j) { return bits_f32((uint32_t)(j + 127) << 23); }
+
+float oracle_exp(float x)
+{
+    if (x != x) return x;
+    if (x > 128.0f) x = 128.0f;            /* e^128 and e^-128 are already beyond */
+    if (x < -128.0f) x = -128.0f;          /* binary32's range                    */
+    const float log2e = (float)(1.0 / log(2.0));
+    const float L1 = 0.693145751953125f;   /* ln 2 to 16 significant bits */
+    const float L2 = (float)(log(2.0) - 0.693145751953125);
+    float k = rintf(x * log2e);            /* nearest integer, ties to even */
+    float r = fmaf(-k, L1, x);
+    r = fmaf(-k, L2, r);
+    /* e^r by its Taylor polynomial of degree 7, Horner's rule from the top */
+    double fact = 1.0;
+    for (int n = 2; n <= 7; ++n) fact *= n;            /* 7! */
+    float p = (float)(1.0 / fact);
+    for (int n = 6; n >= 0; --n) {
+        fact /= (n + 1);                                 /* n! */
+        p = fmaf(p, r, (float)(1.0 / fact));
+    }
+    int ki = (int)k;
+    int k1 = (int)floorf(k * 0.5f), k2 = ki - k1;
+    return (p * pow2i(k1)) * pow2i(k2);
+}
+
+float oracle_silu(float g)
+{
+    float e = oracle_exp(-g);
+    float t = 1.0f + e;
+    return g / t;
+}
+
+void oracle_swiglu_quant_fp8(const uint16_t* gate, int64_t ld_gate, const uint16_t* up, int64_t ld_up,
+                             int64_t m, int64_t n, uint8_t* q, int64_t ldq, float* scales,
+                             int64_t scale_stride_row, int64_t scale_stride_group)
+{
+    float h[128];
+    for (int64_t r = 0; r < m; ++r) {
+        for (int64_t g0 = 0; g0 < n; g0 += 128) {
+            for (int i = 0; i < 128; ++i) {
+                float gv = oracle_bf16_to_f32(gate[r * ld_gate + g0 + i]);
+                float uv = oracle_bf16_to_f32(up[r * ld_up + g0 + i]);
+                h[i] = oracle_silu(gv) * uv;       /* FP32, no rounding to the input type */
+            }
+            scales[r * scale_stride_row + (g0 / 128) * scale_stride_group] =
+                oracle_fp8_group(h, q + r * ldq + g0);
+        }
+    }
+}
+
+void oracle_exp_n(const float* x, int64_t count, float* out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = oracle_exp(x[i]);
+}
+
+void oracle_silu_n(const float* x, int64_t count, float* out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = oracle_silu(x[i]);
+}

@@ -91,6 +91,27 @@ void oracle_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d_pe
                                  const float* amax_in, uint8_t* codes, uint8_t* scales,
                                  float* global_scale, float* amax_out);
 
+/* ---- SwiGLU -> FP8 1x128 ---------------------------------------------------------
+ * EXP(x), e^x in binary32 by these steps (one rounding per operation):
+ *   NaN -> NaN; x clamped to [-128, 128];
+ *   k = rint(fl(x * F(log2 e))); r = fma(-k, L1, x); r = fma(-k, L2, r) with
+ *   L1 = 0.693145751953125 (ln 2 to 16 bits) and L2 = F(ln 2 - L1);
+ *   p = the degree-7 Taylor polynomial of e^r with coefficients F(1/n!) by Horner's
+ *   rule (p = fma(p, r, F(1/n!)) from n = 6 down to 0, starting from F(1/7!));
+ *   result = fl(fl(p * 2^k1) * 2^k2), k1 = floor(k/2), k2 = k - k1.
+ * SILU(g) = fl(g / fl(1 + EXP(-g)));  the SwiGLU value h = fl(SILU(gate) * up) stays
+ * FP32 and goes straight into FP8 1x128 (oracle_fp8_group). */
+float oracle_exp(float x);
+float oracle_silu(float g);
+/* gate [m][ld_gate], up [m][ld_up] BF16; n % 128 == 0; q [m][ldq];
+ * scales[r*scale_stride_row + g*scale_stride_group] for group g of row r. */
+void oracle_swiglu_quant_fp8(const uint16_t* gate, int64_t ld_gate, const uint16_t* up, int64_t ld_up,
+                             int64_t m, int64_t n, uint8_t* q, int64_t ldq, float* scales,
+                             int64_t scale_stride_row, int64_t scale_stride_group);
+/* count values through oracle_exp / oracle_silu (for sweeps) */
+void oracle_exp_n(const float* x, int64_t count, float* out);
+void oracle_silu_n(const float* x, int64_t count, float* out);
+
 /* ---- NVFP4 -------------------------------------------------------------------- */
 /* g = fl(max(A, F(1e-10)) * F(1/2688)) */
 float oracle_nvfp4_global_scale(float amax);
