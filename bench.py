@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="grouped_nvfp4_rht",
                     choices=["grouped_nvfp4_rht", "grouped_nvfp4_rht_sr", "large_moe_nvfp4_fp8",
-                             "dsa_rotate_fp8", "dsa_rotate_nvfp4", "fp8_1x128"])
+                             "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8", "fp8_1x128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="steady-state steps only, then one 256 MiB device copy (the counter calibration "
@@ -60,7 +60,7 @@ def main():
 
     # ---------------------------------------------------------------- workload
     wl = args.workload
-    grouped = wl not in ("fp8_1x128", "dsa_rotate_fp8", "dsa_rotate_nvfp4")
+    grouped = wl not in ("fp8_1x128", "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8")
     if wl == "fp8_1x128":
         w = synth.plain_fp8(device=dev)
         x = w.tensors["x"]
@@ -89,6 +89,20 @@ def main():
         in_bytes = m * 128 * 2
         alg_bytes = in_bytes + m * 128 + m * 4
         desc = f"dsa cat+WHT128+fp8_1x128, {m} rows (4096 tokens x 64 heads) bf16"
+    elif wl == "swiglu_fp8":
+        w = synth.swiglu_fp8(device=dev)
+        gu = w.tensors["gate_up"]
+        m, n = gu.shape[0], gu.shape[1] // 2
+
+        def make_call():
+            gi = gu.clone()
+            q = torch.empty((m, n), dtype=torch.uint8, device=dev)
+            s = torch.empty((m, n // 128), dtype=torch.float32, device=dev)
+            return lambda: mxq.mxq_swiglu_quant_fp8(gi[:, :n], gi[:, n:], q=q, scales=s)
+        call = make_call()
+        in_bytes = m * n * 2 * 2
+        alg_bytes = in_bytes + m * n + m * (n // 128) * 4
+        desc = f"swiglu -> fp8_1x128, {m} tokens x {n} (fused gate|up bf16 buffer)"
     elif wl == "dsa_rotate_nvfp4":
         w = synth.dsa_rotate_fp8(device=dev)
         pe, nope = w.tensors["pe"], w.tensors["nope"]
@@ -162,6 +176,20 @@ def main():
     kern = None
     if grouped:
         kern = kernel_times(mxq, torch, calls, n_sets, K, stream, ("k_nvfp4_amax", "k_nvfp4_quant"))
+    elif wl == "swiglu_fp8":
+        w = synth.swiglu_fp8(device=dev)
+        gu = w.tensors["gate_up"]
+        m, n = gu.shape[0], gu.shape[1] // 2
+
+        def make_call():
+            gi = gu.clone()
+            q = torch.empty((m, n), dtype=torch.uint8, device=dev)
+            s = torch.empty((m, n // 128), dtype=torch.float32, device=dev)
+            return lambda: mxq.mxq_swiglu_quant_fp8(gi[:, :n], gi[:, n:], q=q, scales=s)
+        call = make_call()
+        in_bytes = m * n * 2 * 2
+        alg_bytes = in_bytes + m * n + m * (n // 128) * 4
+        desc = f"swiglu -> fp8_1x128, {m} tokens x {n} (fused gate|up bf16 buffer)"
     elif wl == "dsa_rotate_nvfp4":
         kern = kernel_times(mxq, torch, calls, n_sets, K, stream,
                             ("k_dsa_nvfp4_amax+k_dsa_nvfp4_scale", "k_dsa_nvfp4_quant"))

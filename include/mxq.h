@@ -2,8 +2,9 @@
  * mxq.h -- C ABI of the mxq block-quantization library for AMD Instinct MI355X
  * (gfx950).
  *
- * Four entry points quantize BF16 activations on the GPU:
+ * Five entry points quantize BF16 activations on the GPU:
  *   mxq_quant_fp8_1x128        FP8 E4M3 with one FP32 scale per 1x128 group
+ *   mxq_swiglu_quant_fp8       FP32 SiLU(gate) * up -> FP8 1x128 (no BF16 round)
  *   mxq_hadamard_quant_fp8     cat[qk_pe, qk_nope] -> normalized 128-point
  *                              Walsh-Hadamard rotation -> FP8 1x128
  *   mxq_hadamard_quant_nvfp4   the same rotation -> NVFP4 row-wise (1x16 blocks,
@@ -96,6 +97,32 @@ mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int
                                uint8_t* q_e4m3, int64_t ldq,
                                float* scales, int64_t scale_stride_row, int64_t scale_stride_group,
                                void* stream);
+
+/* ---------------------------------------------------------------------------
+ * SwiGLU -> FP8 1x128: the second dynamic quantizer of a W8A8 MoE, directly after
+ * the FP32 SiLU/SwiGLU of the gate and up projections (onnxruntime PR #33644,
+ * Description: no round to the input type between SwiGLU and the quantizer; the
+ * same FP8 recipe as mxq_quant_fp8_1x128).  For each element:
+ *   h = fl(SILU(gate) * up),  SILU(g) = fl(g / fl(1 + EXP(-g)))   (all FP32)
+ * and then, per group G of 128 consecutive h of a row, exactly as
+ * mxq_quant_fp8_1x128 (a = max |h| without NaNs, s = fl(max(a, F(1e-10)) * F(1/448)),
+ * q = E4M3(fl(h / s)), 0x7F for a NaN).  EXP(x) is e^x by a stated binary32
+ * algorithm (the pages do not fix one): NaN kept; x clamped to [-128, 128];
+ * k = rint(fl(x * F(log2 e))); r = fma(-k, 0.693145751953125, x);
+ * r = fma(-k, F(ln 2 - 0.693145751953125), r); p = the degree-7 Taylor polynomial of
+ * e^r with coefficients F(1/n!) by Horner's rule with fma; EXP = fl(fl(p * 2^k1) * 2^k2),
+ * k1 = floor(k/2), k2 = k - k1.  Inputs whose product overflows FP32 are out of
+ * contract (as are infinite inputs).
+ *
+ *   gate_bf16 [m][ld_gate], up_bf16 [m][ld_up] BF16 (separate buffers, or the two
+ *             halves of one [m][2n] buffer with up = gate + n)
+ *   q_e4m3    [m][ldq] E4M3 codes; scales as mxq_quant_fp8_1x128 (row / group strides)
+ * Requirements: n % 128 == 0; ld_gate, ld_up multiples of 8, ldq of 16; gate, up,
+ * q 16-byte aligned; scales 4-byte aligned.  m == 0 is a successful no-op.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_swiglu_quant_fp8(const uint16_t* gate_bf16, int64_t ld_gate, const uint16_t* up_bf16, int64_t ld_up,
+                                int64_t m, int64_t n, uint8_t* q_e4m3, int64_t ldq,
+                                float* scales, int64_t scale_stride_row, int64_t scale_stride_group, void* stream);
 
 /* ---------------------------------------------------------------------------
  * DSA-indexer rotate + quantize.  For each row r:

@@ -26,7 +26,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_MISALIGNED",
 EXPORTED = ("mxq_status_string", "mxq_version", "mxq_quant_fp8_1x128", "mxq_hadamard_quant_fp8",
             "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4",
             "mxq_group_rht_quant_nvfp4_with_amax", "mxq_set_launch_marks",
-            "mxq_hadamard_quant_nvfp4_workspace_size", "mxq_hadamard_quant_nvfp4")
+            "mxq_hadamard_quant_nvfp4_workspace_size", "mxq_hadamard_quant_nvfp4", "mxq_swiglu_quant_fp8")
 
 
 class MxqError(RuntimeError):
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_rht_quant_nvfp4_with_amax.restype = ctypes.c_int
         L.mxq_group_rht_quant_nvfp4_with_amax.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
                                                           p, p, p, p, p, ctypes.c_size_t, p]
+        L.mxq_swiglu_quant_fp8.restype = ctypes.c_int
+        L.mxq_swiglu_quant_fp8.argtypes = [p, i64, p, i64, i64, i64, p, i64, p, i64, i64, p]
         L.mxq_hadamard_quant_nvfp4_workspace_size.restype = ctypes.c_size_t
         L.mxq_hadamard_quant_nvfp4_workspace_size.argtypes = [i64]
         L.mxq_hadamard_quant_nvfp4.restype = ctypes.c_int
@@ -189,6 +191,31 @@ def mxq_hadamard_quant_fp8(pe: Optional[torch.Tensor], nope: Optional[torch.Tens
     ld_nope = _row_stride(nope)
     _check(lib().mxq_hadamard_quant_fp8(_ptr(pe), ld_pe, d_pe, _ptr(nope), ld_nope, m, _ptr(q), _ptr(scales),
                                         _stream(stream)), "mxq_hadamard_quant_fp8")
+    return q, scales
+
+
+# ---------------------------------------------------------------------------- SwiGLU -> FP8
+def mxq_swiglu_quant_fp8(gate: torch.Tensor, up: torch.Tensor, q: Optional[torch.Tensor] = None,
+                         scales: Optional[torch.Tensor] = None, scale_transposed: bool = False, stream=None):
+    """FP32 SiLU(gate) * up -> FP8 1x128 along the last dim.  gate, up: [m][n] BF16 with
+    unit column stride (row strides may differ: two halves of one [m][2n] buffer
+    work).  Returns (codes [m][n], scales [m][n/128], or [n/128][m] when transposed)."""
+    m, n = gate.shape
+    if up.shape != (m, n):
+        raise ValueError("gate and up must have the same shape")
+    for t in (gate, up):
+        if t.numel() > 0 and t.stride(1) != 1:
+            raise ValueError("gate / up need unit column stride")
+    gate, up = _bf16_bits(gate), _bf16_bits(up)
+    if q is None:
+        q = torch.empty((m, n), dtype=torch.uint8, device=gate.device)
+    if scales is None:
+        shape = (n // 128, m) if scale_transposed else (m, n // 128)
+        scales = torch.empty(shape, dtype=torch.float32, device=gate.device)
+    sr, sg = (1, m) if scale_transposed else (n // 128, 1)
+    _check(lib().mxq_swiglu_quant_fp8(_ptr(gate), _row_stride(gate), _ptr(up), _row_stride(up), m, n,
+                                      _ptr(q), _row_stride(q), _ptr(scales), sr, sg, _stream(stream)),
+           "mxq_swiglu_quant_fp8")
     return q, scales
 
 

@@ -74,6 +74,23 @@ mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int
     return mxq::launch_quant_fp8_1x128(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
+mxq_status mxq_swiglu_quant_fp8(const uint16_t* gate_bf16, int64_t ld_gate, const uint16_t* up_bf16, int64_t ld_up,
+                                int64_t m, int64_t n, uint8_t* q_e4m3, int64_t ldq,
+                                float* scales, int64_t scale_stride_row, int64_t scale_stride_group, void* stream) {
+    if (m < 0 || n <= 0 || ld_gate < n || ld_up < n || ldq < n || scale_stride_row < 0 || scale_stride_group < 0)
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (n % 128 != 0 || ld_gate % 8 != 0 || ld_up % 8 != 0 || ldq % 16 != 0) return MXQ_ERR_MISALIGNED;
+    if (m == 0) return MXQ_OK;
+    if (!gate_bf16 || !up_bf16 || !q_e4m3 || !scales) return MXQ_ERR_INVALID_ARGUMENT;
+    if (!aligned(gate_bf16, 16) || !aligned(up_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4))
+        return MXQ_ERR_MISALIGNED;
+    if (m > kMaxRows || m * n >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    if (ceil_div(m * (n / 128), 32) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+    mxq::SwigluFp8Args a{gate_bf16, up_bf16, q_e4m3, scales, m, n, ld_gate, ld_up, ldq, scale_stride_row,
+                         scale_stride_group};
+    return mxq::launch_swiglu_quant_fp8(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
 mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
                                   const uint16_t* nope, int64_t ld_nope, int64_t m,
                                   uint8_t* q_e4m3, float* scales, void* stream) {

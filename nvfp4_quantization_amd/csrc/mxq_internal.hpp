@@ -16,6 +16,16 @@ struct Fp8Args {
 };
 hipError_t launch_quant_fp8_1x128(const Fp8Args& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- SwiGLU -> FP8 1x128
+struct SwigluFp8Args {
+    const uint16_t* gate;
+    const uint16_t* up;
+    uint8_t* q;
+    float* scales;
+    int64_t m, n, ld_gate, ld_up, ldq, srow, sgroup;
+};
+hipError_t launch_swiglu_quant_fp8(const SwigluFp8Args& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- DSA rotate + FP8
 struct DsaArgs {
     const uint16_t* pe;

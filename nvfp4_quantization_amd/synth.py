@@ -160,6 +160,15 @@ def plain_fp8(m=256, k=1024, seed=1, device="cpu") -> Workload:
     return Workload("fp8_1x128", {"x": x}, {"m": m, "k": k})
 
 
+def swiglu_fp8(tokens=16384, n=4096, seed=6, device="cpu") -> Workload:
+    """Fused SwiGLU input of a W8A8 MoE expert: one BF16 [tokens][2n] buffer, gate in
+    the first half (N(0,1) * 2) and up in the second (N(0,1))."""
+    gate = normal(seed, 0, tokens * n, device).view(tokens, n) * 2.0
+    up = normal(seed, 1, tokens * n, device).view(tokens, n)
+    gu = torch.cat([to_bf16(gate), to_bf16(up)], dim=1).contiguous()
+    return Workload("swiglu_fp8", {"gate_up": gu}, {"tokens": tokens, "n": n})
+
+
 def dsa_rotate_fp8(tokens=4096, heads=64, d_pe=64, seed=2, outlier_frac=0.02,
                    outlier_scale=20.0, device="cpu") -> Workload:
     """DSA-indexer Q: [tokens*heads] rows of cat[qk_pe(d_pe), qk_nope(128-d_pe)],

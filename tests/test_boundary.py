@@ -203,3 +203,19 @@ def test_dsa_nvfp4_workspace_size(L):
     assert q(64 * 64) == 2048 + 256
     assert q(64 * 64 + 1) == 2048 + 512
     assert q(262144) == 2048 + 4 * 4096
+
+
+def swiglu(L, g=A, ldg=256, u=A, ldu=256, m=8, n=256, q=A, ldq=256, s=A, sr=2, sg=1):
+    return L.mxq_swiglu_quant_fp8(g, ldg, u, ldu, m, n, q, ldq, s, sr, sg, None)
+
+
+def test_swiglu_argument_errors(L):
+    assert swiglu(L, n=192, ldg=192, ldu=192, ldq=192) == MISALIGNED
+    assert swiglu(L, ldg=128) == INVALID
+    assert swiglu(L, ldu=264, u=A + 8) == MISALIGNED
+    assert swiglu(L, ldq=264) == MISALIGNED
+    assert swiglu(L, g=None) == INVALID
+    assert swiglu(L, s=A + 2) == MISALIGNED
+    assert swiglu(L, sr=-1) == INVALID
+    assert swiglu(L, m=0, g=None, u=None, q=None, s=None) == OK
+    assert swiglu(L, m=1 << 31) == UNSUPPORTED

@@ -43,6 +43,23 @@ def test_full_dsa(orc):
     assert_same("scales", host(s), np.concatenate([p[1] for p in parts]))
 
 
+def test_full_swiglu_fp8(orc):
+    dev = device()
+    announce("full size: SwiGLU -> FP8 1x128, 16384 tokens x 4096 (fused gate|up buffer)")
+    w = synth.swiglu_fp8(device=dev)
+    gu = w.tensors["gate_up"]
+    n = gu.shape[1] // 2
+    q, s = mxq.mxq_swiglu_quant_fp8(gu[:, :n], gu[:, n:])
+    torch.cuda.synchronize()
+    gb, ub = bits16(gu[:, :n].contiguous()), bits16(gu[:, n:].contiguous())
+    m = gb.shape[0]
+    step = (m + THREADS - 1) // THREADS
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(lambda r0: orc.swiglu_quant_fp8(gb[r0:r0 + step], ub[r0:r0 + step]), range(0, m, step)))
+    assert_same("scales", host(s), np.concatenate([p[1] for p in parts]))
+    assert_same("codes", host(q), np.concatenate([p[0] for p in parts]))
+
+
 def test_full_dsa_nvfp4(orc):
     dev = device()
     announce("full size: DSA rotate+NVFP4 4096 tokens x 64 heads")

@@ -99,6 +99,75 @@ def test_fp8_1x128_empty():
     assert q.shape == (0, 256)
 
 
+# ============================================================== SwiGLU -> FP8 1x128
+def swiglu_inputs(m, n, seed, edges=False):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((m, n)).astype(np.float32) * 3
+    u = rng.standard_normal((m, n)).astype(np.float32) * np.exp2(rng.integers(-10, 10, (m, 1)))
+    gb = torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    ub = torch.from_numpy(u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    if edges and m >= 8:
+        gb[0, 5] = 0x7FC0                  # NaN gate
+        ub[1, 7] = 0xFFC1                  # NaN up
+        gb[2, :] = 0                       # SiLU(0) = 0: a zero row
+        gb[3, :] = 0x4200                  # gate 32: SiLU(g) = g exactly
+        gb[4, :] = 0xC2C0                  # gate -96: e^96 overflows, SiLU = -0
+        gb[5, :64] = rng.integers(1, 0x80, 64)        # subnormal gates
+        ub[6, :] = rng.integers(0x8001, 0x8080, n)    # subnormal ups
+        gb[7, :] = 0xC1A0                  # gate -20 (a tiny negative SiLU)
+    return gb, ub
+
+
+@pytest.mark.parametrize("m,n", [(1, 128), (33, 384), (256, 2048), (7, 4096)])
+def test_swiglu_fp8_random(orc, m, n):
+    dev = device()
+    announce(f"swiglu fp8 m={m} n={n}")
+    gb, ub = swiglu_inputs(m, n, 400 + m)
+    q, s = mxq.mxq_swiglu_quant_fp8(bf16_dev(gb, dev), bf16_dev(ub, dev))
+    torch.cuda.synchronize()
+    rq, rs = orc.swiglu_quant_fp8(gb, ub)
+    assert_same("scales", host(s), rs)
+    assert_same("codes", host(q), rq)
+
+
+def test_swiglu_fp8_fused_layout_and_edges(orc):
+    """gate / up as the two halves of one [m][2n] buffer, transposed scales, and NaN,
+    zero, overflowing-exponential and subnormal rows."""
+    dev = device()
+    announce("swiglu fp8 fused layout + edges")
+    m, n = 40, 256
+    gb, ub = swiglu_inputs(m, n, 77, edges=True)
+    gu = bf16_dev(np.concatenate([gb, ub], axis=1), dev)
+    q, s = mxq.mxq_swiglu_quant_fp8(gu[:, :n], gu[:, n:], scale_transposed=True)
+    torch.cuda.synchronize()
+    rq, rs = orc.swiglu_quant_fp8(gb, ub, scale_transposed=True)
+    assert_same("scales", host(s), rs)
+    assert_same("codes", host(q), rq)
+
+
+def test_swiglu_fp8_exp_sweep(orc):
+    """The kernel's SiLU on a dense sweep of gates (every BF16 value in [-104, 104] with
+    up = 1): h = SILU(g) exactly, so the codes and scales show the GPU's EXP and
+    division match the stated algorithm bit for bit wherever they decide a code."""
+    dev = device()
+    announce("swiglu fp8 exp sweep")
+    b = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    v = f32 = (b.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isfinite(f32) & (np.abs(v) <= 104.0)
+    gates = b[keep]
+    n = 128
+    m = (gates.size + n - 1) // n
+    gb = np.zeros(m * n, np.uint16)
+    gb[:gates.size] = gates
+    gb = gb.reshape(m, n)
+    ub = np.full((m, n), 0x3F80, np.uint16)
+    q, s = mxq.mxq_swiglu_quant_fp8(bf16_dev(gb, dev), bf16_dev(ub, dev))
+    torch.cuda.synchronize()
+    rq, rs = orc.swiglu_quant_fp8(gb, ub)
+    assert_same("scales", host(s), rs)
+    assert_same("codes", host(q), rq)
+
+
 # ============================================================== DSA rotate + FP8
 @pytest.mark.parametrize("tokens,heads,d_pe", [(64, 8, 64), (7, 9, 64), (32, 4, 0), (32, 4, 128), (16, 5, 8)])
 def test_dsa_random(orc, tokens, heads, d_pe):
