@@ -54,6 +54,16 @@ def lib():
         L.oracle_quant_fp8_1x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64]
         L.oracle_hadamard_quant_fp8.restype = None
         L.oracle_hadamard_quant_fp8.argtypes = [_p, _i64, ctypes.c_int32, _p, _i64, _i64, _p, _p]
+        L.oracle_pow2_ceil.restype = ctypes.c_float
+        L.oracle_pow2_ceil.argtypes = [ctypes.c_float]
+        L.oracle_fp8_block.restype = ctypes.c_float
+        L.oracle_fp8_block.argtypes = [_p, ctypes.c_int, ctypes.c_uint32, _p]
+        L.oracle_quant_fp8_blockwise.restype = None
+        L.oracle_quant_fp8_blockwise.argtypes = [_p, _i64, _i64, _i64, ctypes.c_uint32,
+                                                 _p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64]
+        L.oracle_hadamard_quant_fp8_ex.restype = None
+        L.oracle_hadamard_quant_fp8_ex.argtypes = [_p, _i64, ctypes.c_int32, _p, _i64, _i64, ctypes.c_uint32,
+                                                   _i64, _p, _p, _i64, _i64]
         L.oracle_exp.restype = ctypes.c_float
         L.oracle_exp.argtypes = [ctypes.c_float]
         L.oracle_silu.restype = ctypes.c_float
@@ -194,6 +204,43 @@ def fp8_group(x):
     codes = np.empty(128, np.uint8)
     s = lib().oracle_fp8_group(_ptr(x), _ptr(codes))
     return np.float32(s), codes
+
+
+FP8_UE8M0 = 1
+
+
+def quant_fp8_blockwise(x_bf16, options=0, rowwise=True, columnwise=True):
+    """x: [m][k] uint16, k % 128 == 0.  Returns (row_codes [m][k], row_scales [m][k/128],
+    col_codes [k][m] (row c = column c of x), col_scales [k][ceil(m/128)]), with None
+    for an output not asked for."""
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    nb = (m + 127) // 128
+    rq = np.empty((m, k), np.uint8) if rowwise else None
+    rs = np.empty((m, k // 128), np.float32) if rowwise else None
+    cq = np.empty((k, m), np.uint8) if columnwise else None
+    cs = np.empty((k, nb), np.float32) if columnwise else None
+    lib().oracle_quant_fp8_blockwise(_ptr(x), m, k, k, options, _ptr(rq), k, _ptr(rs), k // 128, 1,
+                                     _ptr(cq), m, _ptr(cs), nb, 1)
+    return rq, rs, cq, cs
+
+
+def hadamard_quant_fp8_ex(pe, nope, options=0, heads=1, token_stride=None, head_stride=None, scale_size=None):
+    """The DSA rotate + FP8 with options and scale index token*token_stride +
+    head*head_stride (defaults: [tokens][heads]).  Returns (codes [m][128], scales
+    (flat array of scale_size floats, NaN where nothing is written))."""
+    pe = _c(pe, np.uint16)
+    nope = _c(nope, np.uint16)
+    m, d_pe = pe.shape
+    tokens = m // heads
+    ts = heads if token_stride is None else token_stride
+    hs = 1 if head_stride is None else head_stride
+    size = m if scale_size is None else scale_size
+    q = np.empty((m, 128), np.uint8)
+    s = np.full(size, np.nan, np.float32)
+    lib().oracle_hadamard_quant_fp8_ex(_ptr(pe), max(d_pe, 1), d_pe, _ptr(nope), max(128 - d_pe, 1), m, options,
+                                       heads, _ptr(q), _ptr(s), ts, hs)
+    return q, s
 
 
 def exp(x):

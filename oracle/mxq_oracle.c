@@ -563,3 +563,69 @@ void oracle_silu_n(const float* x, int64_t count, float* out)
 {
     for (int64_t i = 0; i < count; ++i) out[i] = oracle_silu(x[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP8 block variants: UE8M0 scales, 128x1 column blocks, scale layouts      */
+/* ------------------------------------------------------------------------ */
+float oracle_pow2_ceil(float s)
+{
+    /* the smallest power of two >= s, for a positive normal s: the exponent of s,
+     * plus one unless s is already a power of two */
+    int e;
+    float f = frexpf(s, &e);                  /* s = f * 2^e, f in [0.5, 1) */
+    return (f == 0.5f) ? s : ldexpf(1.0f, e);
+}
+
+float oracle_fp8_block(const float* x, int n, uint32_t options, uint8_t* codes)
+{
+    float a = oracle_amax(x, n);
+    float floor_ = F_1E_10();
+    float s = ((a > floor_) ? a : floor_) * F_1_OVER_448();
+    if (options & ORACLE_FP8_UE8M0) s = oracle_pow2_ceil(s);
+    for (int i = 0; i < n; ++i) codes[i] = oracle_e4m3_encode(x[i] / s);
+    return s;
+}
+
+void oracle_quant_fp8_blockwise(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, uint32_t options,
+                                uint8_t* row_codes, int64_t row_ld, float* row_scales,
+                                int64_t row_stride_r, int64_t row_stride_g,
+                                uint8_t* col_codes, int64_t col_ld, float* col_scales,
+                                int64_t col_stride_c, int64_t col_stride_b)
+{
+    float v[128];
+    uint8_t c[128];
+    if (row_codes) {
+        for (int64_t r = 0; r < m; ++r)
+            for (int64_t g = 0; g < k / 128; ++g) {
+                for (int i = 0; i < 128; ++i) v[i] = oracle_bf16_to_f32(x[r * ldx + g * 128 + i]);
+                row_scales[r * row_stride_r + g * row_stride_g] =
+                    oracle_fp8_block(v, 128, options, row_codes + r * row_ld + g * 128);
+            }
+    }
+    if (col_codes) {
+        /* column c, row block b: rows 128b .. min(128b + 128, m) - 1 of column c;
+         * the codes go to row c of the transposed output */
+        for (int64_t cc = 0; cc < k; ++cc)
+            for (int64_t b = 0; 128 * b < m; ++b) {
+                int n = (int)((m - 128 * b) < 128 ? (m - 128 * b) : 128);
+                for (int i = 0; i < n; ++i) v[i] = oracle_bf16_to_f32(x[(128 * b + i) * ldx + cc]);
+                col_scales[cc * col_stride_c + b * col_stride_b] = oracle_fp8_block(v, n, options, c);
+                for (int i = 0; i < n; ++i) col_codes[cc * col_ld + 128 * b + i] = c[i];
+            }
+    }
+}
+
+void oracle_hadamard_quant_fp8_ex(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                  const uint16_t* nope, int64_t ld_nope, int64_t m, uint32_t options,
+                                  int64_t heads, uint8_t* q, float* scales,
+                                  int64_t scale_stride_token, int64_t scale_stride_head)
+{
+    float v[128], y[128];
+    for (int64_t r = 0; r < m; ++r) {
+        for (int i = 0; i < d_pe; ++i)   v[i] = oracle_bf16_to_f32(pe[r * ld_pe + i]);
+        for (int i = d_pe; i < 128; ++i) v[i] = oracle_bf16_to_f32(nope[r * ld_nope + (i - d_pe)]);
+        oracle_wht(v, 128, 0u, F_C128(), y);
+        int64_t token = r / heads, head = r % heads;
+        scales[token * scale_stride_token + head * scale_stride_head] = oracle_fp8_block(y, 128, options, q + r * 128);
+    }
+}

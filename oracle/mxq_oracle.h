@@ -91,6 +91,30 @@ void oracle_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d_pe
                                  const float* amax_in, uint8_t* codes, uint8_t* scales,
                                  float* global_scale, float* amax_out);
 
+/* ---- FP8 block variants ----------------------------------------------------------
+ * ORACLE_FP8_UE8M0: the scale s = fl(max(a, F(1e-10)) * F(1/448)) is rounded up to
+ * the nearest power of two (a UE8M0-representable scale; amax / s then stays <= 448). */
+#define ORACLE_FP8_UE8M0 1u
+float oracle_pow2_ceil(float s);                   /* smallest power of two >= s (s > 0 normal) */
+/* n <= 128 values as one block: s as above (UE8M0 with the option), codes E4M3(fl(x/s)). */
+float oracle_fp8_block(const float* x, int n, uint32_t options, uint8_t* codes);
+/* Row-wise 1x128 (row_codes [m][row_ld], scale of (r, g) at r*row_stride_r + g*row_stride_g)
+ * and column-wise 128x1 blocks on the transpose (col_codes [k][col_ld]: row c holds column c
+ * of x; column c's block b covers rows 128b .. min(128b+128, m)-1; its scale at
+ * c*col_stride_c + b*col_stride_b).  Either output may be NULL.  k % 128 == 0. */
+void oracle_quant_fp8_blockwise(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, uint32_t options,
+                                uint8_t* row_codes, int64_t row_ld, float* row_scales,
+                                int64_t row_stride_r, int64_t row_stride_g,
+                                uint8_t* col_codes, int64_t col_ld, float* col_scales,
+                                int64_t col_stride_c, int64_t col_stride_b);
+/* The DSA rotate + FP8 with options and a (token, head) scale layout: row r is token
+ * r / heads, head r % heads, and its scale goes to token*scale_stride_token +
+ * head*scale_stride_head. */
+void oracle_hadamard_quant_fp8_ex(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                  const uint16_t* nope, int64_t ld_nope, int64_t m, uint32_t options,
+                                  int64_t heads, uint8_t* q, float* scales,
+                                  int64_t scale_stride_token, int64_t scale_stride_head);
+
 /* ---- SwiGLU -> FP8 1x128 ---------------------------------------------------------
  * EXP(x), e^x in binary32 by these steps (one rounding per operation):
  *   NaN -> NaN; x clamped to [-128, 128];
