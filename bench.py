@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="grouped_nvfp4_rht",
                     choices=["grouped_nvfp4_rht", "grouped_nvfp4_rht_sr", "large_moe_nvfp4_fp8",
-                             "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8", "fp8_1x128"])
+                             "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8", "fp8_blockwise", "fp8_1x128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="steady-state steps only, then one 256 MiB device copy (the counter calibration "
@@ -60,7 +60,7 @@ def main():
 
     # ---------------------------------------------------------------- workload
     wl = args.workload
-    grouped = wl not in ("fp8_1x128", "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8")
+    grouped = wl not in ("fp8_1x128", "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8", "fp8_blockwise")
     if wl == "fp8_1x128":
         w = synth.plain_fp8(device=dev)
         x = w.tensors["x"]
@@ -89,6 +89,17 @@ def main():
         in_bytes = m * 128 * 2
         alg_bytes = in_bytes + m * 128 + m * 4
         desc = f"dsa cat+WHT128+fp8_1x128, {m} rows (4096 tokens x 64 heads) bf16"
+    elif wl == "fp8_blockwise":
+        x = synth.grouped_nvfp4(device=dev).tensors["x"]
+        m, k = x.shape
+
+        def make_call(x=x):
+            xi = x.clone()
+            return lambda: mxq.mxq_quant_fp8_blockwise(xi, mxq.MXQ_FP8_UE8M0, rowwise=True, columnwise=True)
+        call = make_call()
+        in_bytes = m * k * 2
+        alg_bytes = in_bytes + 2 * (m * k + m * (k // 128) * 4)
+        desc = f"fp8 row-wise 1x128 + column-wise 128x1 (transposed), UE8M0 scales, {m}x{k} bf16"
     elif wl == "swiglu_fp8":
         w = synth.swiglu_fp8(device=dev)
         gu = w.tensors["gate_up"]
@@ -176,6 +187,17 @@ def main():
     kern = None
     if grouped:
         kern = kernel_times(mxq, torch, calls, n_sets, K, stream, ("k_nvfp4_amax", "k_nvfp4_quant"))
+    elif wl == "fp8_blockwise":
+        x = synth.grouped_nvfp4(device=dev).tensors["x"]
+        m, k = x.shape
+
+        def make_call(x=x):
+            xi = x.clone()
+            return lambda: mxq.mxq_quant_fp8_blockwise(xi, mxq.MXQ_FP8_UE8M0, rowwise=True, columnwise=True)
+        call = make_call()
+        in_bytes = m * k * 2
+        alg_bytes = in_bytes + 2 * (m * k + m * (k // 128) * 4)
+        desc = f"fp8 row-wise 1x128 + column-wise 128x1 (transposed), UE8M0 scales, {m}x{k} bf16"
     elif wl == "swiglu_fp8":
         w = synth.swiglu_fp8(device=dev)
         gu = w.tensors["gate_up"]

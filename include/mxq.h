@@ -2,8 +2,11 @@
  * mxq.h -- C ABI of the mxq block-quantization library for AMD Instinct MI355X
  * (gfx950).
  *
- * Five entry points quantize BF16 activations on the GPU:
+ * These entry points quantize BF16 activations on the GPU:
  *   mxq_quant_fp8_1x128        FP8 E4M3 with one FP32 scale per 1x128 group
+ *   mxq_quant_fp8_blockwise    the same row-wise and/or 128x1 column-wise on the
+ *                              transpose, optionally with UE8M0 (power-of-two) scales
+ *   mxq_hadamard_quant_fp8_ex  the DSA rotate + FP8 with UE8M0 and scale layouts
  *   mxq_swiglu_quant_fp8       FP32 SiLU(gate) * up -> FP8 1x128 (no BF16 round)
  *   mxq_hadamard_quant_fp8     cat[qk_pe, qk_nope] -> normalized 128-point
  *                              Walsh-Hadamard rotation -> FP8 1x128
@@ -97,6 +100,48 @@ mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int
                                uint8_t* q_e4m3, int64_t ldq,
                                float* scales, int64_t scale_stride_row, int64_t scale_stride_group,
                                void* stream);
+
+/* ---------------------------------------------------------------------------
+ * FP8 block variants (consumer-facing layouts of the same recipe).
+ * TensorRT-LLM PR #15158, review of the DSA scale normalization: a use_ue8m0 option
+ * of fp8_quantize_1x128_sf_transpose, and the 1-D scale tensor padded, reshaped and
+ * transposed for its consumer.  The recipe is mxq_quant_fp8_1x128's.
+ *
+ * MXQ_FP8_UE8M0: every scale s = fl(max(a, F(1e-10)) * F(1/448)) is rounded up to
+ * the nearest power of two (stored as that FP32 power of two: its UE8M0 byte is the
+ * FP32 exponent field, bits >> 23); the codes are E4M3(x / s), exact divisions, and
+ * |x| / s stays <= 448.
+ * ------------------------------------------------------------------------- */
+enum { MXQ_FP8_UE8M0 = 1u };
+
+typedef struct {
+    uint8_t* codes;             /* row-wise: [m][ld];  column-wise: [k][ld], row c = column c of x */
+    int64_t  ld;
+    float*   scales;            /* row-wise: (row r, group g) at r * scale_stride_a + g * scale_stride_b;
+                                   column-wise: (column c, row block b) at c * scale_stride_a + b * scale_stride_b */
+    int64_t  scale_stride_a;
+    int64_t  scale_stride_b;
+} mxq_fp8_block_out;
+
+/* Row-wise 1x128 groups and/or column-wise 128x1 blocks (rows 128b .. min(128b+128,
+ * m)-1 of column c, a ragged last block when m % 128 != 0; its codes go to row c of the
+ * transposed output), from one read of x.  rowwise / columnwise may be NULL (not both).
+ * Requirements: k % 128 == 0; ldx % 8 == 0; ld >= k (row-wise) or >= m (column-wise),
+ * a multiple of 16; x and codes 16-byte aligned, scales 4-byte aligned; options in
+ * {0, MXQ_FP8_UE8M0}.  m == 0 is a successful no-op. */
+mxq_status mxq_quant_fp8_blockwise(const uint16_t* x_bf16, int64_t m, int64_t k, int64_t ldx, uint32_t options,
+                                   const mxq_fp8_block_out* rowwise, const mxq_fp8_block_out* columnwise,
+                                   void* stream);
+
+/* mxq_hadamard_quant_fp8 with options and a (token, head) scale layout: row r is
+ * token r / heads, head r % heads (heads >= 1), and its scale goes to
+ * scales[token * scale_stride_token + head * scale_stride_head]: {heads, 1} is the
+ * plain [tokens][heads] order, {1, T} the transposed [heads][T] one with T >= tokens
+ * (rows T past the tokens are padding the call leaves untouched). */
+mxq_status mxq_hadamard_quant_fp8_ex(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                     const uint16_t* nope, int64_t ld_nope, int64_t m, uint32_t options,
+                                     int64_t heads, uint8_t* q_e4m3, float* scales,
+                                     int64_t scale_stride_token, int64_t scale_stride_head, void* stream);
 
 /* ---------------------------------------------------------------------------
  * SwiGLU -> FP8 1x128: the second dynamic quantizer of a W8A8 MoE, directly after

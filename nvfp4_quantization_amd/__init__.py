@@ -26,7 +26,9 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_MISALIGNED",
 EXPORTED = ("mxq_status_string", "mxq_version", "mxq_quant_fp8_1x128", "mxq_hadamard_quant_fp8",
             "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4",
             "mxq_group_rht_quant_nvfp4_with_amax", "mxq_set_launch_marks",
-            "mxq_hadamard_quant_nvfp4_workspace_size", "mxq_hadamard_quant_nvfp4", "mxq_swiglu_quant_fp8")
+            "mxq_hadamard_quant_nvfp4_workspace_size", "mxq_hadamard_quant_nvfp4", "mxq_swiglu_quant_fp8",
+            "mxq_quant_fp8_blockwise", "mxq_hadamard_quant_fp8_ex")
+MXQ_FP8_UE8M0 = 1
 
 
 class MxqError(RuntimeError):
@@ -41,6 +43,11 @@ class _NVFP4Out(ctypes.Structure):
 
 class _FP8Out(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _FP8BlockOut(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("ld", ctypes.c_int64), ("scales", ctypes.c_void_p),
+                ("scale_stride_a", ctypes.c_int64), ("scale_stride_b", ctypes.c_int64)]
 
 
 class _SR(ctypes.Structure):
@@ -79,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_rht_quant_nvfp4_with_amax.restype = ctypes.c_int
         L.mxq_group_rht_quant_nvfp4_with_amax.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
                                                           p, p, p, p, p, ctypes.c_size_t, p]
+        L.mxq_quant_fp8_blockwise.restype = ctypes.c_int
+        L.mxq_quant_fp8_blockwise.argtypes = [p, i64, i64, i64, ctypes.c_uint32, p, p, p]
+        L.mxq_hadamard_quant_fp8_ex.restype = ctypes.c_int
+        L.mxq_hadamard_quant_fp8_ex.argtypes = [p, i64, ctypes.c_int32, p, i64, i64, ctypes.c_uint32, i64, p, p,
+                                                i64, i64, p]
         L.mxq_swiglu_quant_fp8.restype = ctypes.c_int
         L.mxq_swiglu_quant_fp8.argtypes = [p, i64, p, i64, i64, i64, p, i64, p, i64, i64, p]
         L.mxq_hadamard_quant_nvfp4_workspace_size.restype = ctypes.c_size_t
@@ -191,6 +203,57 @@ def mxq_hadamard_quant_fp8(pe: Optional[torch.Tensor], nope: Optional[torch.Tens
     ld_nope = _row_stride(nope)
     _check(lib().mxq_hadamard_quant_fp8(_ptr(pe), ld_pe, d_pe, _ptr(nope), ld_nope, m, _ptr(q), _ptr(scales),
                                         _stream(stream)), "mxq_hadamard_quant_fp8")
+    return q, scales
+
+
+# ---------------------------------------------------------------------------- FP8 block variants
+def mxq_quant_fp8_blockwise(x: torch.Tensor, options: int = 0, rowwise: bool = True, columnwise: bool = False,
+                            stream=None):
+    """Row-wise 1x128 and/or column-wise 128x1 FP8 (codes of x^T) from one read of x
+    [m][k] BF16.  options: 0 or MXQ_FP8_UE8M0.  Returns (row_codes [m][k], row_scales
+    [m][k/128], col_codes [k][ld >= m], col_scales [k][ceil(m/128)]), None where not asked."""
+    m, k = x.shape
+    x = _bf16_bits(x)
+    dev = x.device
+    nb = (m + 127) // 128
+    ro = co = None
+    rq = rs = cq = cs = None
+    if rowwise:
+        rq = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        rs = torch.empty((m, k // 128), dtype=torch.float32, device=dev)
+        ro = _FP8BlockOut(_ptr(rq), k, _ptr(rs), k // 128, 1)
+    if columnwise:
+        ld = (m + 15) // 16 * 16
+        cq = torch.empty((k, ld), dtype=torch.uint8, device=dev)
+        cs = torch.empty((k, nb), dtype=torch.float32, device=dev)
+        co = _FP8BlockOut(_ptr(cq), ld, _ptr(cs), nb, 1)
+    _check(lib().mxq_quant_fp8_blockwise(_ptr(x), m, k, _row_stride(x), options,
+                                         ctypes.byref(ro) if ro is not None else None,
+                                         ctypes.byref(co) if co is not None else None, _stream(stream)),
+           "mxq_quant_fp8_blockwise")
+    return rq, rs, (cq[:, :m] if cq is not None else None), cs
+
+
+def mxq_hadamard_quant_fp8_ex(pe: Optional[torch.Tensor], nope: Optional[torch.Tensor], options: int = 0,
+                              heads: int = 1, scales: Optional[torch.Tensor] = None, scale_stride_token: int = None,
+                              scale_stride_head: int = None, q: Optional[torch.Tensor] = None, stream=None):
+    """mxq_hadamard_quant_fp8 with options (MXQ_FP8_UE8M0) and a (token, head) scale
+    layout: the scale of row r goes to scales[(r // heads) * scale_stride_token +
+    (r % heads) * scale_stride_head] (defaults: [tokens][heads]).  Returns (q, scales)."""
+    ref = pe if pe is not None else nope
+    m = ref.shape[0]
+    d_pe = pe.shape[1] if pe is not None else 0
+    pe = _bf16_bits(pe) if pe is not None else None
+    nope = _bf16_bits(nope) if nope is not None else None
+    if q is None:
+        q = torch.empty((m, 128), dtype=torch.uint8, device=ref.device)
+    st = heads if scale_stride_token is None else scale_stride_token
+    sh = 1 if scale_stride_head is None else scale_stride_head
+    if scales is None:
+        scales = torch.empty((m,), dtype=torch.float32, device=ref.device)
+    _check(lib().mxq_hadamard_quant_fp8_ex(_ptr(pe), _row_stride(pe), d_pe, _ptr(nope), _row_stride(nope), m,
+                                           options, heads, _ptr(q), _ptr(scales), st, sh, _stream(stream)),
+           "mxq_hadamard_quant_fp8_ex")
     return q, scales
 
 

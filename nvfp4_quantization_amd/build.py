@@ -26,7 +26,7 @@ OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT, "libmxq.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["mxq_fp8.hip", "mxq_swiglu_fp8.hip", "mxq_dsa_nvfp4.hip", "mxq_nvfp4.hip", "mxq_nvfp4_quant_rne.hip", "mxq_nvfp4_quant_sr.hip",
+HIP_SOURCES = ["mxq_fp8.hip", "mxq_fp8_block.hip", "mxq_swiglu_fp8.hip", "mxq_dsa_nvfp4.hip", "mxq_nvfp4.hip", "mxq_nvfp4_quant_rne.hip", "mxq_nvfp4_quant_sr.hip",
                "mxq_nvfp4_quant_rne_aout.hip", "mxq_nvfp4_quant_sr_aout.hip"]
 HOST_SOURCES = ["mxq_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Werror", "-I", "/opt/rocm/include",

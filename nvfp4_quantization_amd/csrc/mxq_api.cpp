@@ -106,8 +106,87 @@ mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_p
         return MXQ_ERR_MISALIGNED;
     if (m > kMaxRows) return MXQ_ERR_UNSUPPORTED;
     if (ceil_div(m, 64) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
-    mxq::DsaArgs a{pe, nope, q_e4m3, scales, ld_pe, ld_nope, m, d_pe};
+    mxq::DsaArgs a{pe, nope, q_e4m3, scales, ld_pe, ld_nope, m, d_pe, 1, 1, 0};
     return mxq::launch_hadamard_quant_fp8(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+mxq_status mxq_hadamard_quant_fp8_ex(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
+                                     const uint16_t* nope, int64_t ld_nope, int64_t m, uint32_t options,
+                                     int64_t heads, uint8_t* q_e4m3, float* scales,
+                                     int64_t scale_stride_token, int64_t scale_stride_head, void* stream) {
+    if (options & ~(uint32_t)MXQ_FP8_UE8M0) return MXQ_ERR_INVALID_ARGUMENT;
+    if (heads <= 0 || scale_stride_token < 0 || scale_stride_head < 0) return MXQ_ERR_INVALID_ARGUMENT;
+    if (m < 0 || d_pe < 0 || d_pe > 128) return MXQ_ERR_INVALID_ARGUMENT;
+    if (d_pe % 8 != 0) return MXQ_ERR_MISALIGNED;
+    if (d_pe > 0 && ld_pe < d_pe) return MXQ_ERR_INVALID_ARGUMENT;
+    if (d_pe < 128 && ld_nope < 128 - d_pe) return MXQ_ERR_INVALID_ARGUMENT;
+    if ((d_pe > 0 && ld_pe % 8 != 0) || (d_pe < 128 && ld_nope % 8 != 0)) return MXQ_ERR_MISALIGNED;
+    if (m == 0) return MXQ_OK;
+    if ((d_pe > 0 && !pe) || (d_pe < 128 && !nope) || !q_e4m3 || !scales) return MXQ_ERR_INVALID_ARGUMENT;
+    if ((d_pe > 0 && !aligned(pe, 16)) || (d_pe < 128 && !aligned(nope, 16)) || !aligned(q_e4m3, 16) ||
+        !aligned(scales, 4))
+        return MXQ_ERR_MISALIGNED;
+    if (m > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    if (ceil_div(m, 64) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+    mxq::DsaArgs a{pe, nope, q_e4m3, scales, ld_pe, ld_nope, m, d_pe, heads, scale_stride_token, scale_stride_head};
+    return mxq::launch_hadamard_quant_fp8(a, static_cast<hipStream_t>(stream), (options & MXQ_FP8_UE8M0) != 0) ==
+                   hipSuccess
+               ? MXQ_OK
+               : MXQ_ERR_HIP;
+}
+
+mxq_status mxq_quant_fp8_blockwise(const uint16_t* x_bf16, int64_t m, int64_t k, int64_t ldx, uint32_t options,
+                                   const mxq_fp8_block_out* rowwise, const mxq_fp8_block_out* columnwise,
+                                   void* stream) {
+    if (options & ~(uint32_t)MXQ_FP8_UE8M0) return MXQ_ERR_INVALID_ARGUMENT;
+    if (!rowwise && !columnwise) return MXQ_ERR_INVALID_ARGUMENT;
+    if (m < 0 || k <= 0 || ldx < k) return MXQ_ERR_INVALID_ARGUMENT;
+    if (k % 128 != 0 || ldx % 8 != 0) return MXQ_ERR_MISALIGNED;
+    if (rowwise) {
+        if (rowwise->ld < k || rowwise->scale_stride_a < 0 || rowwise->scale_stride_b < 0)
+            return MXQ_ERR_INVALID_ARGUMENT;
+        if (rowwise->ld % 16 != 0) return MXQ_ERR_MISALIGNED;
+    }
+    if (columnwise) {
+        if (columnwise->ld < m || columnwise->scale_stride_a < 0 || columnwise->scale_stride_b < 0)
+            return MXQ_ERR_INVALID_ARGUMENT;
+        if (columnwise->ld % 16 != 0) return MXQ_ERR_MISALIGNED;
+    }
+    if (m == 0) return MXQ_OK;
+    if (!x_bf16 || (rowwise && (!rowwise->codes || !rowwise->scales)) ||
+        (columnwise && (!columnwise->codes || !columnwise->scales)))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (!aligned(x_bf16, 16) || (rowwise && (!aligned(rowwise->codes, 16) || !aligned(rowwise->scales, 4))) ||
+        (columnwise && (!aligned(columnwise->codes, 16) || !aligned(columnwise->scales, 4))))
+        return MXQ_ERR_MISALIGNED;
+    if (m > kMaxRows || m * k >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    const bool ue8m0 = (options & MXQ_FP8_UE8M0) != 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!columnwise) {                                    // row-wise alone: the streaming kernel
+        if (ceil_div(m * (k / 128), 32) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+        mxq::Fp8Args a{x_bf16, rowwise->codes, rowwise->scales, m, k, ldx, rowwise->ld,
+                       rowwise->scale_stride_a, rowwise->scale_stride_b};
+        return mxq::launch_quant_fp8_1x128(a, st, ue8m0) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+    }
+    if (ceil_div(m, 128) * (k / 128) > 0xFFFFFFFFll) return MXQ_ERR_UNSUPPORTED;
+    mxq::Fp8BlockArgs a{};
+    a.x = x_bf16;
+    a.m = m;
+    a.k = k;
+    a.ldx = ldx;
+    if (rowwise) {
+        a.rq = rowwise->codes;
+        a.rld = rowwise->ld;
+        a.rs = rowwise->scales;
+        a.rsr = rowwise->scale_stride_a;
+        a.rsg = rowwise->scale_stride_b;
+    }
+    a.cq = columnwise->codes;
+    a.cld = columnwise->ld;
+    a.cs = columnwise->scales;
+    a.csc = columnwise->scale_stride_a;
+    a.csb = columnwise->scale_stride_b;
+    return mxq::launch_quant_fp8_blockwise(a, ue8m0, st) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
 size_t mxq_hadamard_quant_nvfp4_workspace_size(int64_t m) {

@@ -82,6 +82,12 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
     return __builtin_amdgcn_cvt_f32_fp8(code, 0);
 }
+// The smallest power of two >= s (s > 0 normal): a scale a UE8M0 byte can hold.
+__device__ __forceinline__ float pow2_ceil(float s) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, s);
+    return __builtin_bit_cast(float, (b & 0x7FFFFFu) ? (b & 0xFF800000u) + 0x00800000u : b);
+}
+
 // Four E4M3 codes packed into a dword, a in the lowest byte.
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
     uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);

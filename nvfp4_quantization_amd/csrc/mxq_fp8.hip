@@ -17,7 +17,9 @@ __device__ __forceinline__ uint32_t fix_nan_codes(uint32_t c) {
 }
 
 // One 128-element group is held by 8 consecutive lanes, 16 elements each
-// (two 16-byte loads); a 256-thread block covers 32 groups.
+// (two 16-byte loads); a 256-thread block covers 32 groups.  UE8M0: the scale is
+// rounded up to a power of two.
+template <bool UE8M0>
 __global__ __launch_bounds__(256) void k_quant_fp8_1x128(const Fp8Args a) {
     const int64_t gpr = a.k >> 7;
     const int64_t total = a.m * gpr;
@@ -50,7 +52,8 @@ __global__ __launch_bounds__(256) void k_quant_fp8_1x128(const Fp8Args a) {
         m = other > m ? other : m;
     }
     const float amax = bf16_mag(m);
-    const float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
+    float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
+    if (UE8M0) s = pow2_ceil(s);
     const float y = 1.0f / s;
     uint32_t c[4];
 #pragma unroll
@@ -65,16 +68,21 @@ __global__ __launch_bounds__(256) void k_quant_fp8_1x128(const Fp8Args a) {
     }
 }
 
-hipError_t launch_quant_fp8_1x128(const Fp8Args& a, hipStream_t stream) {
+hipError_t launch_quant_fp8_1x128(const Fp8Args& a, hipStream_t stream, bool ue8m0) {
     const int64_t groups = a.m * (a.k / 128);
     const int64_t blocks = (groups + 31) / 32;
-    hipLaunchKernelGGL(k_quant_fp8_1x128, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (ue8m0)
+        hipLaunchKernelGGL(k_quant_fp8_1x128<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_quant_fp8_1x128<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 // One 128-element row v = cat(pe, nope) is held by 4 lanes, 32 consecutive
 // elements each.  Butterfly stages h = 1..16 run inside a lane; h = 32 and 64
-// pair lanes (q ^ 1) and (q ^ 2).  A 256-thread block covers 64 rows.
+// pair lanes (q ^ 1) and (q ^ 2).  A 256-thread block covers 64 rows.  UE8M0:
+// the scale is rounded up to a power of two.
+template <bool UE8M0>
 __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
     const int quarter = threadIdx.x & 3;
     const int64_t r = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
@@ -103,7 +111,8 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
         m = other > m ? other : m;
     }
     const float amax = bf16_mag(m);
-    const float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
+    float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
+    if (UE8M0) s = pow2_ceil(s);
     const float y = 1.0f / s;
     uint32_t cd[8];
 #pragma unroll
@@ -116,13 +125,19 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
         uint4* dst = reinterpret_cast<uint4*>(a.q + r * 128 + quarter * 32);
         dst[0] = make_uint4(cd[0], cd[1], cd[2], cd[3]);
         dst[1] = make_uint4(cd[4], cd[5], cd[6], cd[7]);
-        if (quarter == 0) a.scales[r] = s;
+        if (quarter == 0) {
+            const int64_t token = r / a.heads, head = r - token * a.heads;
+            a.scales[token * a.stride_token + head * a.stride_head] = s;
+        }
     }
 }
 
-hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream) {
+hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream, bool ue8m0) {
     const int64_t blocks = (a.m + 63) / 64;
-    hipLaunchKernelGGL(k_hadamard_quant_fp8, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (ue8m0)
+        hipLaunchKernelGGL(k_hadamard_quant_fp8<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_hadamard_quant_fp8<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

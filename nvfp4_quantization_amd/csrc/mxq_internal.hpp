@@ -14,7 +14,24 @@ struct Fp8Args {
     float* scales;
     int64_t m, k, ldx, ldq, srow, sgroup;
 };
-hipError_t launch_quant_fp8_1x128(const Fp8Args& a, hipStream_t stream);
+hipError_t launch_quant_fp8_1x128(const Fp8Args& a, hipStream_t stream, bool ue8m0 = false);
+
+// ---------------------------------------------------------------- FP8 block variants
+// Row-wise 1x128 and/or column-wise 128x1 (codes of x^T) from one read of x, 128 x 128
+// tiles staged in LDS; ue8m0: scales rounded up to powers of two.
+struct Fp8BlockArgs {
+    const uint16_t* x;
+    int64_t m, k, ldx;
+    uint8_t* rq;                      // row-wise codes [m][rld] (null: not wanted)
+    int64_t rld;
+    float* rs;                        // scale of (row r, group g) at r * rsr + g * rsg
+    int64_t rsr, rsg;
+    uint8_t* cq;                      // column-wise codes [k][cld] (null: not wanted)
+    int64_t cld;
+    float* cs;                        // scale of (column c, row block b) at c * csc + b * csb
+    int64_t csc, csb;
+};
+hipError_t launch_quant_fp8_blockwise(const Fp8BlockArgs& a, bool ue8m0, hipStream_t stream);
 
 // ---------------------------------------------------------------- SwiGLU -> FP8 1x128
 struct SwigluFp8Args {
@@ -31,11 +48,12 @@ struct DsaArgs {
     const uint16_t* pe;
     const uint16_t* nope;
     uint8_t* q;
-    float* scales;
+    float* scales;                    // scale of row r = (token r / heads, head r % heads)
     int64_t ld_pe, ld_nope, m;
     int32_t d_pe;
+    int64_t heads, stride_token, stride_head;
 };
-hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream);
+hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream, bool ue8m0 = false);
 
 // ---------------------------------------------------------------- DSA rotate + NVFP4
 // With a measured tensor amax three kernels: the first rotates 64 rows per

@@ -219,3 +219,37 @@ def test_swiglu_argument_errors(L):
     assert swiglu(L, sr=-1) == INVALID
     assert swiglu(L, m=0, g=None, u=None, q=None, s=None) == OK
     assert swiglu(L, m=1 << 31) == UNSUPPORTED
+
+
+def blockwise(L, x=A, m=256, k=256, ldx=256, options=0, row=(A, 256, A, 2, 1), col=(A, 256, A, 2, 1)):
+    r = mxq._FP8BlockOut(*row) if row is not None else None
+    c = mxq._FP8BlockOut(*col) if col is not None else None
+    return L.mxq_quant_fp8_blockwise(x, m, k, ldx, options, ctypes.byref(r) if r is not None else None,
+                                     ctypes.byref(c) if c is not None else None, None)
+
+
+def test_fp8_blockwise_argument_errors(L):
+    assert blockwise(L, row=None, col=None) == INVALID
+    assert blockwise(L, options=2) == INVALID
+    assert blockwise(L, k=192, ldx=192) == MISALIGNED
+    assert blockwise(L, row=(A, 264, A, 2, 1)) == MISALIGNED
+    assert blockwise(L, col=(A, 128, A, 2, 1)) == INVALID           # ld < m
+    assert blockwise(L, col=(A + 8, 256, A, 2, 1)) == MISALIGNED
+    assert blockwise(L, col=(A, 256, A + 1, 2, 1)) == MISALIGNED
+    assert blockwise(L, row=(None, 256, A, 2, 1)) == INVALID
+    assert blockwise(L, m=0, x=None) == OK
+    assert blockwise(L, m=1 << 31, col=None) == UNSUPPORTED
+
+
+def test_dsa_fp8_ex_argument_errors(L):
+    def ex(**kw):
+        a = dict(pe=A, ld_pe=64, d_pe=64, nope=A, ld_nope=64, m=8, options=0, heads=2, q=A, s=A, st=2, sh=1)
+        a.update(kw)
+        return L.mxq_hadamard_quant_fp8_ex(a["pe"], a["ld_pe"], a["d_pe"], a["nope"], a["ld_nope"], a["m"],
+                                           a["options"], a["heads"], a["q"], a["s"], a["st"], a["sh"], None)
+    assert ex(options=4) == INVALID
+    assert ex(heads=0) == INVALID
+    assert ex(st=-1) == INVALID
+    assert ex(d_pe=60, ld_pe=60, ld_nope=68) == MISALIGNED
+    assert ex(s=A + 2) == MISALIGNED
+    assert ex(m=0) == OK

@@ -43,6 +43,19 @@ def test_full_dsa(orc):
     assert_same("scales", host(s), np.concatenate([p[1] for p in parts]))
 
 
+def test_full_fp8_blockwise(orc):
+    dev = device()
+    announce("full size: FP8 row-wise 1x128 + column-wise 128x1, UE8M0, 16384x4096")
+    x = synth.grouped_nvfp4(device=dev).tensors["x"]
+    rq, rs, cq, cs = mxq.mxq_quant_fp8_blockwise(x, mxq.MXQ_FP8_UE8M0, rowwise=True, columnwise=True)
+    torch.cuda.synchronize()
+    wq, ws, wcq, wcs = orc.quant_fp8_blockwise(bits16(x), orc.FP8_UE8M0)
+    assert_same("row_scales", host(rs), ws)
+    assert_same("row_codes", host(rq), wq)
+    assert_same("col_scales", host(cs), wcs)
+    assert_same("col_codes", host(cq.contiguous()), wcq)
+
+
 def test_full_swiglu_fp8(orc):
     dev = device()
     announce("full size: SwiGLU -> FP8 1x128, 16384 tokens x 4096 (fused gate|up buffer)")

@@ -99,6 +99,71 @@ def test_fp8_1x128_empty():
     assert q.shape == (0, 256)
 
 
+# ============================================================== FP8 block variants
+@pytest.mark.parametrize("m,k", [(256, 256), (300, 384), (1, 128), (129, 128), (1000, 512)])
+@pytest.mark.parametrize("options", [0, 1])
+@pytest.mark.parametrize("dirs", ["row+col", "col", "row"])
+def test_fp8_blockwise(orc, m, k, options, dirs):
+    dev = device()
+    announce(f"fp8 blockwise m={m} k={k} options={options} {dirs}")
+    rng = np.random.default_rng(m + k + options)
+    x = (rng.standard_normal((m, k)).astype(np.float32) * np.exp2(rng.integers(-10, 10, (m, 1)))
+         * np.exp2(rng.integers(-6, 6, (1, k))))
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    row, col = "row" in dirs, "col" in dirs
+    rq, rs, cq, cs = mxq.mxq_quant_fp8_blockwise(bf16_dev(xb, dev), options, rowwise=row, columnwise=col)
+    torch.cuda.synchronize()
+    wq, ws, wcq, wcs = orc.quant_fp8_blockwise(xb, options, rowwise=row, columnwise=col)
+    if row:
+        assert_same("row_scales", host(rs), ws)
+        assert_same("row_codes", host(rq), wq)
+    if col:
+        assert_same("col_scales", host(cs), wcs)
+        assert_same("col_codes", host(cq.contiguous()), wcq)
+
+
+def test_fp8_blockwise_edges(orc):
+    """NaN (quiet, signalling, negative), zero and -0 blocks, subnormals and exact ties
+    in both directions, with a ragged last row block."""
+    dev = device()
+    announce("fp8 blockwise edges")
+    b = edge_matrix(200, 256, 31)
+    b[150:, 7] = 0x7FC0                      # a NaN in column 7 of the ragged block
+    for options in (0, 1):
+        rq, rs, cq, cs = mxq.mxq_quant_fp8_blockwise(bf16_dev(b, dev), options, rowwise=True, columnwise=True)
+        torch.cuda.synchronize()
+        wq, ws, wcq, wcs = orc.quant_fp8_blockwise(b, options)
+        assert_same("row_scales", host(rs), ws)
+        assert_same("row_codes", host(rq), wq)
+        assert_same("col_scales", host(cs), wcs)
+        assert_same("col_codes", host(cq.contiguous()), wcq)
+
+
+@pytest.mark.parametrize("options", [0, 1])
+def test_dsa_fp8_ex_layouts(orc, options):
+    """The (token, head) scale layouts: [tokens][heads] and the transposed [heads][T]
+    with T padded past the tokens (the padding keeps its sentinel), with UE8M0 or not."""
+    dev = device()
+    announce(f"dsa fp8 ex layouts options={options}")
+    tokens, heads, pad = 37, 8, 64
+    w = synth.dsa_rotate_fp8(tokens=tokens, heads=heads, seed=500 + options)
+    pe, nope = w.tensors["pe"].to(dev), w.tensors["nope"].to(dev)
+    pn, nn = bits16(w.tensors["pe"]), bits16(w.tensors["nope"])
+    q, s = mxq.mxq_hadamard_quant_fp8_ex(pe, nope, options, heads)
+    torch.cuda.synchronize()
+    wq, wsc = orc.hadamard_quant_fp8_ex(pn, nn, options, heads)
+    assert_same("codes", host(q), wq)
+    assert_same("scales", host(s), wsc)
+    st = torch.full((heads * pad,), float("nan"), dtype=torch.float32, device=dev)
+    q2, s2 = mxq.mxq_hadamard_quant_fp8_ex(pe, nope, options, heads, scales=st, scale_stride_token=1,
+                                           scale_stride_head=pad)
+    torch.cuda.synchronize()
+    wq2, ws2 = orc.hadamard_quant_fp8_ex(pn, nn, options, heads, token_stride=1, head_stride=pad,
+                                         scale_size=heads * pad)
+    assert_same("codes", host(q2), wq2)
+    assert_same("scales_transposed", host(s2), ws2)
+
+
 # ============================================================== SwiGLU -> FP8 1x128
 def swiglu_inputs(m, n, seed, edges=False):
     rng = np.random.default_rng(seed)
