@@ -29,6 +29,13 @@ __device__ __forceinline__ uint32_t nan_to_7f(uint32_t c) {
     return c ^ (ff * 0x80u);
 }
 
+// fl(x / s): a product when s is a power of two (its reciprocal is exact), else the
+// correctly rounded quotient from the reciprocal.
+template <bool UE8M0>
+__device__ __forceinline__ float quotient(float x, float s, float y) {
+    return UE8M0 ? x * y : div_rn(x, s, y);
+}
+
 template <bool UE8M0>
 __device__ __forceinline__ float block_scale(float amax) {
     const float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
@@ -82,8 +89,8 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const uint32_t w0 = src[2 * j], w1 = src[2 * j + 1];
-            c[j] = e4m3_pack4(div_rn(lo_bf16(w0), s, y), div_rn(hi_bf16(w0), s, y), div_rn(lo_bf16(w1), s, y),
-                              div_rn(hi_bf16(w1), s, y));
+            c[j] = e4m3_pack4(quotient<UE8M0>(lo_bf16(w0), s, y), quotient<UE8M0>(hi_bf16(w0), s, y),
+                              quotient<UE8M0>(lo_bf16(w1), s, y), quotient<UE8M0>(hi_bf16(w1), s, y));
             if (nan) c[j] = nan_to_7f(c[j]);              // only NaN inputs give 0xFF
         }
         if (row0 + r < a.m) {
@@ -118,7 +125,8 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = lo_bf16(col[(half * 64 + 4 * j + e) * (2 * kRowDwords)]);
-            code[j] = e4m3_pack4(div_rn(v[0], s, y), div_rn(v[1], s, y), div_rn(v[2], s, y), div_rn(v[3], s, y));
+            code[j] = e4m3_pack4(quotient<UE8M0>(v[0], s, y), quotient<UE8M0>(v[1], s, y),
+                                 quotient<UE8M0>(v[2], s, y), quotient<UE8M0>(v[3], s, y));
             if (nan) code[j] = nan_to_7f(code[j]);
         }
         const int64_t r_first = row0 + half * 64;
