@@ -366,7 +366,8 @@ __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, fl
 // maxima, where a NaN shows.
 template <bool SR, bool FAST>
 __device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2], int s, int64_t row0, int64_t c0,
-                                          int64_t r_local0, float g_r, float yg_r, const float4* tab_r, bool nan) {
+                                          int64_t r_local0, float g_r, float yg_r, const float4* tab_r, bool nan,
+                                          bool div_mode) {
     const int64_t k = G.k;
     const u32x4 no_rnd = {0, 0, 0, 0};
     auto put = [&](int t, const BlockOut& o) {
@@ -389,22 +390,24 @@ __device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2]
             row_nan |= o.scale == 0x7Fu;
             __builtin_amdgcn_sched_barrier(0);
         }
-    } else {
-        uint32_t redo = 0;
+    } else if (div_mode) {
+        // the section's row table has a scale code without a multiplier: exact division
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const BlockOut o = row_block<Enc::Mul, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m);
+            const BlockOut o = row_block<Enc::Div, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m);
             put(t, o);
-            redo |= (uint32_t)o.unsafe << t;
             amax = __builtin_fmaxf(amax, o.amax);
             row_nan |= o.scale == 0x7Fu;
             if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
         }
-        if (__ballot(redo != 0) != 0) {
-            launder(p);
+    } else {
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
-                if ((redo >> t) & 1u) put(t, row_block<Enc::Div, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m));
+        for (int t = 0; t < 16; ++t) {
+            const BlockOut o = row_block<Enc::Mul, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m);
+            put(t, o);
+            amax = __builtin_fmaxf(amax, o.amax);
+            row_nan |= o.scale == 0x7Fu;
+            if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
         }
     }
     const bool redo_nan = FAST ? nan : row_nan;
@@ -452,14 +455,24 @@ __device__ __forceinline__ float4 table_entry(int code, float g, bool quarter) {
     return make_float4(d, y, ym, 0.0f);
 }
 
-// Scale tables of section s (row-wise, then column-wise).
+// Scale tables of section s (row-wise, then column-wise), built by one wave.  Entry
+// 0's fourth value flags a direction with a scale code that has no multiplier (its
+// exact ties need opposite roundings): that direction's pass then divides exactly.
 template <bool ROW, bool COL>
 __device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g_r, float g_c) {
+    bool none[2] = {false, false};
 #pragma unroll
     for (int e = threadIdx.x; e < 256; e += 64) {
         const int dir = e >> 7, code = e & 127;
         if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
-        G.tables[(s * 2 + dir) * 128 + code] = table_entry(code, dir ? g_c : g_r, dir == 1);
+        const float4 entry = table_entry(code, dir ? g_c : g_r, dir == 1);
+        none[dir] |= entry.z < 0.0f;
+        G.tables[(s * 2 + dir) * 128 + code] = entry;
+    }
+    const bool flag_r = __ballot(none[0]) != 0, flag_c = __ballot(none[1]) != 0;
+    if (threadIdx.x == 0) {
+        if (ROW) G.tables[(s * 2) * 128].w = flag_r ? 1.0f : 0.0f;
+        if (COL) G.tables[(s * 2 + 1) * 128].w = flag_c ? 1.0f : 0.0f;
     }
 }
 
@@ -620,24 +633,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
                 if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        } else if (tab_c[0].w != 0.0f) {
+            // the section's column table has a scale code without a multiplier:
+            // exact division for the whole pass
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const BlockOut o = column_block<Enc::Div>(p, j, mask, g_c, yg_c, tab_c, no_rnd);
+                put(j, o);
+                lane_nan |= o.scale == 0x7Fu;
+                if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
+                if (j & 1) __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
-            // No branch in this loop, so the scheduler can overlap neighbouring
-            // columns; blocks whose scale code needs the exact division are redone.
-            uint32_t redo = 0;
+            // No branch in this loop, so the scheduler can overlap neighbouring columns.
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const BlockOut o = column_block<Enc::Mul>(p, j, mask, g_c, yg_c, tab_c, no_rnd);
                 put(j, o);
-                redo |= (uint32_t)o.unsafe << j;
                 lane_nan |= o.scale == 0x7Fu;
                 if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
                 if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two columns at a time: bounds registers
-            }
-            if (__ballot(redo != 0) != 0) {
-                launder(p);
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if ((redo >> j) & 1u) put(j, column_block<Enc::Div>(p, j, mask, g_c, yg_c, tab_c, no_rnd));
             }
         }
         // the LDS region is this wave's own: order its writes before the reads below
@@ -671,7 +686,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     if (ROW) {
         const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
         const float4* tab_r = tab[0];
-        const float ra = row_pass<SR, COL>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan);
+        const float ra = row_pass<SR, COL>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan,
+                                           tab_r[0].w != 0.0f);
         if (AOUT && G.amax_out_row) {
             // supplied maxima: measure this call's for the caller's next step
             const float w = wave_max_f32(ra);
