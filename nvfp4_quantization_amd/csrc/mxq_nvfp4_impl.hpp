@@ -28,10 +28,12 @@
 // lies within about 2^-21 (relative) of one of the seven E2M1 rounding boundaries
 // 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; BF16 values are 2^-8 apart, so only the two
 // BF16 neighbours of each boundary times d can, and those fourteen are checked
-// against the exact division for ym = y and its nearest neighbours.  The codes of
-// a block come from one multiply per element when its scale code has a
-// multiplier, else (and always with stochastic rounding, which needs the exact
-// quotient) from the exact division.  Column values enter unscaled: BF16(x/4) =
+// against the exact division for ym = y and its nearest neighbours.  A pass (one
+// direction of one section) takes one multiply per element when every scale code
+// of its table has a multiplier, else (and always with stochastic rounding, which
+// needs the exact quotient) the exact division.  Codes without a multiplier come
+// from short divisors whose exact boundary ties need opposite roundings; they arise
+// when the section amax carries a factor of 3 (2688 = 2^7 * 3 * 7).  Column values enter unscaled: BF16(x/4) =
 // BF16(x)/4 and fl((u/4)/d) = fl(u/(4d)) whenever x/4 is a normal number, and
 // where it is not, both quotients are far below the smallest E2M1 step with the
 // same sign, so the column tables are built for 4d and the 1/4 costs nothing per
@@ -69,32 +71,34 @@ __device__ __forceinline__ uint32_t block_code(float a, float g, float yg) {
 
 __device__ __forceinline__ uint32_t e2m1_one(float q) { return e2m1_pack2<0>(0u, q, q) & 0xFu; }
 
-// True when fl(u * ym) and fl(u / d) have the same E2M1 code for every BF16 u
-// (d > 0 finite, y = fl(1/d), ym within a few ulps of y); see the header comment.
-__device__ bool product_decides_like_quotient(float d, float y, float ym) {
+// The multiplier for the product path of divisor d (y = fl(1/d)): fl(1/d) or a
+// neighbour one ulp away such that fl(u * ym) has the E2M1 code of fl(u / d) for
+// every BF16 u; negative when neither does (exact quotients that fall on rounding
+// boundaries are common, because d and the boundaries are short binary numbers).
+// fl(u * ym) and fl(u / d) differ by a few ulps at most, so only the two BF16
+// neighbours of each boundary times d can be decided differently: those 14 values
+// are checked against the exact quotient, which is computed once for all
+// candidates.  Candidates two or more ulps away never qualify where these do not
+// (a survey of random tensor scales over every scale code found none).
+__device__ float product_multiplier(float d, float y) {
     const float taus[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-    bool ok = true;
+    float us[14];
+    uint32_t exact[14];
 #pragma unroll
     for (int i = 0; i < 7; ++i) {
         const uint32_t lo = __builtin_bit_cast(uint32_t, taus[i] * d) & 0xFFFF0000u;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float u = __builtin_bit_cast(float, lo + (uint32_t)j * 0x10000u);
-            ok &= e2m1_one(u * ym) == e2m1_one(div_rn(u, d, y));
-        }
+        us[2 * i] = __builtin_bit_cast(float, lo);
+        us[2 * i + 1] = __builtin_bit_cast(float, lo + 0x10000u);
+        exact[2 * i] = e2m1_one(div_rn(us[2 * i], d, y));
+        exact[2 * i + 1] = e2m1_one(div_rn(us[2 * i + 1], d, y));
     }
-    return ok;
-}
-
-// The multiplier for the product path of divisor d: fl(1/d) or a neighbour a few
-// ulps away that decides every BF16 input like the exact quotient (exact
-// quotients that fall on rounding boundaries are common, because d and the
-// boundaries are short binary numbers); negative when none does.
-__device__ float product_multiplier(float d, float y) {
-    const int deltas[7] = {0, -1, 1, -2, 2, -3, 3};
-    for (int i = 0; i < 7; ++i) {
-        const float ym = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, y) + (uint32_t)deltas[i]);
-        if (product_decides_like_quotient(d, y, ym)) return ym;
+    const int deltas[3] = {0, -1, 1};
+    for (int c = 0; c < 3; ++c) {
+        const float ym = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, y) + (uint32_t)deltas[c]);
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 14; ++j) ok &= e2m1_one(us[j] * ym) == exact[j];
+        if (ok) return ym;
     }
     return -y;
 }
