@@ -71,7 +71,14 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_scale(const DsaNvfp4Args a) {
         A = *a.amax_in;
     } else if (a.m > 0) {
         float p = 0.0f;
-        for (int i = threadIdx.x; i < a.n_wg; i += 256) p = __builtin_fmaxf(p, a.partials[i]);
+        // 16 loads in flight per thread per round
+        for (int i0 = threadIdx.x; i0 < a.n_wg; i0 += 256 * 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = i0 + 256 * u < a.n_wg ? a.partials[i0 + 256 * u] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) p = __builtin_fmaxf(p, v[u]);
+        }
         A = wg_max(p, red);
     }
     const float g = tensor_scale(A);

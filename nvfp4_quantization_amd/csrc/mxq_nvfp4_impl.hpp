@@ -537,10 +537,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
 
     // The section's last tile: every partial is in.
     uint32_t ar = 0, ac = 0;
-    for (int i = lane; i < n; i += 64) {
-        const uint64_t v = ws_load64(G.partials + first + i);
-        ar = (uint32_t)v > ar ? (uint32_t)v : ar;
-        ac = (uint32_t)(v >> 32) > ac ? (uint32_t)(v >> 32) : ac;
+    // 16 loads in flight per lane per round: one at a time would cost a memory round
+    // trip per 64 partials at the very end of the kernel
+    for (int i0 = lane; i0 < n; i0 += 64 * 16) {
+        uint64_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = i0 + 64 * u < n ? ws_load64(G.partials + first + i0 + 64 * u) : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            ar = (uint32_t)v[u] > ar ? (uint32_t)v[u] : ar;
+            ac = (uint32_t)(v[u] >> 32) > ac ? (uint32_t)(v[u] >> 32) : ac;
+        }
     }
     ar = wave_max_u32(ar);
     ac = wave_max_u32(ac);
