@@ -367,17 +367,20 @@ __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, fl
 // The row pass of a tile: 16 row blocks per lane.  FAST (the column pass ran and
 // reports NaN column blocks in nan): block maxima from the FP32 widened values,
 // then the lanes whose sub-tile holds a NaN redo all their rows with packed integer
-// maxima, where a NaN shows.
-template <bool SR, bool FAST>
+// maxima, where a NaN shows.  The scale bytes go to LDS (rsc: row r of the tile at
+// r * RSTRIDE, this lane's block at + cc), to leave later in one piece per row for
+// the whole work-group.
+template <bool SR, bool FAST, int RSTRIDE>
 __device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2], int s, int64_t row0, int64_t c0,
                                           int64_t r_local0, float g_r, float yg_r, const float4* tab_r, bool nan,
-                                          bool div_mode) {
+                                          bool div_mode, uint8_t* rsc) {
     const int64_t k = G.k;
     const u32x4 no_rnd = {0, 0, 0, 0};
+    const int lane_row = (threadIdx.x & 63) >> 3 << 4, cc = threadIdx.x & 7;
     auto put = [&](int t, const BlockOut& o) {
         const int64_t row = row0 + t;
         *reinterpret_cast<uint2*>(G.row_codes + row * (k >> 1) + (c0 >> 1)) = o.codes;
-        G.row_scales[row * (k >> 4) + (c0 >> 4)] = (uint8_t)o.scale;
+        rsc[(lane_row + t) * RSTRIDE + cc] = (uint8_t)o.scale;
     };
     auto rnd_of = [&](int t) {
         return block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
@@ -585,10 +588,14 @@ __global__ __launch_bounds__(64) void k_nvfp4_given(const Nvfp4Group G) {
 }
 
 // AOUT: the section maxima are supplied, and the measured ones are wanted out.
-template <bool ROW, bool COL, bool FP8, bool SR, bool AOUT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_nvfp4_quant(const Nvfp4Group G) {
-    const int lane = threadIdx.x;
-    const int b = blockIdx.x;
+// W waves per work-group take W adjacent column tiles of the same rows (k / 128 a
+// multiple of W), so that each row's W x 8 scale bytes leave as one piece: scattered
+// 8-byte pieces cost the memory system about three times as much per byte.
+template <bool ROW, bool COL, bool FP8, bool SR, bool AOUT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void k_nvfp4_quant(const Nvfp4Group G) {
+    const int lane = threadIdx.x & 63;
+    const int w = W > 1 ? (int)(threadIdx.x >> 6) : 0;
+    const int b = (int)blockIdx.x * W + w;
     const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
     const int s = section_of(G, T);
     const int tb = lane >> 3, cc = lane & 7;
@@ -605,9 +612,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     // Column codes / scales of the tile by (column, 16-row block): 64 + 8 bytes per
     // column, with one more slot after every 16 columns so that the 8 lane groups
     // that write columns 16 apart use both halves of the LDS banks.
-    __shared__ uint2 lds_codes[kTileCols * 8 + 8 * 8];
-    __shared__ uint8_t lds_sc[kTileCols * 8 + 8 * 8];
+    __shared__ uint2 lds_codes_w[W][kTileCols * 8 + 8 * 8];
+    __shared__ uint8_t lds_sc_w[W][kTileCols * 8 + 8 * 8];
+    __shared__ uint8_t lds_rsc[kTileRows * 8 * W];        // row scales of the work-group's tiles
+    uint2* const lds_codes = lds_codes_w[w];
+    uint8_t* const lds_sc = lds_sc_w[w];
     {
+        // every wave writes the whole table (the same values): no wave reads an entry
+        // before its own write
         const float4* src = G.tables + s * 256;
         if (ROW) { tab[0][lane] = src[lane]; tab[0][64 + lane] = src[64 + lane]; }
         if (COL) { tab[1][lane] = src[128 + lane]; tab[1][64 + lane] = src[192 + lane]; }
@@ -697,8 +709,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     if (ROW) {
         const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
         const float4* tab_r = tab[0];
-        const float ra = row_pass<SR, COL>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan,
-                                           tab_r[0].w != 0.0f);
+        const float ra = row_pass<SR, COL, 8 * W>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan,
+                                                  tab_r[0].w != 0.0f, lds_rsc + 8 * w);
+        if (W > 1) {
+            __syncthreads();
+        } else {
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+        // 128 rows x 8W bytes: W consecutive threads store one row's piece
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int i = it * 64 * W + (int)threadIdx.x;
+            const int r = i / W, part = i - r * W;
+            const uint2 v = *reinterpret_cast<const uint2*>(lds_rsc + r * 8 * W + part * 8);
+            *reinterpret_cast<uint2*>(G.row_scales + ((int64_t)T * kTileRows + r) * (k >> 4) + (int64_t)(C - w) * 8 +
+                                      part * 8) = v;
+        }
         if (AOUT && G.amax_out_row) {
             // supplied maxima: measure this call's for the caller's next step
             const float w = wave_max_f32(ra);
@@ -759,14 +786,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 // mxq_nvfp4_quant_*.hip units, one per (SR, AOUT) pair).
 template <bool SR, bool AOUT>
 hipError_t launch_quant_variant(const Nvfp4Group& g, uint32_t flags, hipStream_t stream) {
+    if (g.n_ctiles % 4 == 0) {
+        const dim3 grid((unsigned)(g.total_tiles / 4)), block(256);
+        switch (flags & 7u) {
+            case 1: hipLaunchKernelGGL((k_nvfp4_quant<true, false, false, SR, AOUT, 4>), grid, block, 0, stream, g); break;
+            case 2: hipLaunchKernelGGL((k_nvfp4_quant<false, true, false, SR, AOUT, 4>), grid, block, 0, stream, g); break;
+            case 3: hipLaunchKernelGGL((k_nvfp4_quant<true, true, false, SR, AOUT, 4>), grid, block, 0, stream, g); break;
+            case 5: hipLaunchKernelGGL((k_nvfp4_quant<true, false, true, SR, AOUT, 4>), grid, block, 0, stream, g); break;
+            case 6: hipLaunchKernelGGL((k_nvfp4_quant<false, true, true, SR, AOUT, 4>), grid, block, 0, stream, g); break;
+            case 7: hipLaunchKernelGGL((k_nvfp4_quant<true, true, true, SR, AOUT, 4>), grid, block, 0, stream, g); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)g.total_tiles), block(64);
     switch (flags & 7u) {
-        case 1: hipLaunchKernelGGL((k_nvfp4_quant<true, false, false, SR, AOUT>), grid, block, 0, stream, g); break;
-        case 2: hipLaunchKernelGGL((k_nvfp4_quant<false, true, false, SR, AOUT>), grid, block, 0, stream, g); break;
-        case 3: hipLaunchKernelGGL((k_nvfp4_quant<true, true, false, SR, AOUT>), grid, block, 0, stream, g); break;
-        case 5: hipLaunchKernelGGL((k_nvfp4_quant<true, false, true, SR, AOUT>), grid, block, 0, stream, g); break;
-        case 6: hipLaunchKernelGGL((k_nvfp4_quant<false, true, true, SR, AOUT>), grid, block, 0, stream, g); break;
-        case 7: hipLaunchKernelGGL((k_nvfp4_quant<true, true, true, SR, AOUT>), grid, block, 0, stream, g); break;
+        case 1: hipLaunchKernelGGL((k_nvfp4_quant<true, false, false, SR, AOUT, 1>), grid, block, 0, stream, g); break;
+        case 2: hipLaunchKernelGGL((k_nvfp4_quant<false, true, false, SR, AOUT, 1>), grid, block, 0, stream, g); break;
+        case 3: hipLaunchKernelGGL((k_nvfp4_quant<true, true, false, SR, AOUT, 1>), grid, block, 0, stream, g); break;
+        case 5: hipLaunchKernelGGL((k_nvfp4_quant<true, false, true, SR, AOUT, 1>), grid, block, 0, stream, g); break;
+        case 6: hipLaunchKernelGGL((k_nvfp4_quant<false, true, true, SR, AOUT, 1>), grid, block, 0, stream, g); break;
+        case 7: hipLaunchKernelGGL((k_nvfp4_quant<true, true, true, SR, AOUT, 1>), grid, block, 0, stream, g); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
