@@ -387,10 +387,11 @@ def test_grouped_sign_masks(orc, mask):
     compare_grouped(orc, w.tensors["x"].to(dev), w.params["split_sections"], mask, 3)
 
 
-def test_grouped_sr_small(orc):
+@pytest.mark.parametrize("k", [384, 512])
+def test_grouped_sr_small(orc, k):
     dev = device()
-    announce("grouped sr small")
-    w = synth.grouped_nvfp4_sr(total_rows=1024, k=384, parts=12, forced_empty=3, seed=33)
+    announce(f"grouped sr small k={k}")
+    w = synth.grouped_nvfp4_sr(total_rows=1024, k=k, parts=12, forced_empty=3, seed=33)
     p = w.params
     compare_grouped(orc, w.tensors["x"].to(dev), p["split_sections"], p["sign_mask"], 3, p["seed"],
                     p["row_offsets"], p["col_offsets"])
@@ -434,21 +435,23 @@ def tie_matrix(rows, k, sections, mask, seed):
     return (f32.view(np.uint32) >> 16).astype(np.uint16)    # exact: every value is short
 
 
-def test_grouped_exact_ties(orc):
+@pytest.mark.parametrize("k", [256, 512])
+def test_grouped_exact_ties(orc, k):
     dev = device()
-    announce("grouped exact ties")
+    announce(f"grouped exact ties k={k}")
     sections = [256, 0, 384]
     for mask in (0x0000, 0x6C93):
-        b = tie_matrix(640, 256, sections, mask, 77 + mask)
+        b = tie_matrix(640, k, sections, mask, 77 + mask)
         x = bf16_dev(b, dev)
         compare_grouped(orc, x, sections, mask, 3)
         compare_grouped(orc, x, sections, mask, 7)
 
 
-def test_grouped_edges(orc):
+@pytest.mark.parametrize("k", [256, 512])          # one- and four-wave quant work-groups
+def test_grouped_edges(orc, k):
     dev = device()
-    announce("grouped edges")
-    b = edge_matrix(384, 256, 10)
+    announce(f"grouped edges k={k}")
+    b = edge_matrix(384, k, 10)
     b[100:116, 40] = 0x7FC0            # NaN in a column block
     b[200:216, :] = 0                   # a zero 16-row band
     x = bf16_dev(b, dev)
@@ -458,13 +461,13 @@ def test_grouped_edges(orc):
 
 @pytest.mark.parametrize("sections", [[128], [0, 0, 256, 0], [128] * 9, [0] * 40 + [256] + [0] * 30,
                                       [128, 0] * 70 + [256] * 10, [0, 0, 0]])
-def test_grouped_section_shapes(orc, sections):
+@pytest.mark.parametrize("k", [256, 1024])
+def test_grouped_section_shapes(orc, sections, k):
     """One section, all-empty-but-one, many 128-row sections, more than one launch
     group (> 64 sections), and an all-empty call (only the floor scales are written)."""
     dev = device()
     total = sum(sections)
-    announce(f"grouped sections n={len(sections)} total={total}")
-    k = 256
+    announce(f"grouped sections n={len(sections)} total={total} k={k}")
     w = synth.grouped_nvfp4(total_rows=max(total, 128), k=k, parts=1, seed=35)
     x = w.tensors["x"][:total].contiguous().to(dev)
     compare_grouped(orc, x, sections, 0x1357, 7)
@@ -481,10 +484,11 @@ def test_grouped_max_sections(orc):
                     ro=list(range(256)), co=list(range(1000, 1256)))
 
 
-def test_grouped_guard_bytes(orc):
+@pytest.mark.parametrize("k", [384, 512])
+def test_grouped_guard_bytes(orc, k):
     dev = device()
-    announce("grouped guard bytes")
-    sections, k, flags = [256, 0, 128], 384, 7
+    announce(f"grouped guard bytes k={k}")
+    sections, flags = [256, 0, 128], 7
     total, S = sum(sections), len(sections)
     w = synth.grouped_nvfp4(total_rows=total, k=k, parts=1, seed=37)
     x = w.tensors["x"].to(dev)
