@@ -104,17 +104,13 @@ __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
 // Stochastic E2M1 rounding with 8 random bits r: grid spacing D = 0.5 / 1 / 2
 // below 2 / 4 / 6; with u = |q| / D = k + f the value rounds up iff
 // floor(256 f) + r >= 256; |q| >= 6 saturates.  Returns the 4-bit code.
+// gfx950's stochastic conversion does exactly this for the first value of a pair
+// when the random operand is r << 24 (its low 24 bits zero): checked against the
+// rule for every FP32 value with |q| in [2^-20, 16) and every r, and on sampled
+// smaller, subnormal and larger values.  (The pair's second value draws on the
+// random operand differently, so each value gets a conversion of its own.)
 __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t r) {
-    uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 28) & 8u;
-    float a = __builtin_fabsf(q);
-    float inv_step = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
-    uint32_t base = a < 2.0f ? 0u : (a < 4.0f ? 2u : 4u);
-    float u = a * inv_step;                       // exact (power-of-two factor)
-    float k = __builtin_floorf(u);
-    uint32_t F = (uint32_t)((u - k) * 256.0f);    // exact, in [0, 255]
-    uint32_t code = (uint32_t)k + base + ((F + r) >= 256u ? 1u : 0u);
-    code = a < 6.0f ? code : 7u;
-    return sign | code;
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{q, 0.0f}, r << 24, 1.0f, 0) & 0xFu;
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).
