@@ -214,7 +214,7 @@ def main():
         desc = f"swiglu -> fp8_1x128, {m} tokens x {n} (fused gate|up bf16 buffer)"
     elif wl == "dsa_rotate_nvfp4":
         kern = kernel_times(mxq, torch, calls, n_sets, K, stream,
-                            ("k_dsa_nvfp4_amax+k_dsa_nvfp4_scale", "k_dsa_nvfp4_quant"))
+                            ("k_dsa_nvfp4_amax", "k_dsa_nvfp4_quant"))
 
     if args.profile:
         del calls

@@ -205,9 +205,10 @@ mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_p
  *   global_scale  device float[1]: g (also written for m = 0: the floor scale, or
  *                 the scale of *amax_in)
  *   workspace     device memory of mxq_hadamard_quant_nvfp4_workspace_size(m)
- *                 bytes (2 KB of scale table + 4 bytes per 64 rows, rounded up to
- *                 256), 256-byte aligned, no initialization needed.  Calls that
- *                 share it must be ordered.  May be NULL when m = 0.
+ *                 bytes (16.25 KB of counters, 2 KB of scale table and 4 bytes per
+ *                 64 rows, rounded up to 256), 256-byte aligned, ZERO-FILLED BEFORE
+ *                 ITS FIRST USE; every call leaves its counters at zero again.  Calls
+ *                 that share it must be ordered.  May be NULL when m = 0.
  * Requirements: as mxq_hadamard_quant_fp8; codes and block_scales 16-byte aligned,
  * global_scale, amax_in, amax_out 4-byte aligned; m <= 2^31 - 128.  Errors are
  * returned before anything is enqueued.

@@ -296,8 +296,8 @@ def mxq_hadamard_quant_nvfp4_workspace_size(m: int) -> int:
 
 
 class HadamardNVFP4:
-    """A prepared DSA rotate + NVFP4 call: outputs and a workspace are allocated
-    once; each call runs the quantizer on `pe`, `nope` as they are then.
+    """A prepared DSA rotate + NVFP4 call: outputs and a zero-filled workspace are
+    allocated once; each call runs the quantizer on `pe`, `nope` as they are then.
     pe: [m][d_pe], nope: [m][128-d_pe] BF16 with unit column stride (either may be
     None when empty).  amax_in: None (measure), a float, or a device float32 tensor
     of one element.  amax_out: also return the measured max |y|."""

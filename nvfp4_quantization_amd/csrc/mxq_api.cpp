@@ -229,6 +229,7 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
     a.global_scale = global_scale;
     a.amax_in = amax_in;
     a.amax_out = amax_out;
+    a.ctrl = m > 0 ? reinterpret_cast<uint32_t*>(ws + mxq::kDsaCtrlOffset) : nullptr;
     a.table = m > 0 ? reinterpret_cast<float4*>(ws + mxq::kDsaTableOffset) : nullptr;
     a.partials = m > 0 ? reinterpret_cast<float*>(ws + mxq::kDsaPartialsOffset) : nullptr;
     return mxq::launch_hadamard_quant_nvfp4(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK

@@ -42,9 +42,14 @@ __device__ __forceinline__ void halves(const float (&v)[32], float (&h0)[16], fl
 
 }  // namespace
 
-// Phase A: max |y| of the work-group's 64 rows into its partial (a plain store:
-// the scale kernel that folds the partials runs after this kernel has ended).
+// Phase A: max |y| of the work-group's 64 rows into its partial.  The work-group
+// that finishes last folds the partials into the tensor scale and writes the
+// table.  Which one that is comes from two levels of counters: work-group i counts
+// in at group counter i % 64, and the last of each group at the top counter, so
+// that no counter takes more than about n_wg / 64 atomics (a single counter for all
+// 4096 work-groups serialized them and cost 40 us).
 __global__ __launch_bounds__(256) void k_dsa_nvfp4_amax(const DsaNvfp4Args a) {
+    __shared__ uint32_t last_s;
     __shared__ float red[4];
     const int quarter = threadIdx.x & 3;
     const int64_t r = (int64_t)blockIdx.x * kDsaRows + (threadIdx.x >> 2);
@@ -58,34 +63,57 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_amax(const DsaNvfp4Args a) {
     const float m = __builtin_fmaxf(absmax16(h0), absmax16(h1));
     const float lane = v[0] != v[0] ? 0.0f : round_bf16(m * k_inv_sqrt128());
     const float wg = wg_max(lane, red);
-    if (threadIdx.x == 0) a.partials[blockIdx.x] = wg;
-}
-
-// The tensor scale and the scale table: A is the supplied amax, or the maximum of
-// the partials (measured), or 0 for a tensor without rows.  With a supplied amax
-// the measured-amax output is zeroed here and raised by the quantize kernel.
-__global__ __launch_bounds__(256) void k_dsa_nvfp4_scale(const DsaNvfp4Args a) {
-    __shared__ float red[4];
-    float A = 0.0f;
-    if (a.amax_in) {
-        A = *a.amax_in;
-    } else if (a.m > 0) {
-        float p = 0.0f;
-        // 16 loads in flight per thread per round
-        for (int i0 = threadIdx.x; i0 < a.n_wg; i0 += 256 * 16) {
-            float v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = i0 + 256 * u < a.n_wg ? a.partials[i0 + 256 * u] : 0.0f;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) p = __builtin_fmaxf(p, v[u]);
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.partials) + blockIdx.x, __builtin_bit_cast(uint32_t, wg),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): the partial is stored
+        const int grp = (int)(blockIdx.x % kDsaGroups);
+        const int n_grp = (a.n_wg - grp + kDsaGroups - 1) / kDsaGroups;
+        uint32_t last = 0;
+        if (__hip_atomic_fetch_add(a.ctrl + grp * kDsaCtrlStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (uint32_t)(n_grp - 1)) {
+            const int groups = a.n_wg < kDsaGroups ? a.n_wg : kDsaGroups;
+            last = __hip_atomic_fetch_add(a.ctrl + kDsaGroups * kDsaCtrlStride, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(groups - 1);
         }
-        A = wg_max(p, red);
+        last_s = last;
     }
-    const float g = tensor_scale(A);
-    if (a.m > 0 && threadIdx.x < 128) a.table[threadIdx.x] = table_entry((int)threadIdx.x, g, false);
+    __syncthreads();
+    if (!last_s) return;
+
+    // The last work-group: every partial is in.  Non-negative floats order like
+    // their bit patterns; 16 loads in flight per thread per round.
+    uint32_t A = 0;
+    for (int i0 = threadIdx.x; i0 < a.n_wg; i0 += 256 * 16) {
+        uint32_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            v[u] = i0 + 256 * u < a.n_wg ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(a.partials) + i0 + 256 * u,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                         : 0u;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) A = v[u] > A ? v[u] : A;
+    }
+    const float amax = wg_max(__builtin_bit_cast(float, A), red);
+    const float g = tensor_scale(amax);
+    if (threadIdx.x < 128) a.table[threadIdx.x] = table_entry((int)threadIdx.x, g, false);
+    if (threadIdx.x <= kDsaGroups)                                 // ready for the next call
+        __hip_atomic_store(a.ctrl + threadIdx.x * kDsaCtrlStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) {
         *a.global_scale = g;
-        if (a.amax_out) *a.amax_out = a.amax_in ? 0.0f : A;
+        if (a.amax_out) *a.amax_out = amax;
+    }
+}
+
+// The tensor scale and the scale table from the supplied amax, or from A = 0 for a
+// tensor without rows.  With a supplied amax the measured-amax output is zeroed
+// here and raised by the quantize kernel.
+__global__ __launch_bounds__(128) void k_dsa_nvfp4_scale(const DsaNvfp4Args a) {
+    const float g = tensor_scale(a.amax_in ? *a.amax_in : 0.0f);
+    if (a.m > 0) a.table[threadIdx.x] = table_entry((int)threadIdx.x, g, false);
+    if (threadIdx.x == 0) {
+        *a.global_scale = g;
+        if (a.amax_out) *a.amax_out = 0.0f;
     }
 }
 
@@ -139,11 +167,10 @@ hipError_t launch_hadamard_quant_nvfp4(const DsaNvfp4Args& a, hipStream_t stream
     const bool given = a.amax_in != nullptr;
     hipError_t e = launch_mark(0, stream);
     if (e != hipSuccess) return e;
-    if (!given && a.m > 0) {
+    if (!given && a.m > 0)
         hipLaunchKernelGGL(k_dsa_nvfp4_amax, dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k_dsa_nvfp4_scale, dim3(1), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_dsa_nvfp4_scale, dim3(1), dim3(128), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess || a.m == 0) return e;
     if ((e = launch_mark(1, stream)) != hipSuccess) return e;
     if (given && a.amax_out)

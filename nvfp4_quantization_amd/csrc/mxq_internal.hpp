@@ -56,11 +56,11 @@ struct DsaArgs {
 hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream, bool ue8m0 = false);
 
 // ---------------------------------------------------------------- DSA rotate + NVFP4
-// With a measured tensor amax three kernels: the first rotates 64 rows per
-// 256-thread work-group and stores the work-group's max |y| as a partial; a
-// one-work-group kernel folds the partials into the tensor scale and writes the
-// scale table; the last rotates again and encodes.  With a supplied amax the first
-// is left out.
+// Two kernels: the first rotates 64 rows per 256-thread work-group and stores the
+// work-group's max |y| as a partial; the work-group that finishes last (two levels
+// of counters tell which) folds the partials into the tensor scale, writes the
+// scale table and resets the counters; the second rotates again and encodes.  With
+// a supplied amax a one-work-group kernel forms the scale and the table instead.
 struct DsaNvfp4Args {
     const uint16_t* pe;
     const uint16_t* nope;
@@ -72,12 +72,18 @@ struct DsaNvfp4Args {
     float* global_scale;              // [1]
     const float* amax_in;             // [1] or null: measure
     float* amax_out;                  // [1] or null
+    uint32_t* ctrl;                   // workspace: kDsaGroups group counters and the top counter
     float4* table;                    // workspace: 128 scale-table entries
     float* partials;                  // workspace: one max per work-group
 };
 hipError_t launch_hadamard_quant_nvfp4(const DsaNvfp4Args& a, hipStream_t stream);
-// Workspace layout of the DSA NVFP4 call (byte offsets).
-constexpr int64_t kDsaTableOffset = 0;
+// Workspace layout of the DSA NVFP4 call (byte offsets): counters (each on its own
+// 256-byte line: group counter g at word g * kDsaCtrlStride, the top counter after
+// them), the scale table, one partial per work-group.
+constexpr int kDsaGroups = 64;
+constexpr int kDsaCtrlStride = 64;
+constexpr int64_t kDsaCtrlOffset = 0;
+constexpr int64_t kDsaTableOffset = (int64_t)(kDsaGroups + 1) * kDsaCtrlStride * 4;
 constexpr int64_t kDsaPartialsOffset = kDsaTableOffset + 128 * 16;
 
 // ---------------------------------------------------------------- grouped NVFP4

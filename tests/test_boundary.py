@@ -196,13 +196,15 @@ def test_dsa_nvfp4_argument_errors(L):
 
 
 def test_dsa_nvfp4_workspace_size(L):
-    """128 table entries, then 4 bytes per 64 rows, rounded to 256."""
+    """65 counters on their own 256-byte lines, 128 table entries, then 4 bytes per
+    64 rows, rounded to 256."""
     q = L.mxq_hadamard_quant_nvfp4_workspace_size
+    fixed = 65 * 256 + 2048
     assert q(0) == 0 and q(-5) == 0
-    assert q(1) == 2048 + 256
-    assert q(64 * 64) == 2048 + 256
-    assert q(64 * 64 + 1) == 2048 + 512
-    assert q(262144) == 2048 + 4 * 4096
+    assert q(1) == fixed + 256
+    assert q(64 * 64) == fixed + 256
+    assert q(64 * 64 + 1) == fixed + 512
+    assert q(262144) == fixed + 4 * 4096
 
 
 def swiglu(L, g=A, ldg=256, u=A, ldu=256, m=8, n=256, q=A, ldq=256, s=A, sr=2, sg=1):

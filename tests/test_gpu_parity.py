@@ -278,6 +278,9 @@ def compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_in=None, amax_out=False, ca
     assert_same("codes", host(res.codes), ref.codes)
     if amax_out:
         assert_same("amax", host(res.amax), np.array([ref.amax], np.float32))
+    if pe_np.shape[0] > 0:
+        ctr = host(call.workspace)[:65 * 256].view(np.uint32)[::64]
+        assert not ctr.any(), "a completion counter was left nonzero"
     return res, ref
 
 
@@ -337,7 +340,8 @@ def test_dsa_nvfp4_empty(orc):
 
 def test_dsa_nvfp4_reuse(orc):
     """One prepared call run twice, then a smaller input through the same workspace
-    (left over partials and table from the larger call): every run matches."""
+    (left over partials and table from the larger call): every run matches and
+    leaves the counters at zero."""
     dev = device()
     announce("dsa nvfp4 reuse")
     w = synth.dsa_rotate_fp8(tokens=100, heads=8, seed=78)
