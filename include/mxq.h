@@ -264,7 +264,7 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
  *
  * workspace: device memory of at least
  *   mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
- *   bytes (0 when only MXQ_FP8_ROWWISE is requested; otherwise 136 KB plus 8 bytes
+ *   bytes (0 when only MXQ_FP8_ROWWISE is requested; otherwise 264 KB plus 8 bytes
  *   per 128 x 128 tile of x), 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE.
  *   It holds per-section counters, per-tile partial maxima and per-section scale
  *   tables through which the two kernels of a call meet; every call leaves the

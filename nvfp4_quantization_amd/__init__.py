@@ -379,7 +379,7 @@ def alloc_nvfp4_outputs(total_rows: int, k: int, num_sections: int, flags: int, 
     return r
 
 
-WORKSPACE_COUNTERS = 32            # per-section counters at the start of the workspace
+WORKSPACE_COUNTERS = 32 * 17          # per launch group: 16 group counters and a top counter per section
 WORKSPACE_COUNTER_STRIDE = 256     # bytes between two counters
 
 

@@ -142,13 +142,15 @@ hipError_t launch_quant_rne_aout(const Nvfp4Group& g, uint32_t flags, hipStream_
 hipError_t launch_quant_sr_aout(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
 
 // Workspace layout (byte offsets):
-//   kCtrlOffset    counter of section s at word kCtrlStride * s (own 256-byte line)
+//   kCtrlOffset    section s: kCtrlGroups group counters and a top counter, each on
+//                  its own 256-byte line, at words kCtrlStride * ((kCtrlGroups + 1) * s + i)
 //   kTablesOffset  section s, direction dir (0 row, 1 column), scale code c:
 //                  float4 at index (s * 2 + dir) * 128 + c = (d, 1/d, multiplier, 0)
 //   kPartialsOffset  one 8-byte partial per 128 x 128 tile
 constexpr int kCtrlStride = 64;
+constexpr int kCtrlGroups = 16;
 constexpr int64_t kCtrlOffset = 0;
-constexpr int64_t kTablesOffset = (int64_t)kGroupSections * kCtrlStride * 4;
+constexpr int64_t kTablesOffset = (int64_t)kGroupSections * (kCtrlGroups + 1) * kCtrlStride * 4;
 constexpr int64_t kTablesBytes = (int64_t)kGroupSections * 2 * 128 * 16;
 constexpr int64_t kPartialsOffset = kTablesOffset + kTablesBytes;
 

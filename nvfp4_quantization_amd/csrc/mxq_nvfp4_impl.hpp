@@ -529,12 +529,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
 
     const int first = G.tt_start[s] * G.n_ctiles;                 // first tile of the section
     const int n = (G.tt_start[s + 1] - G.tt_start[s]) * G.n_ctiles;
-    uint32_t* counter = G.ctrl + kCtrlStride * s;
+    // Which tile of the section finishes last comes from two levels of counters: the
+    // tile counts in at group counter (b - first) % kCtrlGroups, the last of each
+    // group at the section's top counter, so that no counter takes more than about
+    // n / kCtrlGroups atomics (same-address atomics are served one at a time).
+    uint32_t* const ctrl_s = G.ctrl + kCtrlStride * (kCtrlGroups + 1) * s;
     uint32_t last = 0;
     if (lane == 0) {
         ws_store64(G.partials + b, (uint64_t)(mr << 16) | ((uint64_t)__builtin_bit_cast(uint32_t, mc) << 32));
         __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): the partial is stored
-        last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(n - 1);
+        const int grp = (b - first) % kCtrlGroups;
+        const int n_grp = (n - grp + kCtrlGroups - 1) / kCtrlGroups;
+        if (__hip_atomic_fetch_add(ctrl_s + kCtrlStride * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (uint32_t)(n_grp - 1)) {
+            const int groups = n < kCtrlGroups ? n : kCtrlGroups;
+            last = __hip_atomic_fetch_add(ctrl_s + kCtrlStride * kCtrlGroups, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(groups - 1);
+        }
     }
     if (!__shfl((int)last, 0, 64)) return;
 
@@ -560,8 +571,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
     if (lane == 0) {
         if (ROW) G.row_global[s] = g_r;
         if (COL) G.col_global[s] = g_c;
-        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
     }
+    if (lane <= kCtrlGroups)                                      // ready for the next call
+        __hip_atomic_store(ctrl_s + kCtrlStride * lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     build_tables<ROW, COL>(G, s, g_r, g_c);
     if (lane == 0) {
         // the measured maxima for a caller's next-step scaling

@@ -120,7 +120,7 @@ def test_workspace_size_query(L):
     assert q(16384, 4096, 8, 4) == 0                              # FP8 only: no amax pass
     # counters (32 x 256 B) and scale tables (32 sections x 2 directions x 128 x 16 B)
     # of one launch group, then one 8-byte partial per 128 x 128 tile
-    fixed = 32 * 256 + 32 * 2 * 128 * 16
+    fixed = 32 * 17 * 256 + 32 * 2 * 128 * 16
     for total, k, S in [(0, 4096, 8), (16384, 4096, 8), (65536, 7168, 32), (128, 128, 1), (16384, 4096, 256)]:
         for flags in (1, 2, 3, 7):
             need = q(total, k, S, flags)
