@@ -572,8 +572,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
         if (ROW) G.row_global[s] = g_r;
         if (COL) G.col_global[s] = g_c;
     }
-    if (lane <= kCtrlGroups)                                      // ready for the next call
-        __hip_atomic_store(ctrl_s + kCtrlStride * lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = lane; i <= kCtrlGroups; i += 64)                 // ready for the next call
+        __hip_atomic_store(ctrl_s + kCtrlStride * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     build_tables<ROW, COL>(G, s, g_r, g_c);
     if (lane == 0) {
         // the measured maxima for a caller's next-step scaling
