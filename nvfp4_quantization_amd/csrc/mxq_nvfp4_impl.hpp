@@ -465,19 +465,54 @@ __device__ __forceinline__ float4 table_entry(int code, float g, bool quarter) {
 // Scale tables of section s (row-wise, then column-wise), built by one wave.  Entry
 // 0's fourth value flags a direction with a scale code that has no multiplier (its
 // exact ties need opposite roundings): that direction's pass then divides exactly.
+//
+// Every nonzero E4M3 value is (1 + m/8) 2^e, so the divisors d of codes that share
+// m differ by exact powers of two, and so do their critical inputs, reciprocals and
+// candidate multipliers, with the same quotients and products.  Lanes 0..15 search
+// the multiplier of the representative 1 + m/8 (m = lane & 7, direction lane >> 3)
+// once; each entry takes it scaled by 2^-e when its own d and fl(1/d) are the
+// representative's scaled exactly and g < 2^100 keeps every intermediate value of
+// the search normal and finite, and searches on its own otherwise.
 template <bool ROW, bool COL>
 __device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g_r, float g_c) {
+    const int lane = threadIdx.x & 63;
+    const float rep_m = 1.0f + (float)(lane & 7) * 0.125f;
+    float rep_ym = 0.0f;
+    if (lane < 16) {
+        const bool quarter = lane >= 8;
+        float d = rep_m * (quarter ? g_c : g_r);
+        float y = 1.0f / d;
+        if (quarter) { d *= 4.0f; y *= 0.25f; }
+        rep_ym = product_multiplier(d, y);
+    }
     bool none[2] = {false, false};
 #pragma unroll
-    for (int e = threadIdx.x; e < 256; e += 64) {
+    for (int e = lane; e < 256; e += 64) {
         const int dir = e >> 7, code = e & 127;
         if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
-        const float4 entry = table_entry(code, dir ? g_c : g_r, dir == 1);
+        const float g = dir ? g_c : g_r;
+        const float v = e4m3_value((uint32_t)code);
+        const uint32_t vb = __builtin_bit_cast(uint32_t, v);
+        const int m = (int)((vb >> 20) & 7), ex = (int)((vb >> 23) & 0xFF) - 127;
+        const float cls_ym = __shfl(rep_ym, dir * 8 + m, 64);
+        float4 entry;
+        if (code == 0 || code == 127) {
+            entry = table_entry(code, g, dir == 1);
+        } else {
+            float d = v * g, y = 1.0f / d;
+            float rd = (1.0f + (float)m * 0.125f) * g, ry = 1.0f / rd;
+            if (dir == 1) { d *= 4.0f; y *= 0.25f; rd *= 4.0f; ry *= 0.25f; }
+            const bool scaled = g < 0x1p100f && d == __builtin_ldexpf(rd, ex) && y == __builtin_ldexpf(ry, -ex);
+            float ym;
+            if (scaled) ym = __builtin_ldexpf(cls_ym, -ex);
+            else ym = product_multiplier(d, y);
+            entry = make_float4(d, y, ym, 0.0f);
+        }
         none[dir] |= entry.z < 0.0f;
         G.tables[(s * 2 + dir) * 128 + code] = entry;
     }
     const bool flag_r = __ballot(none[0]) != 0, flag_c = __ballot(none[1]) != 0;
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
         if (ROW) G.tables[(s * 2) * 128].w = flag_r ? 1.0f : 0.0f;
         if (COL) G.tables[(s * 2 + 1) * 128].w = flag_c ? 1.0f : 0.0f;
     }
