@@ -272,8 +272,9 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
  *   that share a workspace must be ordered (same stream, or synchronized).
  *
  * Requirements: k % 128 == 0, every m_s % 128 == 0 (else MXQ_ERR_MISALIGNED, with
- * no unfused fallback); 1 <= num_sections <= MXQ_MAX_SECTIONS; total_rows <= 2^31 -
- * 128 and total_rows * k < 2^40; the requested outputs non-NULL and 16-byte aligned
+ * no unfused fallback); 1 <= num_sections <= MXQ_MAX_SECTIONS; k <= 2^26,
+ * total_rows <= 2^31 - 128 and total_rows * k < 2^40 (else MXQ_ERR_UNSUPPORTED);
+ * the requested outputs non-NULL and 16-byte aligned
  * (global scales 4-byte aligned); outputs of directions not requested may be NULL.
  * ------------------------------------------------------------------------- */
 enum { MXQ_ROWWISE = 1u, MXQ_COLUMNWISE = 2u, MXQ_FP8_ROWWISE = 4u };

@@ -16,6 +16,7 @@ namespace {
 constexpr int64_t kMaxGridThreads = 0xFFFFFFFFll;    // 1-D grids only; threads per launch < 2^32
 constexpr int64_t kMaxRows = (1ll << 31) - 128;
 constexpr int64_t kMaxElems = 1ll << 40;
+constexpr int64_t kMaxGroupK = 1ll << 26;   // the grouped kernels address a tile row with 32-bit offsets
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -265,7 +266,7 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
                                                void* workspace, size_t workspace_bytes, void* stream) {
     // ---- checks (nothing is enqueued before all of them pass)
     if (k <= 0 || !split_sections || num_sections < 1) return MXQ_ERR_INVALID_ARGUMENT;
-    if (num_sections > MXQ_MAX_SECTIONS) return MXQ_ERR_UNSUPPORTED;
+    if (num_sections > MXQ_MAX_SECTIONS || k > kMaxGroupK) return MXQ_ERR_UNSUPPORTED;
     if (flags == 0 || (flags & ~(uint32_t)(MXQ_ROWWISE | MXQ_COLUMNWISE | MXQ_FP8_ROWWISE)))
         return MXQ_ERR_INVALID_ARGUMENT;
     if (k % 128 != 0) return MXQ_ERR_MISALIGNED;

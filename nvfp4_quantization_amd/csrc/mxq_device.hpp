@@ -76,8 +76,10 @@ __device__ __forceinline__ float div_rn(float x, float d, float y) {
 }
 
 // E4M3 code (low byte) of a finite v with |v| < 464; nearest-even.
+// (The conversion keeps the high half of its third operand, which the mask drops:
+// passing v's own bits there lets it write v's register in place.)
 __device__ __forceinline__ uint32_t e4m3_code(float v) {
-    return __builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFFu;
+    return __builtin_amdgcn_cvt_pk_fp8_f32(v, v, __builtin_bit_cast(int, v), false) & 0xFFu;
 }
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
     return __builtin_amdgcn_cvt_f32_fp8(code, 0);

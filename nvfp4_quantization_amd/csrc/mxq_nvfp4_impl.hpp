@@ -188,16 +188,17 @@ enum class Enc { Mul, Div, Sr };
 template <Enc E>
 __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, const u32x4& rnd, int r0) {
     uint32_t c = 0;
-    if (E == Enc::Mul) {
-        c = e2m1_pack2<0>(c, u[0] * y, u[1] * y);
-        c = e2m1_pack2<1>(c, u[2] * y, u[3] * y);
-        c = e2m1_pack2<2>(c, u[4] * y, u[5] * y);
-        c = e2m1_pack2<3>(c, u[6] * y, u[7] * y);
-    } else if (E == Enc::Div) {
-        c = e2m1_pack2<0>(c, div_rn(u[0], d, y), div_rn(u[1], d, y));
-        c = e2m1_pack2<1>(c, div_rn(u[2], d, y), div_rn(u[3], d, y));
-        c = e2m1_pack2<2>(c, div_rn(u[4], d, y), div_rn(u[5], d, y));
-        c = e2m1_pack2<3>(c, div_rn(u[6], d, y), div_rn(u[7], d, y));
+    if (E == Enc::Mul || E == Enc::Div) {
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = E == Enc::Mul ? u[i] * y : div_rn(u[i], d, y);
+        // each conversion writes one byte of c and keeps the others; all four are
+        // written, so c starts as the bits of q[0], whose register the first
+        // conversion can then overwrite in place (no zeroing instruction)
+        c = e2m1_pack2<0>(__builtin_bit_cast(uint32_t, q[0]), q[0], q[1]);
+        c = e2m1_pack2<1>(c, q[2], q[3]);
+        c = e2m1_pack2<2>(c, q[4], q[5]);
+        c = e2m1_pack2<3>(c, q[6], q[7]);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -359,7 +360,9 @@ __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, fl
     }
     m_out = m;
     const uint32_t sc = block_code(bf16_mag(m), g_r, yg_r);
-    BlockOut o = encode_block<E>(u, sc, m > 0x7F80u, tab_r, rnd);
+    // (FAST: the FP32 maximum ignores NaNs, so m never flags one; the lanes whose
+    // sub-tile holds a NaN redo their rows without FAST)
+    BlockOut o = encode_block<E>(u, sc, !FAST && m > 0x7F80u, tab_r, rnd);
     o.amax = bf16_mag(m);                            // FAST, or no NaN: max |x| (a NaN block is
     return o;                                        // measured again where that matters)
 }
@@ -369,17 +372,20 @@ __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, fl
 // then the lanes whose sub-tile holds a NaN redo all their rows with packed integer
 // maxima, where a NaN shows.  The scale bytes go to LDS (rsc: row r of the tile at
 // r * RSTRIDE, this lane's block at + cc), to leave later in one piece per row for
-// the whole work-group.
+// the whole work-group.  rc_tile: the tile's first row-code byte (wave-uniform).
 template <bool SR, bool FAST, int RSTRIDE>
 __device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2], int s, int64_t row0, int64_t c0,
                                           int64_t r_local0, float g_r, float yg_r, const float4* tab_r, bool nan,
-                                          bool div_mode, uint8_t* rsc) {
+                                          bool div_mode, uint8_t* rsc, uint8_t* rc_tile) {
     const int64_t k = G.k;
     const u32x4 no_rnd = {0, 0, 0, 0};
     const int lane_row = (threadIdx.x & 63) >> 3 << 4, cc = threadIdx.x & 7;
+    // the lane's offset in the tile fits 32 bits (k <= 2^26), so that each row's
+    // store is a uniform base plus this offset, with no vector address arithmetic
+    const uint32_t lane_off = (uint32_t)lane_row * (uint32_t)(k >> 1) + (uint32_t)cc * 8u;
     auto put = [&](int t, const BlockOut& o) {
-        const int64_t row = row0 + t;
-        *reinterpret_cast<uint2*>(G.row_codes + row * (k >> 1) + (c0 >> 1)) = o.codes;
+        uint8_t* const row_base = rc_tile + (int64_t)t * (k >> 1);
+        *reinterpret_cast<uint2*>(row_base + lane_off) = o.codes;
         rsc[(lane_row + t) * RSTRIDE + cc] = (uint8_t)o.scale;
     };
     auto rnd_of = [&](int t) {
@@ -641,7 +647,7 @@ __global__ __launch_bounds__(64) void k_nvfp4_given(const Nvfp4Group G) {
 template <bool ROW, bool COL, bool FP8, bool SR, bool AOUT, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void k_nvfp4_quant(const Nvfp4Group G) {
     const int lane = threadIdx.x & 63;
-    const int w = W > 1 ? (int)(threadIdx.x >> 6) : 0;
+    const int w = W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;   // wave-uniform
     const int b = (int)blockIdx.x * W + w;
     const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
     const int s = section_of(G, T);
@@ -756,8 +762,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (ROW) {
         const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
         const float4* tab_r = tab[0];
+        uint8_t* const rc_tile = G.row_codes + (int64_t)T * kTileRows * (k >> 1) + (int64_t)C * (kTileCols / 2);
         const float ra = row_pass<SR, COL, 8 * W>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan,
-                                                  tab_r[0].w != 0.0f, lds_rsc + 8 * w);
+                                                  tab_r[0].w != 0.0f, lds_rsc + 8 * w, rc_tile);
         if (W > 1) {
             __syncthreads();
         } else {
