@@ -113,6 +113,7 @@ def test_grouped_argument_errors(L):
     assert grouped(L, ws_bytes=need - 1) == WS_SMALL
     assert grouped(L, ws=A + 64) == MISALIGNED
     assert grouped(L, sections=(1 << 31,)) == UNSUPPORTED
+    assert grouped(L, k=(1 << 26) + 128) == UNSUPPORTED           # tile rows use 32-bit offsets
 
 
 def test_workspace_size_query(L):
