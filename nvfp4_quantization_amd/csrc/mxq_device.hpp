@@ -13,8 +13,9 @@
 //  * The E4M3 / E2M1 / BF16 conversions use gfx950's hardware conversions.  Over
 //    all 2^32 FP32 inputs they equal nearest-even with saturation for every
 //    finite input below 464 (E4M3) and every non-NaN input (E2M1, BF16); the
-//    kernels clamp to 448 (or never exceed 464) before the E4M3 conversion, and
-//    pass a NaN to it only on the NaN path, which rewrites the result.
+//    kernels clamp to 448 (or never exceed 464) before the E4M3 conversion.  A NaN
+//    converts to 0xFF: FP8 element codes turn it into 0x7F, block scales mask it
+//    to the NaN code 0x7F.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +32,8 @@ __device__ __forceinline__ float k_floor() { return __builtin_bit_cast(float, 0x
 __device__ __forceinline__ float k_inv448() { return __builtin_bit_cast(float, 0x3B124925u); }     // 1/448
 __device__ __forceinline__ float k_inv2688() { return __builtin_bit_cast(float, 0x39C30C31u); }    // 1/2688
 __device__ __forceinline__ float k_inv6() { return __builtin_bit_cast(float, 0x3E2AAAABu); }       // 1/6
+// all-ones bit pattern (a table word used as an AND mask, never as a number)
+__device__ __forceinline__ float k_keep_codes() { return __builtin_bit_cast(float, 0xFFFFFFFFu); }
 __device__ __forceinline__ float k_inv_sqrt128() { return __builtin_bit_cast(float, 0x3DB504F3u); } // 1/sqrt(128)
 
 __device__ __forceinline__ float lo_bf16(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
@@ -74,6 +77,20 @@ __device__ __forceinline__ float div_rn(float x, float d, float y) {
     float rn = __builtin_fmaf(q0, d, -x);
     return __builtin_fmaf(-rn, y, q0);
 }
+
+// fl(x / d) with IEEE's special cases: div_fixup returns the quotient of infinite
+// or zero operands as IEEE division gives it (inf / finite = inf, finite / inf = 0,
+// inf / inf = NaN, ...) and div_rn's correctly rounded quotient otherwise (div_rn
+// alone gives NaN for an infinite x or d).
+__device__ __forceinline__ float div_ieee(float x, float d, float y) {
+    return __builtin_amdgcn_div_fixupf(div_rn(x, d, y), d, x);
+}
+
+// The divisor that div_rn takes for an FP8 scale s (y = fl(1/s)): s, or for an
+// infinite s (an infinite group amax) the largest finite value.  With y = 0 the
+// quotient then comes out as IEEE's x / inf: +-0 for finite x, NaN for infinite x
+// (div_rn(x, inf, 0) would give NaN for every x).
+__device__ __forceinline__ float fp8_divisor(float s) { return __builtin_fminf(s, 0x1.fffffep127f); }
 
 // E4M3 code (low byte) of a finite v with |v| < 464; nearest-even.
 // (The conversion keeps the high half of its third operand, which the mask drops:

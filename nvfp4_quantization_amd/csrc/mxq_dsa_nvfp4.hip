@@ -56,12 +56,13 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_amax(const DsaNvfp4Args a) {
     const bool live = r < a.m;
     float v[32];
     wht128_quarter(a.pe, a.ld_pe, a.d_pe, a.nope, a.ld_nope, r, live, quarter, v);
-    // max |BF16(fl(v C))| = BF16(fl(max |v| C)) (both roundings are monotone); a
-    // NaN input reaches all 128 outputs of its row, which is then left out
+    // max |BF16(fl(v C))| = BF16(fl(max |v| C)) (both roundings are monotone), NaN
+    // outputs left out (a NaN input makes all 128 of its row NaN: then m is NaN and
+    // the lane gives 0; inf - inf makes some NaN and leaves the rest infinite)
     float h0[16], h1[16];
     halves(v, h0, h1);
     const float m = __builtin_fmaxf(absmax16(h0), absmax16(h1));
-    const float lane = v[0] != v[0] ? 0.0f : round_bf16(m * k_inv_sqrt128());
+    const float lane = m != m ? 0.0f : round_bf16(m * k_inv_sqrt128());
     const float wg = wg_max(lane, red);
     if (threadIdx.x == 0) {
         __hip_atomic_store(reinterpret_cast<uint32_t*>(a.partials) + blockIdx.x, __builtin_bit_cast(uint32_t, wg),
@@ -131,32 +132,36 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_quant(const DsaNvfp4Args a) {
     const bool live = r < a.m;
     float v[32];
     wht128_quarter(a.pe, a.ld_pe, a.d_pe, a.nope, a.ld_nope, r, live, quarter, v);
-    const bool nan = v[0] != v[0];                   // the whole row is NaN
     const float c = k_inv_sqrt128();
     const u32x4 no_rnd = {0, 0, 0, 0};
     float h[2][16];
     halves(v, h[0], h[1]);
     BlockOut o[2];
-    float lane_max = 0.0f;
+    float lane_max = 0.0f;                           // (AOUT) max |y| of the lane, NaNs left out
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        const float ab = round_bf16(absmax16(h[b]) * c);             // block max |y|
+        // block max |y|, NaN when the block holds a NaN (its scale is then 0x7F)
+        const float ab = round_bf16(absmax16_nan(h[b]) * c);
         const uint32_t sc = block_code(ab, g, yg);
 #pragma unroll
         for (int i = 0; i < 16; ++i) h[b][i] = round_bf16(h[b][i] * c);
-        o[b] = encode_block<Enc::Mul>(h[b], sc, nan, tab, no_rnd);
-        lane_max = __builtin_fmaxf(lane_max, ab);
+        o[b] = encode_block<Enc::Mul>(h[b], sc, tab, no_rnd);
+        if (AOUT) {
+            float am = ab;
+            if (ab != ab) am = absmax16(h[b]);
+            lane_max = __builtin_fmaxf(lane_max, am);
+        }
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-        if (o[b].unsafe) o[b] = encode_block<Enc::Div>(h[b], o[b].scale, nan, tab, no_rnd);
+        if (o[b].unsafe) o[b] = encode_block<Enc::Div>(h[b], o[b].scale, tab, no_rnd);
     if (live) {
         *reinterpret_cast<uint4*>(a.codes + r * 64 + quarter * 16) =
             make_uint4(o[0].codes.x, o[0].codes.y, o[1].codes.x, o[1].codes.y);
         *reinterpret_cast<uint16_t*>(a.scales + r * 8 + quarter * 2) = (uint16_t)(o[0].scale | (o[1].scale << 8));
     }
     if (AOUT) {
-        const float wg = wg_max(live && !nan ? lane_max : 0.0f, red);
+        const float wg = wg_max(live ? lane_max : 0.0f, red);
         if (threadIdx.x == 0)
             __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(a.amax_out), __builtin_bit_cast(uint32_t, wg),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -54,13 +54,14 @@ __global__ __launch_bounds__(256) void k_quant_fp8_1x128(const Fp8Args a) {
     const float amax = bf16_mag(m);
     float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
     if (UE8M0) s = pow2_ceil(s);
-    const float y = 1.0f / s;
+    const float y = 1.0f / s, sd = fp8_divisor(s);
+    const bool fix = has_nan || s == __builtin_inff();   // NaN codes: NaN elements, or inf / inf
     uint32_t c[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        c[j] = e4m3_pack4(div_rn(lo_bf16(w[2 * j]), s, y), div_rn(hi_bf16(w[2 * j]), s, y),
-                          div_rn(lo_bf16(w[2 * j + 1]), s, y), div_rn(hi_bf16(w[2 * j + 1]), s, y));
-        if (has_nan) c[j] = fix_nan_codes(c[j]);
+        c[j] = e4m3_pack4(div_rn(lo_bf16(w[2 * j]), sd, y), div_rn(hi_bf16(w[2 * j]), sd, y),
+                          div_rn(lo_bf16(w[2 * j + 1]), sd, y), div_rn(hi_bf16(w[2 * j + 1]), sd, y));
+        if (fix) c[j] = fix_nan_codes(c[j]);
     }
     if (live) {
         *reinterpret_cast<uint4*>(a.q + r * a.ldq + g * 128 + part * 16) = make_uint4(c[0], c[1], c[2], c[3]);
@@ -113,13 +114,14 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
     const float amax = bf16_mag(m);
     float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
     if (UE8M0) s = pow2_ceil(s);
-    const float y = 1.0f / s;
+    const float y = 1.0f / s, sd = fp8_divisor(s);
+    const bool fix = has_nan || s == __builtin_inff();   // NaN codes: NaN values, or inf / inf
     uint32_t cd[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        cd[j] = e4m3_pack4(div_rn(lo_bf16(w[2 * j]), s, y), div_rn(hi_bf16(w[2 * j]), s, y),
-                           div_rn(lo_bf16(w[2 * j + 1]), s, y), div_rn(hi_bf16(w[2 * j + 1]), s, y));
-        if (has_nan) cd[j] = fix_nan_codes(cd[j]);
+        cd[j] = e4m3_pack4(div_rn(lo_bf16(w[2 * j]), sd, y), div_rn(hi_bf16(w[2 * j]), sd, y),
+                           div_rn(lo_bf16(w[2 * j + 1]), sd, y), div_rn(hi_bf16(w[2 * j + 1]), sd, y));
+        if (fix) cd[j] = fix_nan_codes(cd[j]);
     }
     if (live) {
         uint4* dst = reinterpret_cast<uint4*>(a.q + r * 128 + quarter * 32);

@@ -84,14 +84,15 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
         const uint32_t mo = __builtin_bit_cast(uint32_t, quad_swap<0xB1>(__builtin_bit_cast(float, m)));
         m = mo > m ? mo : m;
         const float s = block_scale<UE8M0>(bf16_mag(m));
-        const float y = 1.0f / s;
+        const float y = 1.0f / s, sd = fp8_divisor(s);
+        const bool fix = nan || s == __builtin_inff();  // 0xFF codes: NaN inputs, or inf / inf
         uint32_t c[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const uint32_t w0 = src[2 * j], w1 = src[2 * j + 1];
-            c[j] = e4m3_pack4(quotient<UE8M0>(lo_bf16(w0), s, y), quotient<UE8M0>(hi_bf16(w0), s, y),
-                              quotient<UE8M0>(lo_bf16(w1), s, y), quotient<UE8M0>(hi_bf16(w1), s, y));
-            if (nan) c[j] = nan_to_7f(c[j]);              // only NaN inputs give 0xFF
+            c[j] = e4m3_pack4(quotient<UE8M0>(lo_bf16(w0), sd, y), quotient<UE8M0>(hi_bf16(w0), sd, y),
+                              quotient<UE8M0>(lo_bf16(w1), sd, y), quotient<UE8M0>(hi_bf16(w1), sd, y));
+            if (fix) c[j] = nan_to_7f(c[j]);
         }
         if (row0 + r < a.m) {
             uint4* dst = reinterpret_cast<uint4*>(a.rq + (row0 + r) * a.rld + c0 + half * 64);
@@ -118,16 +119,17 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
         const uint32_t p0 = red[0][c], p1 = red[1][c];
         const uint32_t m0 = p0 & 0xFFFFu, m1 = p1 & 0xFFFFu;
         const float s = block_scale<UE8M0>(bf16_mag(m0 > m1 ? m0 : m1));
-        const float y = 1.0f / s;
+        const float y = 1.0f / s, sd = fp8_divisor(s);
+        const bool fix = nan || s == __builtin_inff();
         uint32_t code[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = lo_bf16(col[(half * 64 + 4 * j + e) * (2 * kRowDwords)]);
-            code[j] = e4m3_pack4(quotient<UE8M0>(v[0], s, y), quotient<UE8M0>(v[1], s, y),
-                                 quotient<UE8M0>(v[2], s, y), quotient<UE8M0>(v[3], s, y));
-            if (nan) code[j] = nan_to_7f(code[j]);
+            code[j] = e4m3_pack4(quotient<UE8M0>(v[0], sd, y), quotient<UE8M0>(v[1], sd, y),
+                                 quotient<UE8M0>(v[2], sd, y), quotient<UE8M0>(v[3], sd, y));
+            if (fix) code[j] = nan_to_7f(code[j]);
         }
         const int64_t r_first = row0 + half * 64;
         uint8_t* dst = a.cq + (c0 + c) * a.cld + r_first;

@@ -63,10 +63,16 @@ __device__ __forceinline__ float tensor_scale(float amax) {
 // E4M3(fl(fl(a * F(1/6)) / g)), yg = fl(1/g).  The quotient is clamped to 448
 // before the conversion so that it saturates: with a measured tensor amax it never
 // exceeds 448 by more than rounding, but a caller-supplied amax below the data's
-// can push it anywhere up to infinity.  A NaN quotient becomes 448 here; the NaN
-// path rewrites those blocks.
+// can push it anywhere up to infinity.  The division's special cases are IEEE's
+// (div_fixup: an infinite a over a finite g gives infinity, hence 448; a finite a
+// over an infinite g gives 0; infinite over infinite gives NaN).  The clamp keeps a
+// NaN (IEEE minimum), and the conversion turns it into the NaN code 0x7F: a block
+// whose amax is NaN gets the NaN scale with no separate test.  (a >= 0: the sign
+// bit is clear.)
 __device__ __forceinline__ uint32_t block_code(float a, float g, float yg) {
-    return e4m3_code(__builtin_fminf(div_rn(a * k_inv6(), g, yg), 448.0f));
+    const float a6 = a * k_inv6();
+    const float t = div_ieee(a6, g, yg);
+    return e4m3_code(__builtin_elementwise_minimum(t, 448.0f)) & 0x7Fu;
 }
 
 __device__ __forceinline__ uint32_t e2m1_one(float q) { return e2m1_pack2<0>(0u, q, q) & 0xFu; }
@@ -181,6 +187,36 @@ __device__ __forceinline__ float absmax16(const float (&v)[16]) {
     return __builtin_fmaxf(m3(a, b, c), m3(d, e, v[15]));
 }
 
+// max |v_i| over 16 values, NaN when any of them is NaN (IEEE maximum; a block that
+// holds a NaN thus gets the NaN scale from block_code).
+__device__ __forceinline__ float absmax16_nan(const float (&v)[16]) {
+    auto m3 = [](float a, float b, float c) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)),
+                                             __builtin_fabsf(c));
+    };
+    const float a = m3(v[0], v[1], v[2]), b = m3(v[3], v[4], v[5]), c = m3(v[6], v[7], v[8]);
+    const float d = m3(v[9], v[10], v[11]), e = m3(v[12], v[13], v[14]);
+    return __builtin_elementwise_maximum(m3(a, b, c), m3(d, e, v[15]));
+}
+
+// max |v_i| over 16 widened BF16 values, 8 three-input maxima with |.| modifiers.
+// Written out because the compiler quiets operands that come from bit operations
+// first (2 more instructions per block); NaNs give no defined result here (the
+// callers redo blocks that may hold one).
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float absmax16_raw(const float (&v)[16]) {
+    const float a = max3_abs(v[0], v[1], v[2]), b = max3_abs(v[3], v[4], v[5]), c = max3_abs(v[6], v[7], v[8]);
+    const float d = max3_abs(v[9], v[10], v[11]), e = max3_abs(v[12], v[13], v[14]);
+    const float f = max3_abs(a, b, c), h = max3_abs(d, e, v[15]);
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(f), "v"(h));
+    return r;
+}
+
 // E2M1 codes of 8 values u[0..7] (element 2i in the low nibble of byte i):
 // nearest-even of u * y (MUL), of fl(u / d), or stochastic with random bytes
 // r0 .. r0+7 of rnd.
@@ -191,7 +227,7 @@ __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, co
     if (E == Enc::Mul || E == Enc::Div) {
         float q[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = E == Enc::Mul ? u[i] * y : div_rn(u[i], d, y);
+        for (int i = 0; i < 8; ++i) q[i] = E == Enc::Mul ? u[i] * y : div_ieee(u[i], d, y);
         // each conversion writes one byte of c and keeps the others; all four are
         // written, so c starts as the bits of q[0], whose register the first
         // conversion can then overwrite in place (no zeroing instruction)
@@ -202,8 +238,8 @@ __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, co
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t c0 = e2m1_sr(div_rn(u[2 * i], d, y), rbyte(rnd, r0 + 2 * i));
-            const uint32_t c1 = e2m1_sr(div_rn(u[2 * i + 1], d, y), rbyte(rnd, r0 + 2 * i + 1));
+            const uint32_t c0 = e2m1_sr(div_ieee(u[2 * i], d, y), rbyte(rnd, r0 + 2 * i));
+            const uint32_t c1 = e2m1_sr(div_ieee(u[2 * i + 1], d, y), rbyte(rnd, r0 + 2 * i + 1));
             c |= (c0 | (c1 << 4)) << (8 * i);
         }
     }
@@ -298,16 +334,18 @@ struct BlockOut {
     float amax;           // max |value| of the block without NaNs (column: before BF16 rounding)
 };
 
-// 16 codes of one block of values u with scale code sc (nan: the block holds a NaN).
+// 16 codes of one block of values u with scale code sc <= 0x7F (0x7F: the block holds
+// a NaN).  The table entry's fourth word keeps the codes (all ones) or clears them
+// (zero: scale 0, whose blocks decode to zero, and the NaN scale 0x7F).
 template <Enc E>
-__device__ __forceinline__ BlockOut encode_block(const float (&u)[16], uint32_t sc, bool nan, const float4* tab,
+__device__ __forceinline__ BlockOut encode_block(const float (&u)[16], uint32_t sc, const float4* tab,
                                                  const u32x4& rnd) {
-    const float4 e = tab[sc & 0x7Fu];
+    const float4 e = tab[sc];
     const float d = e.x, y = E == Enc::Mul ? __builtin_fabsf(e.z) : e.y;
+    const uint32_t keep = __builtin_bit_cast(uint32_t, e.w);
     BlockOut o;
-    o.codes = make_uint2(encode8<E>(u, d, y, rnd, 0), encode8<E>(u + 8, d, y, rnd, 8));
-    if (nan || sc == 0u) o.codes = make_uint2(0u, 0u);
-    o.scale = nan ? 0x7Fu : sc;
+    o.codes = make_uint2(encode8<E>(u, d, y, rnd, 0) & keep, encode8<E>(u + 8, d, y, rnd, 8) & keep);
+    o.scale = sc;
     o.unsafe = e.z < 0.0f;
     return o;
 }
@@ -325,14 +363,17 @@ __device__ __forceinline__ BlockOut column_block(const uint4 (&p)[16][2], int j,
         v[t] = (j & 1) ? hi_signed(w, neg) : lo_signed(w, neg);
     }
     butterfly16(v);
-    const bool nan = v[0] != v[0];                   // a NaN input reaches every output
-    const float m = absmax16(v);
+    // NaN when an output is: a NaN input reaches all of them, and inf - inf (from
+    // infinite or overflowing inputs) some
+    const float m = absmax16_nan(v);
     // block amax of the column values BF16(v/4) = BF16(max |v|) / 4
     const uint32_t sc = block_code(0.25f * round_bf16(m), g_c, yg_c);
+    float m_nonan = m;                               // the block's measured amax leaves NaNs out
+    if (m != m) m_nonan = absmax16(v);
 #pragma unroll
     for (int t = 0; t < 16; ++t) v[t] = round_bf16(v[t]);
-    BlockOut o = encode_block<E>(v, sc, nan, tab_c, rnd);
-    o.amax = m;
+    BlockOut o = encode_block<E>(v, sc, tab_c, rnd);
+    o.amax = m_nonan;
     return o;
 }
 
@@ -349,21 +390,23 @@ __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, fl
         u[2 * i] = lo_bf16(P(t, i));
         u[2 * i + 1] = hi_bf16(P(t, i));
     }
-    uint32_t m;                                      // max |x| (BF16 bits)
+    uint32_t m = 0;                                  // max |x| (BF16 bits; not FAST)
+    float a;                                         // max |x|
     if (FAST) {
-        m = __builtin_bit_cast(uint32_t, absmax16(u)) >> 16;
+        a = absmax16_raw(u);                         // one of the values: BF16 already
     } else {
         uint32_t acc = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
         m = fold_pk(acc);
+        a = bf16_mag(m);
     }
     m_out = m;
-    const uint32_t sc = block_code(bf16_mag(m), g_r, yg_r);
-    // (FAST: the FP32 maximum ignores NaNs, so m never flags one; the lanes whose
-    // sub-tile holds a NaN redo their rows without FAST)
-    BlockOut o = encode_block<E>(u, sc, !FAST && m > 0x7F80u, tab_r, rnd);
-    o.amax = bf16_mag(m);                            // FAST, or no NaN: max |x| (a NaN block is
+    const uint32_t sc = block_code(a, g_r, yg_r);
+    // Not FAST, a NaN makes a NaN and so sc = 0x7F.  FAST ignores NaNs: the lanes whose
+    // sub-tile holds one redo their rows without FAST.
+    BlockOut o = encode_block<E>(u, sc, tab_r, rnd);
+    o.amax = a;                                      // FAST, or no NaN: max |x| (a NaN block is
     return o;                                        // measured again where that matters)
 }
 
@@ -453,23 +496,25 @@ __device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2]
     return amax;
 }
 
-// Scale-table entry of scale code `code` for tensor scale g: (d, fl(1/d), ym, 0)
+// Scale-table entry of scale code `code` for tensor scale g: (d, fl(1/d), ym, keep)
 // with d = fl(E4M3(code) * g), or (4d, fl(1/d)/4, ...) for column values that enter
-// unscaled (quarter); entry 0 (scale code 0 never divides) holds (g, fl(1/g)).
+// unscaled (quarter), and keep = all ones (the codes stay).  Entry 0 (scale code 0
+// never divides) holds (g, fl(1/g), fl(1/g), 0) and entry 127 (the NaN scale) zeros:
+// both clear their blocks' codes.  Entry 127's first word is free for a flag.
 __device__ __forceinline__ float4 table_entry(int code, float g, bool quarter) {
     if (code == 0) {
         const float yg = 1.0f / g;
         return make_float4(g, yg, yg, 0.0f);
     }
+    if (code == 127) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float d = e4m3_value((uint32_t)code) * g;
     float y = 1.0f / d;
     if (quarter) { d *= 4.0f; y *= 0.25f; }
-    const float ym = code == 127 ? y : product_multiplier(d, y);
-    return make_float4(d, y, ym, 0.0f);
+    return make_float4(d, y, product_multiplier(d, y), k_keep_codes());
 }
 
 // Scale tables of section s (row-wise, then column-wise), built by one wave.  Entry
-// 0's fourth value flags a direction with a scale code that has no multiplier (its
+// 127's first word flags a direction with a scale code that has no multiplier (its
 // exact ties need opposite roundings): that direction's pass then divides exactly.
 //
 // Every nonzero E4M3 value is (1 + m/8) 2^e, so the divisors d of codes that share
@@ -491,9 +536,11 @@ __device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g
         if (quarter) { d *= 4.0f; y *= 0.25f; }
         rep_ym = product_multiplier(d, y);
     }
+    float4 ent[4];
     bool none[2] = {false, false};
 #pragma unroll
-    for (int e = lane; e < 256; e += 64) {
+    for (int it = 0; it < 4; ++it) {
+        const int e = lane + 64 * it;
         const int dir = e >> 7, code = e & 127;
         if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
         const float g = dir ? g_c : g_r;
@@ -501,9 +548,8 @@ __device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g
         const uint32_t vb = __builtin_bit_cast(uint32_t, v);
         const int m = (int)((vb >> 20) & 7), ex = (int)((vb >> 23) & 0xFF) - 127;
         const float cls_ym = __shfl(rep_ym, dir * 8 + m, 64);
-        float4 entry;
         if (code == 0 || code == 127) {
-            entry = table_entry(code, g, dir == 1);
+            ent[it] = table_entry(code, g, dir == 1);
         } else {
             float d = v * g, y = 1.0f / d;
             float rd = (1.0f + (float)m * 0.125f) * g, ry = 1.0f / rd;
@@ -512,15 +558,21 @@ __device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g
             float ym;
             if (scaled) ym = __builtin_ldexpf(cls_ym, -ex);
             else ym = product_multiplier(d, y);
-            entry = make_float4(d, y, ym, 0.0f);
+            ent[it] = make_float4(d, y, ym, k_keep_codes());
         }
-        none[dir] |= entry.z < 0.0f;
-        G.tables[(s * 2 + dir) * 128 + code] = entry;
+        none[dir] |= ent[it].z < 0.0f;
     }
     const bool flag_r = __ballot(none[0]) != 0, flag_c = __ballot(none[1]) != 0;
-    if (lane == 0) {
-        if (ROW) G.tables[(s * 2) * 128].w = flag_r ? 1.0f : 0.0f;
-        if (COL) G.tables[(s * 2 + 1) * 128].w = flag_c ? 1.0f : 0.0f;
+    if (lane == 63) {                                // entries 127 (rounds 1 and 3) carry the flags
+        ent[1].x = flag_r ? 1.0f : 0.0f;
+        ent[3].x = flag_c ? 1.0f : 0.0f;
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = lane + 64 * it;
+        const int dir = e >> 7, code = e & 127;
+        if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
+        G.tables[(s * 2 + dir) * 128 + code] = ent[it];
     }
 }
 
@@ -709,7 +761,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else if (tab_c[0].w != 0.0f) {
+        } else if (tab_c[127].x != 0.0f) {
             // the section's column table has a scale code without a multiplier:
             // exact division for the whole pass
 #pragma unroll
@@ -764,7 +816,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const float4* tab_r = tab[0];
         uint8_t* const rc_tile = G.row_codes + (int64_t)T * kTileRows * (k >> 1) + (int64_t)C * (kTileCols / 2);
         const float ra = row_pass<SR, COL, 8 * W>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan,
-                                                  tab_r[0].w != 0.0f, lds_rsc + 8 * w, rc_tile);
+                                                  tab_r[127].x != 0.0f, lds_rsc + 8 * w, rc_tile);
         if (W > 1) {
             __syncthreads();
         } else {
@@ -813,13 +865,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             mf = group8_max_u32(mf);
             const float amax = bf16_mag(mf);
             const float sf = (amax > k_floor() ? amax : k_floor()) * k_inv448();
-            const float yf = 1.0f / sf;
+            const float yf = 1.0f / sf, sd = fp8_divisor(sf);
+            const bool fix = nan || sf == __builtin_inff();     // NaN codes: NaN values, or inf / inf
             uint32_t c4[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                c4[j] = e4m3_pack4(div_rn(u[4 * j], sf, yf), div_rn(u[4 * j + 1], sf, yf),
-                                   div_rn(u[4 * j + 2], sf, yf), div_rn(u[4 * j + 3], sf, yf));
-                if (nan) {
+                c4[j] = e4m3_pack4(div_rn(u[4 * j], sd, yf), div_rn(u[4 * j + 1], sd, yf),
+                                   div_rn(u[4 * j + 2], sd, yf), div_rn(u[4 * j + 3], sd, yf));
+                if (fix) {
                     // a NaN element: the conversion gives 0xFF, the format's NaN code is 0x7F
                     const uint32_t cj = c4[j];
                     const uint32_t ff = cj & (cj >> 1) & (cj >> 2) & (cj >> 3) & (cj >> 4) & (cj >> 5) &

@@ -94,13 +94,15 @@ __global__ __launch_bounds__(256) void k_swiglu_quant_fp8(const SwigluFp8Args a)
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) m = __builtin_fmaxf(m, shfl_xor_f32(m, o));
     const float s = (m > k_floor() ? m : k_floor()) * k_inv448();
-    const float y = 1.0f / s;
+    // (an h that overflowed to inf makes s infinite: finite h / inf = +-0, inf / inf NaN)
+    const float y = 1.0f / s, sd = fp8_divisor(s);
+    const bool fix = has_nan || s == __builtin_inff();
     uint32_t c[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        c[j] = e4m3_pack4(div_rn(h[4 * j], s, y), div_rn(h[4 * j + 1], s, y), div_rn(h[4 * j + 2], s, y),
-                          div_rn(h[4 * j + 3], s, y));
-        if (has_nan) c[j] = nan_codes_to_7f(c[j]);
+        c[j] = e4m3_pack4(div_rn(h[4 * j], sd, y), div_rn(h[4 * j + 1], sd, y), div_rn(h[4 * j + 2], sd, y),
+                          div_rn(h[4 * j + 3], sd, y));
+        if (fix) c[j] = nan_codes_to_7f(c[j]);
     }
     if (live) {
         *reinterpret_cast<uint4*>(a.q + r * a.ldq + g * 128 + part * 16) = make_uint4(c[0], c[1], c[2], c[3]);

@@ -286,7 +286,10 @@ void oracle_nvfp4_block(const float* v, float g, const uint8_t* rbits,
     float t  = a6 / g;
     uint8_t sc = oracle_e4m3_encode(t);
     *scale_code = sc;
-    if (sc == 0x00) {                   /* scale underflow: the block decodes to zero */
+    /* Scale underflow: the block decodes to zero.  The NaN scale (t = inf / inf: an
+     * infinite block amax over the infinite tensor scale of an infinite tensor
+     * amax) has no finite decode: its block carries zero codes, as a NaN block does. */
+    if (sc == 0x00 || sc == 0x7F) {
         for (int j = 0; j < 16; ++j) codes[j] = 0;
         return;
     }
@@ -570,7 +573,9 @@ void oracle_silu_n(const float* x, int64_t count, float* out)
 float oracle_pow2_ceil(float s)
 {
     /* the smallest power of two >= s, for a positive normal s: the exponent of s,
-     * plus one unless s is already a power of two */
+     * plus one unless s is already a power of two.  An infinite s (an infinite
+     * group amax) stays infinite. */
+    if (isinf(s)) return s;
     int e;
     float f = frexpf(s, &e);                  /* s = f * 2^e, f in [0.5, 1) */
     return (f == 0.5f) ? s : ldexpf(1.0f, e);

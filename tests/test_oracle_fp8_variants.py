@@ -104,3 +104,38 @@ def test_dsa_scale_layout(orc):
     assert np.isnan(s2[:, tokens:]).all()
     q3, s3 = orc.hadamard_quant_fp8_ex(pe, nope, orc.FP8_UE8M0, heads)
     assert not (s3.view(np.uint32) & 0x7FFFFF).any() and (s3 >= s0).all() and (s3 < 2 * s0).all()
+
+
+def test_infinite_group(orc):
+    """IEEE arithmetic as written: an infinite element makes its group's amax and
+    scale infinite (UE8M0 keeps infinity); the finite elements then encode x / inf
+    = +-0 (codes 0x00 / 0x80, signed zeros kept) and the infinite one inf / inf =
+    NaN (0x7F).  Groups without an infinity are untouched."""
+    x = np.tile(np.linspace(-3, 3, 128).astype(np.float32), (2, 1))
+    x[0, 17] = np.inf
+    xb = bf16_bits(x)
+    for opt in (0, orc.FP8_UE8M0):
+        q, s, _, _ = orc.quant_fp8_blockwise(xb, opt, columnwise=False)
+        assert np.isinf(s[0, 0]) and np.isfinite(s[1, 0])
+        want = np.where(np.signbit(x[0]), 0x80, 0x00).astype(np.uint8)
+        want[17] = 0x7F
+        np.testing.assert_array_equal(q[0], want)
+        q1, s1, _, _ = orc.quant_fp8_blockwise(xb[1:], opt, columnwise=False)
+        np.testing.assert_array_equal(q[1], q1[0])
+
+
+def test_dsa_infinite_row(orc):
+    """One infinity in a DSA row reaches all 128 rotated values as +-inf (the
+    Hadamard matrix has no zero entry): the row's group scale is infinite and every
+    code is inf / inf = NaN (0x7F); the other rows match the call without that row."""
+    tokens, heads = 4, 2
+    rng = np.random.default_rng(25)
+    v = bf16_bits(rng.standard_normal((tokens * heads, 128)))
+    v[3, 70] = 0x7F80
+    pe, nope = v[:, :64].copy(), v[:, 64:].copy()
+    q, s = orc.hadamard_quant_fp8(pe, nope)
+    assert np.isinf(s[3]) and (q[3] == 0x7F).all()
+    keep = np.arange(tokens * heads) != 3
+    q2, s2 = orc.hadamard_quant_fp8(pe[keep], nope[keep])
+    np.testing.assert_array_equal(q[keep], q2)
+    np.testing.assert_array_equal(s[keep], s2)

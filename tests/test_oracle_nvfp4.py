@@ -82,6 +82,65 @@ def test_nan_block(orc):
     assert sc == 0x7F and not codes.any()
 
 
+def test_inf_block_cases(orc):
+    """IEEE arithmetic as written (O3, O16).  An infinity over a finite tensor scale
+    makes t infinite: the scale saturates to 448 (0x7E) and the infinity encodes as
+    +6; the other values encode against d = 448 g.  Over the infinite g of an
+    infinite tensor amax, a finite block amax gives t = 0 (scale 0, zero codes) and
+    an infinite one t = inf / inf = NaN: the NaN scale 0x7F with zero codes, as for a
+    NaN block."""
+    g = np.float32(0.01)
+    blk = np.ones(16, np.float32)
+    blk[4], blk[7] = np.inf, np.float32(-2.0)
+    sc, codes = orc.nvfp4_block(blk, g)
+    assert sc == 0x7E and codes[4] == 7
+    d = np.float32(448.0) * g                      # 4.48: 1 / d = 0.22 -> 0, -2 / d = -0.45 -> -0.5
+    assert codes[0] == 0 and codes[7] == 0x9
+    gi = orc.nvfp4_global_scale(np.float32(np.inf))
+    assert np.isinf(gi) and gi > 0
+    sc, codes = orc.nvfp4_block(np.ones(16, np.float32), gi)
+    assert sc == 0 and not codes.any()
+    sc, codes = orc.nvfp4_block(blk, gi)
+    assert sc == 0x7F and not codes.any()
+
+
+def test_inf_in_column_blocks(orc):
+    """One +inf in a 16-row column block: all 16 rotated values are infinite (H16 has
+    no zero entry), so the column block's scale saturates (0x7E) and its codes are
+    +-6 with the signs of column 5 of H16 (sign mask 0).  Two +infs at rows 2 and 3
+    of a column cancel (inf - inf = NaN) in the rotated values of odd index, where
+    H16's columns 2 and 3 differ: that block gets the NaN scale 0x7F and zero codes.
+    The tensor amax (NaN left out) is measured as inf; finite supplied maxima keep g
+    finite so that the rest of the tile encodes normally, and the measured maxima
+    still come out infinite."""
+    m, k = 128, 128
+    x = np.zeros((m, k), np.float32)
+    x[:, :] = np.random.default_rng(31).standard_normal((m, k))
+    x[5, 3] = np.inf
+    x[2, 10] = x[3, 10] = np.inf
+    xb = bf16(x)
+    amax = (np.float32([8.0]), np.float32([8.0]))
+    out = orc.group_rht_quant_nvfp4(xb, [m], 0, orc.ROWWISE | orc.COLUMNWISE, amax_in=amax)
+    assert np.isinf(out.row_amax[0]) and np.isinf(out.col_amax[0])
+    cs = out.col_scales.reshape(k, m // 16)
+    cc = unpack(out.col_codes.reshape(k, m // 2))
+    H = scipy.linalg.hadamard(16)
+    assert cs[3, 0] == 0x7E
+    np.testing.assert_array_equal(cc[3, :16], np.where(H[:, 5] > 0, 0x7, 0xF))
+    assert cs[10, 0] == 0x7F and not cc[10, :16].any()
+    rs = out.row_scales.reshape(m, k // 16)
+    rc = unpack(out.row_codes.reshape(m, k // 2))
+    assert rs[5, 0] == 0x7E and rc[5, 3] == 7
+    assert rs[2, 0] == 0x7E and rs[3, 0] == 0x7E and rc[2, 10] == 7
+    # measured: g is infinite, every finite block gets scale 0 and the infinite
+    # ones the NaN scale; all codes are zero
+    meas = orc.group_rht_quant_nvfp4(xb, [m], 0, orc.ROWWISE | orc.COLUMNWISE)
+    assert np.isinf(meas.row_global[0]) and np.isinf(meas.col_global[0])
+    assert not meas.row_codes.any() and not meas.col_codes.any()
+    rs = meas.row_scales.reshape(m, k // 16)
+    assert set(np.unique(rs)) == {0, 0x7F} and rs[5, 0] == 0x7F and rs[4, 0] == 0
+
+
 def test_zero_block(orc):
     sc, codes = orc.nvfp4_block(np.zeros(16, np.float32), np.float32(0.01))
     assert sc == 0 and not codes.any()

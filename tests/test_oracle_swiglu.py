@@ -102,3 +102,18 @@ def test_swiglu_quant_hand_rows(orc):
     amax = np.float32(32.0) * np.abs(f32_of_bf16(up[1])).max()
     assert s[1, 0] == amax * np.float32(1.0 / 448.0)
     assert q[1, np.argmax(np.abs(f32_of_bf16(up[1])))] & 0x7F == 0x7E
+
+
+def test_swiglu_overflow_to_inf(orc):
+    """A product that overflows FP32 (SILU(10) * 3e38) is +inf: its group's scale is
+    infinite, the finite values encode as +-0 and the infinite one as NaN (0x7F)."""
+    n = 128
+    g = np.ones((2, n), np.float32)
+    u = np.ones((2, n), np.float32)
+    u[0, 1::2] = -1.0
+    g[0, 5], u[0, 5] = 10.0, 3.0e38
+    q, s = orc.swiglu_quant_fp8(bf16_bits(g), bf16_bits(u))
+    assert np.isinf(s[0, 0]) and np.isfinite(s[1, 0])
+    want = np.where(u[0] < 0, 0x80, 0x00).astype(np.uint8)
+    want[5] = 0x7F
+    np.testing.assert_array_equal(q[0], want)
