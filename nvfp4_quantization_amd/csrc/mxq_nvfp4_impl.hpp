@@ -219,15 +219,16 @@ __device__ __forceinline__ float absmax16_raw(const float (&v)[16]) {
 
 // E2M1 codes of 8 values u[0..7] (element 2i in the low nibble of byte i):
 // nearest-even of u * y (MUL), of fl(u / d), or stochastic with random bytes
-// r0 .. r0+7 of rnd.
+// r0 .. r0+7 of rnd.  IEEE: the quotients with IEEE's special cases (an infinite u,
+// or an overflowing quotient), which only a block whose scale saturated can meet.
 enum class Enc { Mul, Div, Sr };
-template <Enc E>
+template <Enc E, bool IEEE = false>
 __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, const u32x4& rnd, int r0) {
     uint32_t c = 0;
     if (E == Enc::Mul || E == Enc::Div) {
         float q[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = E == Enc::Mul ? u[i] * y : div_ieee(u[i], d, y);
+        for (int i = 0; i < 8; ++i) q[i] = E == Enc::Mul ? u[i] * y : IEEE ? div_ieee(u[i], d, y) : div_rn(u[i], d, y);
         // each conversion writes one byte of c and keeps the others; all four are
         // written, so c starts as the bits of q[0], whose register the first
         // conversion can then overwrite in place (no zeroing instruction)
@@ -238,8 +239,10 @@ __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, co
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t c0 = e2m1_sr(div_ieee(u[2 * i], d, y), rbyte(rnd, r0 + 2 * i));
-            const uint32_t c1 = e2m1_sr(div_ieee(u[2 * i + 1], d, y), rbyte(rnd, r0 + 2 * i + 1));
+            const float q0 = IEEE ? div_ieee(u[2 * i], d, y) : div_rn(u[2 * i], d, y);
+            const float q1 = IEEE ? div_ieee(u[2 * i + 1], d, y) : div_rn(u[2 * i + 1], d, y);
+            const uint32_t c0 = e2m1_sr(q0, rbyte(rnd, r0 + 2 * i));
+            const uint32_t c1 = e2m1_sr(q1, rbyte(rnd, r0 + 2 * i + 1));
             c |= (c0 | (c1 << 4)) << (8 * i);
         }
     }
@@ -344,7 +347,17 @@ __device__ __forceinline__ BlockOut encode_block(const float (&u)[16], uint32_t 
     const float d = e.x, y = E == Enc::Mul ? __builtin_fabsf(e.z) : e.y;
     const uint32_t keep = __builtin_bit_cast(uint32_t, e.w);
     BlockOut o;
-    o.codes = make_uint2(encode8<E>(u, d, y, rnd, 0) & keep, encode8<E>(u + 8, d, y, rnd, 8) & keep);
+    // Only a saturated scale lets a value be infinite or a quotient overflow (below it
+    // |u / d| stays near 6 or less, where div_rn is exact).  The division path takes
+    // the IEEE quotients throughout (one more operation per element, cheaper than a
+    // branch per block); stochastic rounding, where the division is on every element,
+    // branches.
+    if (E == Enc::Sr && sc == 0x7Eu) {
+        o.codes = make_uint2(encode8<E, true>(u, d, y, rnd, 0) & keep, encode8<E, true>(u + 8, d, y, rnd, 8) & keep);
+    } else {
+        constexpr bool kIeee = E == Enc::Div;
+        o.codes = make_uint2(encode8<E, kIeee>(u, d, y, rnd, 0) & keep, encode8<E, kIeee>(u + 8, d, y, rnd, 8) & keep);
+    }
     o.scale = sc;
     o.unsafe = e.z < 0.0f;
     return o;
