@@ -31,9 +31,11 @@ hipError_t launch_sel(const Nvfp4Group& g, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.total_tiles == 0) return e;
-    const unsigned grid = (unsigned)g.total_tiles;
     if (!given) {
-        hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL>), dim3(grid), dim3(64), 0, stream, g);
+        if (g.total_tiles % 4 == 0)
+            hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL, 4>), dim3((unsigned)(g.total_tiles / 4)), dim3(256), 0, stream, g);
+        else
+            hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL, 1>), dim3((unsigned)g.total_tiles), dim3(64), 0, stream, g);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

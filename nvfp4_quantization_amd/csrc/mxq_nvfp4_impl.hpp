@@ -17,8 +17,10 @@
 //                  tells which) folds the section's partials into the two tensor
 //                  scales, writes the section's scale tables and puts the counter
 //                  back to zero, so the workspace is ready for the next call.
-//   k_nvfp4_quant  re-reads the tile (usually from the Infinity Cache) and writes
-//                  every requested output.
+//   k_nvfp4_quant  re-reads the tile (partly from the Infinity Cache) and writes
+//                  every requested output: the row pass first (a row block needs
+//                  only its own row, so it starts as the rows arrive), then the
+//                  column pass (all 16 rows of each column block), then FP8.
 //
 // Scale tables: for each direction and E4M3 scale code c the quantizer divides by
 // d = fl(E4M3(c) * g).  The table holds (d, y = fl(1/d), ym): ym is a multiplier
@@ -199,24 +201,6 @@ __device__ __forceinline__ float absmax16_nan(const float (&v)[16]) {
     return __builtin_elementwise_maximum(m3(a, b, c), m3(d, e, v[15]));
 }
 
-// max |v_i| over 16 widened BF16 values, 8 three-input maxima with |.| modifiers.
-// Written out because the compiler quiets operands that come from bit operations
-// first (2 more instructions per block); NaNs give no defined result here (the
-// callers redo blocks that may hold one).
-__device__ __forceinline__ float max3_abs(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-__device__ __forceinline__ float absmax16_raw(const float (&v)[16]) {
-    const float a = max3_abs(v[0], v[1], v[2]), b = max3_abs(v[3], v[4], v[5]), c = max3_abs(v[6], v[7], v[8]);
-    const float d = max3_abs(v[9], v[10], v[11]), e = max3_abs(v[12], v[13], v[14]);
-    const float f = max3_abs(a, b, c), h = max3_abs(d, e, v[15]);
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(f), "v"(h));
-    return r;
-}
-
 // E2M1 codes of 8 values u[0..7] (element 2i in the low nibble of byte i):
 // nearest-even of u * y (MUL), of fl(u / d), or stochastic with random bytes
 // r0 .. r0+7 of rnd.  IEEE: the quotients with IEEE's special cases (an infinite u,
@@ -390,48 +374,41 @@ __device__ __forceinline__ BlockOut column_block(const uint4 (&p)[16][2], int j,
     return o;
 }
 
-// Row t of the lane: columns 16 cc .. +15 (one row-wise block).  FAST: no NaN
-// anywhere in the wave's tile, so max |x| is the FP32 maximum of the widened values;
-// otherwise packed integer maxima of |x| bits, where a NaN shows as a value above
-// 0x7F80.
-template <Enc E, bool FAST>
+// Row t of the lane: columns 16 cc .. +15 (one row-wise block).  The block maximum
+// is IEEE's: NaN when the block holds a NaN, which block_code turns into the NaN scale
+// 0x7F (whose table entry clears the codes).
+template <Enc E>
 __device__ __forceinline__ BlockOut row_block(const uint4 (&p)[16][2], int t, float g_r, float yg_r,
-                                              const float4* tab_r, const u32x4& rnd, uint32_t& m_out) {
+                                              const float4* tab_r, const u32x4& rnd) {
     float u[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         u[2 * i] = lo_bf16(P(t, i));
         u[2 * i + 1] = hi_bf16(P(t, i));
     }
-    uint32_t m = 0;                                  // max |x| (BF16 bits; not FAST)
-    float a;                                         // max |x|
-    if (FAST) {
-        a = absmax16_raw(u);                         // one of the values: BF16 already
-    } else {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = absmax_pk(acc, P(t, i));
-        m = fold_pk(acc);
-        a = bf16_mag(m);
-    }
-    m_out = m;
+    const float a = absmax16_nan(u);                 // one of the values: BF16 already
     const uint32_t sc = block_code(a, g_r, yg_r);
-    // Not FAST, a NaN makes a NaN and so sc = 0x7F.  FAST ignores NaNs: the lanes whose
-    // sub-tile holds one redo their rows without FAST.
     BlockOut o = encode_block<E>(u, sc, tab_r, rnd);
-    o.amax = a;                                      // FAST, or no NaN: max |x| (a NaN block is
-    return o;                                        // measured again where that matters)
+    o.amax = a;
+    return o;
 }
 
-// The row pass of a tile: 16 row blocks per lane.  FAST (the column pass ran and
-// reports NaN column blocks in nan): block maxima from the FP32 widened values,
-// then the lanes whose sub-tile holds a NaN redo all their rows with packed integer
-// maxima, where a NaN shows.  The scale bytes go to LDS (rsc: row r of the tile at
-// r * RSTRIDE, this lane's block at + cc), to leave later in one piece per row for
-// the whole work-group.  rc_tile: the tile's first row-code byte (wave-uniform).
-template <bool SR, bool FAST, int RSTRIDE>
-__device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2], int s, int64_t row0, int64_t c0,
-                                          int64_t r_local0, float g_r, float yg_r, const float4* tab_r, bool nan,
+// max |x| of row t of the lane without NaNs (packed integer maxima: every NaN,
+// signalling or quiet, has |bits| above 0x7F80).
+__device__ __forceinline__ float row_absmax_nonan(const uint4 (&p)[16][2], int t) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = absmax_pk_nonan(m, P(t, i));
+    return bf16_mag(m);
+}
+
+// The row pass of a tile: 16 row blocks per lane.  The scale bytes go to LDS (rsc:
+// row r of the tile at r * RSTRIDE, this lane's block at + cc), to leave later in one
+// piece per row for the whole work-group.  rc_tile: the tile's first row-code byte
+// (wave-uniform).  Returns the lane's max |x| without NaNs (used with supplied maxima).
+template <bool SR, int RSTRIDE>
+__device__ __forceinline__ float row_pass(const Nvfp4Group& G, const uint4 (&p)[16][2], int s, int64_t c0,
+                                          int64_t r_local0, float g_r, float yg_r, const float4* tab_r,
                                           bool div_mode, uint8_t* rsc, uint8_t* rc_tile) {
     const int64_t k = G.k;
     const u32x4 no_rnd = {0, 0, 0, 0};
@@ -439,71 +416,36 @@ __device__ __forceinline__ float row_pass(const Nvfp4Group& G, uint4 (&p)[16][2]
     // the lane's offset in the tile fits 32 bits (k <= 2^26), so that each row's
     // store is a uniform base plus this offset, with no vector address arithmetic
     const uint32_t lane_off = (uint32_t)lane_row * (uint32_t)(k >> 1) + (uint32_t)cc * 8u;
+    float amax = 0.0f;                               // max |x| of the lane's rows, NaNs aside
     auto put = [&](int t, const BlockOut& o) {
         uint8_t* const row_base = rc_tile + (int64_t)t * (k >> 1);
         *reinterpret_cast<uint2*>(row_base + lane_off) = o.codes;
         rsc[(lane_row + t) * RSTRIDE + cc] = (uint8_t)o.scale;
+        float am = o.amax;
+        if (am != am) am = row_absmax_nonan(p, t);  // a NaN block: its other values count
+        amax = __builtin_fmaxf(amax, am);
     };
     auto rnd_of = [&](int t) {
         return block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
     };
-    uint32_t m;
-    float amax = 0.0f;                               // max |x| of the lane's rows, NaNs aside
-    bool row_nan = false;                            // (not FAST) a block held a NaN
     if (SR && G.sr_row) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const BlockOut o = row_block<Enc::Sr, FAST>(p, t, g_r, yg_r, tab_r, rnd_of(t), m);
-            put(t, o);
-            amax = __builtin_fmaxf(amax, o.amax);
-            row_nan |= o.scale == 0x7Fu;
+            put(t, row_block<Enc::Sr>(p, t, g_r, yg_r, tab_r, rnd_of(t)));
             __builtin_amdgcn_sched_barrier(0);
         }
     } else if (div_mode) {
         // the section's row table has a scale code without a multiplier: exact division
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const BlockOut o = row_block<Enc::Div, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m);
-            put(t, o);
-            amax = __builtin_fmaxf(amax, o.amax);
-            row_nan |= o.scale == 0x7Fu;
+            put(t, row_block<Enc::Div>(p, t, g_r, yg_r, tab_r, no_rnd));
             if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
         }
     } else {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const BlockOut o = row_block<Enc::Mul, FAST>(p, t, g_r, yg_r, tab_r, no_rnd, m);
-            put(t, o);
-            amax = __builtin_fmaxf(amax, o.amax);
-            row_nan |= o.scale == 0x7Fu;
+            put(t, row_block<Enc::Mul>(p, t, g_r, yg_r, tab_r, no_rnd));
             if (t & 1) __builtin_amdgcn_sched_barrier(0);   // two rows at a time
-        }
-    }
-    const bool redo_nan = FAST ? nan : row_nan;
-    if (__ballot(redo_nan) != 0) {
-        // rare: the lane's rows again, loaded afresh one at a time, so that nothing of
-        // the main path stays live for this branch; packed integer maxima show NaNs
-        asm volatile("" ::: "memory");
-        if (redo_nan) {
-            const uint16_t* xr = G.x + row0 * k + c0;
-            amax = 0.0f;
-#pragma unroll 1
-            for (int t = 0; t < 16; ++t) {
-                uint4 q[16][2];
-                q[0][0] = *reinterpret_cast<const uint4*>(xr + t * k);
-                q[0][1] = *reinterpret_cast<const uint4*>(xr + t * k + 8);
-                if (FAST) {
-                    if (SR && G.sr_row) put(t, row_block<Enc::Sr, false>(q, 0, g_r, yg_r, tab_r, rnd_of(t), m));
-                    else put(t, row_block<Enc::Div, false>(q, 0, g_r, yg_r, tab_r, no_rnd, m));
-                }
-                uint32_t mn = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    mn = absmax_pk_nonan(mn, i == 0 ? q[0][0].x : i == 1 ? q[0][0].y : i == 2 ? q[0][0].z : q[0][0].w);
-                    mn = absmax_pk_nonan(mn, i == 0 ? q[0][1].x : i == 1 ? q[0][1].y : i == 2 ? q[0][1].z : q[0][1].w);
-                }
-                amax = __builtin_fmaxf(amax, bf16_mag(mn));
-            }
         }
     }
     return amax;
@@ -592,10 +534,12 @@ __device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g
 }  // namespace
 
 // ---------------------------------------------------------------- the kernels
-template <bool ROW, bool COL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_nvfp4_amax(const Nvfp4Group G) {
-    const int lane = threadIdx.x;
-    const int b = blockIdx.x;
+// W waves per work-group, one tile each (no interaction between them): fewer, larger
+// work-groups dispatch faster (4096 one-wave work-groups cost about 7 us to dispatch).
+template <bool ROW, bool COL, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) void k_nvfp4_amax(const Nvfp4Group G) {
+    const int lane = threadIdx.x & 63;
+    const int b = (int)blockIdx.x * W + (W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0);
     const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
     const int s = section_of(G, T);
     const uint16_t* base = G.x + ((int64_t)T * kTileRows + (lane >> 5) * 16) * G.k + (int64_t)C * kTileCols + (lane & 31) * 4;
@@ -719,12 +663,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int tb = lane >> 3, cc = lane & 7;
     const int64_t k = G.k;
     const uint16_t* base = G.x + ((int64_t)T * kTileRows + tb * 16) * k + (int64_t)C * kTileCols + cc * 16;
+    // The section's scale tables are loaded before the tile: loads complete in order,
+    // so waiting for the table does not wait for the tile, and the first pass can
+    // start on the rows that have arrived.
+    const float4* src = G.tables + s * 256;
+    const float4 te0 = ROW ? src[lane] : float4{}, te1 = ROW ? src[64 + lane] : float4{};
+    const float4 te2 = COL ? src[128 + lane] : float4{}, te3 = COL ? src[192 + lane] : float4{};
+    __builtin_amdgcn_sched_barrier(0);
     uint4 p[16][2];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         p[t][0] = *reinterpret_cast<const uint4*>(base + t * k);
         p[t][1] = *reinterpret_cast<const uint4*>(base + t * k + 8);
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     __shared__ float4 tab[2][128];
     // Column codes / scales of the tile by (column, 16-row block): 64 + 8 bytes per
@@ -735,13 +687,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ uint8_t lds_rsc[kTileRows * 8 * W];        // row scales of the work-group's tiles
     uint2* const lds_codes = lds_codes_w[w];
     uint8_t* const lds_sc = lds_sc_w[w];
-    {
-        // every wave writes the whole table (the same values): no wave reads an entry
-        // before its own write
-        const float4* src = G.tables + s * 256;
-        if (ROW) { tab[0][lane] = src[lane]; tab[0][64 + lane] = src[64 + lane]; }
-        if (COL) { tab[1][lane] = src[128 + lane]; tab[1][64 + lane] = src[192 + lane]; }
-    }
+    // every wave writes the whole table (the same values): no wave reads an entry
+    // before its own write
+    if (ROW) { tab[0][lane] = te0; tab[0][64 + lane] = te1; }
+    if (COL) { tab[1][lane] = te2; tab[1][64 + lane] = te3; }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
 
@@ -752,7 +701,38 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int64_t c0 = (int64_t)C * kTileCols + cc * 16;
     const int64_t r_local0 = (int64_t)T_local * kTileRows + tb * 16;  // section-local
     const u32x4 no_rnd = {0, 0, 0, 0};
-    bool lane_nan = !COL;                            // a NaN column block (unknown without the column pass)
+    if (ROW) {
+        const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
+        const float4* tab_r = tab[0];
+        uint8_t* const rc_tile = G.row_codes + (int64_t)T * kTileRows * (k >> 1) + (int64_t)C * (kTileCols / 2);
+        // first, so that its rows can start as their loads arrive (each row block needs
+        // one row; the column pass needs all 16)
+        const float ra = row_pass<SR, 8 * W>(G, p, s, c0, r_local0, g_r, yg_r, tab_r, tab_r[127].x != 0.0f,
+                                             lds_rsc + 8 * w, rc_tile);
+        if (W > 1) {
+            __syncthreads();
+        } else {
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+        // 128 rows x 8W bytes: W consecutive threads store one row's piece
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int i = it * 64 * W + (int)threadIdx.x;
+            const int r = i / W, part = i - r * W;
+            const uint2 v = *reinterpret_cast<const uint2*>(lds_rsc + r * 8 * W + part * 8);
+            *reinterpret_cast<uint2*>(G.row_scales + ((int64_t)T * kTileRows + r) * (k >> 4) + (int64_t)(C - w) * 8 +
+                                      part * 8) = v;
+        }
+        if (AOUT && G.amax_out_row) {
+            // supplied maxima: measure this call's for the caller's next step
+            const float w = wave_max_f32(ra);
+            if (lane == 0)
+                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_row + s), __builtin_bit_cast(uint32_t, w),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        launder(p);
+    }
 
     if (COL) {
         const float g_c = tab[1][0].x, yg_c = tab[1][0].y;
@@ -770,7 +750,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const u32x4 rnd = block_random(G.seed, G.col_off[s], (uint64_t)((c0 + j) * (int64_t)(ms >> 4) + b_local));
                 const BlockOut o = column_block<Enc::Sr>(p, j, mask, g_c, yg_c, tab_c, rnd);
                 put(j, o);
-                lane_nan |= o.scale == 0x7Fu;
                 if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -781,7 +760,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int j = 0; j < 16; ++j) {
                 const BlockOut o = column_block<Enc::Div>(p, j, mask, g_c, yg_c, tab_c, no_rnd);
                 put(j, o);
-                lane_nan |= o.scale == 0x7Fu;
                 if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
                 if (j & 1) __builtin_amdgcn_sched_barrier(0);
             }
@@ -791,7 +769,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int j = 0; j < 16; ++j) {
                 const BlockOut o = column_block<Enc::Mul>(p, j, mask, g_c, yg_c, tab_c, no_rnd);
                 put(j, o);
-                lane_nan |= o.scale == 0x7Fu;
                 if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
                 if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two columns at a time: bounds registers
             }
@@ -822,36 +799,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         launder(p);
-    }
-
-    if (ROW) {
-        const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
-        const float4* tab_r = tab[0];
-        uint8_t* const rc_tile = G.row_codes + (int64_t)T * kTileRows * (k >> 1) + (int64_t)C * (kTileCols / 2);
-        const float ra = row_pass<SR, COL, 8 * W>(G, p, s, row0, c0, r_local0, g_r, yg_r, tab_r, lane_nan,
-                                                  tab_r[127].x != 0.0f, lds_rsc + 8 * w, rc_tile);
-        if (W > 1) {
-            __syncthreads();
-        } else {
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-        }
-        // 128 rows x 8W bytes: W consecutive threads store one row's piece
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int i = it * 64 * W + (int)threadIdx.x;
-            const int r = i / W, part = i - r * W;
-            const uint2 v = *reinterpret_cast<const uint2*>(lds_rsc + r * 8 * W + part * 8);
-            *reinterpret_cast<uint2*>(G.row_scales + ((int64_t)T * kTileRows + r) * (k >> 4) + (int64_t)(C - w) * 8 +
-                                      part * 8) = v;
-        }
-        if (AOUT && G.amax_out_row) {
-            // supplied maxima: measure this call's for the caller's next step
-            const float w = wave_max_f32(ra);
-            if (lane == 0)
-                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_row + s), __builtin_bit_cast(uint32_t, w),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
 
     if (FP8) {
