@@ -307,6 +307,9 @@ def main():
     }
     if not args.no_cpu_baseline and wl.startswith("grouped"):
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows)
+        # the same oracle functions over independent (section, row-block) ranges on the
+        # host's cores (a secondary figure; cpu_baseline is the single-core one)
+        line["cpu_baseline_all_cores"] = cpu_baseline(w, args.cpu_sample_rows, threads=host_threads())
     print(json.dumps(line), flush=True)
 
 
@@ -371,8 +374,18 @@ def measured_traffic(wl, kernel):
         return None
 
 
-def cpu_baseline(w, sample_rows):
-    """The oracle as it stands (plain single-threaded C, one host core) on the same
+def host_threads() -> int:
+    """Host cores this process may use, at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(w, sample_rows, threads=1):
+    """The oracle as it stands (plain C; one host core, or `threads` workers over
+    independent section and row-block ranges of the same functions) on the same
     input: the whole workload's sections (or the sections that fit in the first
     `sample_rows` rows), all requested outputs, timed on this host."""
     import numpy as np
@@ -396,14 +409,15 @@ def cpu_baseline(w, sample_rows):
     while True:                        # repeat to about 10 s of CPU time
         oracle.group_rht_quant_nvfp4(x, sections, p["sign_mask"], p["flags"], p["seed"] or 0,
                                      p["row_offsets"][:S] if p["row_offsets"] else None,
-                                     p["col_offsets"][:S] if p["col_offsets"] else None)
+                                     p["col_offsets"][:S] if p["col_offsets"] else None, threads=threads)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= 10.0 or reps >= 10:
             break
     what = "the whole workload" if rows == total else f"its first {S} sections ({rows} of {total} rows)"
-    return {"value": round(reps * x.nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}, all requested outputs, {reps} run(s) in {dt:.1f} s on one core"}
+    where = "on one core" if threads == 1 else f"on {threads} threads"
+    return {"value": round(reps * x.nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, all requested outputs, {reps} run(s) in {dt:.1f} s {where}"}
 
 
 if __name__ == "__main__":
