@@ -45,8 +45,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(how the path would shard is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import nvfp4_quantization_amd as mxq
