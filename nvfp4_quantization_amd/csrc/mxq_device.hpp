@@ -31,7 +31,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float k_floor() { return __builtin_bit_cast(float, 0x2EDBE6FFu); }      // 1e-10
 __device__ __forceinline__ float k_inv448() { return __builtin_bit_cast(float, 0x3B124925u); }     // 1/448
 __device__ __forceinline__ float k_inv2688() { return __builtin_bit_cast(float, 0x39C30C31u); }    // 1/2688
-typedef unsigned u32x4v __attribute__((ext_vector_type(4)));   // for vector non-temporal stores
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));   // for vector non-temporal accesses
+
+// 16 bytes loaded non-temporally, for a kernel that is the data's last reader.  Not
+// a rule: it pays for wide tiles (the grouped quantize pass, the blockwise and SwiGLU
+// kernels) and costs 5-25 % on the kernels that read 256-byte rows a quarter per lane
+// (1x128 FP8 and the Hadamard paths), which keep plain loads.
+__device__ __forceinline__ uint4 nt_load16(const void* p) {
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ float k_inv6() { return __builtin_bit_cast(float, 0x3E2AAAABu); }       // 1/6
 // all-ones bit pattern (a table word used as an AND mask, never as a number)
 __device__ __forceinline__ float k_keep_codes() { return __builtin_bit_cast(float, 0xFFFFFFFFu); }

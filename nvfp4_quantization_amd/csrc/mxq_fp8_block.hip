@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
         const int j = it * 256 + t;
         const int r = j >> 4, ch = j & 15;
         uint4 w = {0, 0, 0, 0};
-        if (row0 + r < a.m) w = *reinterpret_cast<const uint4*>(a.x + (row0 + r) * a.ldx + c0 + ch * 8);
+        if (row0 + r < a.m) w = nt_load16(a.x + (row0 + r) * a.ldx + c0 + ch * 8);
         uint32_t* dst = tile + r * kRowDwords + ch * 4;
         dst[0] = w.x;
         dst[1] = w.y;

@@ -68,12 +68,12 @@ __global__ __launch_bounds__(256) void k_swiglu_quant_fp8(const SwigluFp8Args a)
 
     uint4 g0 = {0, 0, 0, 0}, g1 = {0, 0, 0, 0}, u0 = {0, 0, 0, 0}, u1 = {0, 0, 0, 0};
     if (live) {
-        const uint4* gs = reinterpret_cast<const uint4*>(a.gate + r * a.ld_gate + g * 128 + part * 16);
-        const uint4* us = reinterpret_cast<const uint4*>(a.up + r * a.ld_up + g * 128 + part * 16);
-        g0 = gs[0];
-        g1 = gs[1];
-        u0 = us[0];
-        u1 = us[1];
+        const uint16_t* gs = a.gate + r * a.ld_gate + g * 128 + part * 16;
+        const uint16_t* us = a.up + r * a.ld_up + g * 128 + part * 16;
+        g0 = nt_load16(gs);
+        g1 = nt_load16(gs + 8);
+        u0 = nt_load16(us);
+        u1 = nt_load16(us + 8);
     }
     const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
