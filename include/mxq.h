@@ -80,6 +80,11 @@ const char* mxq_version(void);
 /* Limits of the supported profile. */
 #define MXQ_ROW_ALIGN 128          /* rows per section and k: multiples of this   */
 #define MXQ_MAX_SECTIONS 256       /* split sections per grouped call             */
+/* Every array a call addresses spans fewer than MXQ_MAX_EXTENT elements: rows of
+ * length n at stride ld span (rows - 1) * ld + n, and a scale array addressed as
+ * r * s_r + c * s_c reaches index (rows - 1) * s_r + (cols - 1) * s_c.  Larger
+ * extents give MXQ_ERR_UNSUPPORTED before anything is enqueued. */
+#define MXQ_MAX_EXTENT (1LL << 40)
 
 /* ---------------------------------------------------------------------------
  * FP8 E4M3 (OCP E4M3FN), one FP32 scale per 1x128 group along k.

@@ -21,6 +21,24 @@ constexpr int64_t kMaxGroupK = 1ll << 26;   // the grouped kernels address a til
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// a * b < lim for a, b >= 0 and lim >= 1, without forming the product.
+bool product_below(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= (lim - 1) / a; }
+
+// A [rows][ld] array whose rows hold len elements spans (rows - 1) * ld + len
+// elements: below kMaxElems (rows >= 1, 0 <= len).  Bounding every array this way
+// keeps the kernels' int64 index arithmetic exact.
+bool extent_ok(int64_t rows, int64_t ld, int64_t len) {
+    return len < kMaxElems && product_below(rows - 1, ld, kMaxElems - len);
+}
+
+// The largest index of a [rows][cols] array addressed as r * s_r + c * s_c is below
+// kMaxElems (rows, cols >= 1; s_r, s_c >= 0).
+bool index2_ok(int64_t rows, int64_t s_r, int64_t cols, int64_t s_c) {
+    if (!product_below(rows - 1, s_r, kMaxElems) || !product_below(cols - 1, s_c, kMaxElems)) return false;
+    return (rows - 1) * s_r < kMaxElems - (cols - 1) * s_c;
+}
+
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 thread_local hipEvent_t t_marks[3] = {nullptr, nullptr, nullptr};
@@ -68,7 +86,9 @@ mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int
     if (m == 0) return MXQ_OK;
     if (!x_bf16 || !q_e4m3 || !scales) return MXQ_ERR_INVALID_ARGUMENT;
     if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4)) return MXQ_ERR_MISALIGNED;
-    if (m > kMaxRows || m * k >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    if (m > kMaxRows || !extent_ok(m, ldx, k) || !extent_ok(m, ldq, k) ||
+        !index2_ok(m, scale_stride_row, k / 128, scale_stride_group))
+        return MXQ_ERR_UNSUPPORTED;
     const int64_t blocks = ceil_div(m * (k / 128), 32);
     if (blocks * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
     mxq::Fp8Args a{x_bf16, q_e4m3, scales, m, k, ldx, ldq, scale_stride_row, scale_stride_group};
@@ -85,7 +105,9 @@ mxq_status mxq_swiglu_quant_fp8(const uint16_t* gate_bf16, int64_t ld_gate, cons
     if (!gate_bf16 || !up_bf16 || !q_e4m3 || !scales) return MXQ_ERR_INVALID_ARGUMENT;
     if (!aligned(gate_bf16, 16) || !aligned(up_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4))
         return MXQ_ERR_MISALIGNED;
-    if (m > kMaxRows || m * n >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    if (m > kMaxRows || !extent_ok(m, ld_gate, n) || !extent_ok(m, ld_up, n) || !extent_ok(m, ldq, n) ||
+        !index2_ok(m, scale_stride_row, n / 128, scale_stride_group))
+        return MXQ_ERR_UNSUPPORTED;
     if (ceil_div(m * (n / 128), 32) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
     mxq::SwigluFp8Args a{gate_bf16, up_bf16, q_e4m3, scales, m, n, ld_gate, ld_up, ldq, scale_stride_row,
                          scale_stride_group};
@@ -105,7 +127,8 @@ mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_p
     if ((d_pe > 0 && !aligned(pe, 16)) || (d_pe < 128 && !aligned(nope, 16)) || !aligned(q_e4m3, 16) ||
         !aligned(scales, 4))
         return MXQ_ERR_MISALIGNED;
-    if (m > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    if (m > kMaxRows || (d_pe > 0 && !extent_ok(m, ld_pe, d_pe)) || (d_pe < 128 && !extent_ok(m, ld_nope, 128 - d_pe)))
+        return MXQ_ERR_UNSUPPORTED;
     if (ceil_div(m, 64) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
     mxq::DsaArgs a{pe, nope, q_e4m3, scales, ld_pe, ld_nope, m, d_pe, 1, 1, 0};
     return mxq::launch_hadamard_quant_fp8(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
@@ -127,7 +150,9 @@ mxq_status mxq_hadamard_quant_fp8_ex(const uint16_t* pe, int64_t ld_pe, int32_t 
     if ((d_pe > 0 && !aligned(pe, 16)) || (d_pe < 128 && !aligned(nope, 16)) || !aligned(q_e4m3, 16) ||
         !aligned(scales, 4))
         return MXQ_ERR_MISALIGNED;
-    if (m > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    if (m > kMaxRows || (d_pe > 0 && !extent_ok(m, ld_pe, d_pe)) || (d_pe < 128 && !extent_ok(m, ld_nope, 128 - d_pe)) ||
+        !index2_ok(heads < m ? ceil_div(m, heads) : 1, scale_stride_token, heads < m ? heads : m, scale_stride_head))
+        return MXQ_ERR_UNSUPPORTED;
     if (ceil_div(m, 64) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
     mxq::DsaArgs a{pe, nope, q_e4m3, scales, ld_pe, ld_nope, m, d_pe, heads, scale_stride_token, scale_stride_head};
     return mxq::launch_hadamard_quant_fp8(a, static_cast<hipStream_t>(stream), (options & MXQ_FP8_UE8M0) != 0) ==
@@ -160,7 +185,13 @@ mxq_status mxq_quant_fp8_blockwise(const uint16_t* x_bf16, int64_t m, int64_t k,
     if (!aligned(x_bf16, 16) || (rowwise && (!aligned(rowwise->codes, 16) || !aligned(rowwise->scales, 4))) ||
         (columnwise && (!aligned(columnwise->codes, 16) || !aligned(columnwise->scales, 4))))
         return MXQ_ERR_MISALIGNED;
-    if (m > kMaxRows || m * k >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    if (m > kMaxRows || !extent_ok(m, ldx, k)) return MXQ_ERR_UNSUPPORTED;
+    if (rowwise && (!extent_ok(m, rowwise->ld, k) ||
+                    !index2_ok(m, rowwise->scale_stride_a, k / 128, rowwise->scale_stride_b)))
+        return MXQ_ERR_UNSUPPORTED;
+    if (columnwise && (!extent_ok(k, columnwise->ld, m) ||
+                       !index2_ok(k, columnwise->scale_stride_a, ceil_div(m, 128), columnwise->scale_stride_b)))
+        return MXQ_ERR_UNSUPPORTED;
     const bool ue8m0 = (options & MXQ_FP8_UE8M0) != 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!columnwise) {                                    // row-wise alone: the streaming kernel
@@ -208,6 +239,8 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
     if (!global_scale) return MXQ_ERR_INVALID_ARGUMENT;
     if (!aligned(global_scale, 4) || !aligned(amax_in, 4) || !aligned(amax_out, 4)) return MXQ_ERR_MISALIGNED;
     if (m > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    if (m > 0 && ((d_pe > 0 && !extent_ok(m, ld_pe, d_pe)) || (d_pe < 128 && !extent_ok(m, ld_nope, 128 - d_pe))))
+        return MXQ_ERR_UNSUPPORTED;
     if (m > 0) {
         if ((d_pe > 0 && !pe) || (d_pe < 128 && !nope) || !codes || !block_scales || !workspace)
             return MXQ_ERR_INVALID_ARGUMENT;
@@ -240,6 +273,7 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
 size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k, int64_t num_sections,
                                                 uint32_t flags) {
     if (total_rows < 0 || k <= 0 || num_sections <= 0) return 0;
+    if (total_rows > kMaxRows || k > kMaxGroupK) return 0;         // outside the supported profile
     if (!(flags & (MXQ_ROWWISE | MXQ_COLUMNWISE))) return 0;
     // counters and scale tables of one launch group, then one 8-byte partial per
     // 128 x 128 tile of the largest group (bounded by all rows)

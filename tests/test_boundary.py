@@ -256,3 +256,31 @@ def test_dsa_fp8_ex_argument_errors(L):
     assert ex(d_pe=60, ld_pe=60, ld_nope=68) == MISALIGNED
     assert ex(s=A + 2) == MISALIGNED
     assert ex(m=0) == OK
+    assert ex(st=1 << 40) == UNSUPPORTED                            # scale index 3 * 2^40
+    assert ex(heads=1 << 62, sh=1 << 40) == UNSUPPORTED             # no overflow forming the token count
+
+
+def test_extent_limits(L):
+    """No array a call addresses may span 2^40 or more elements (MXQ_MAX_EXTENT):
+    such calls are rejected without forming an overflowing product, and the grouped
+    size query answers 0 beyond the supported profile.  Only rejected calls are made
+    here: an accepted one would launch on the fake addresses."""
+    big = 1 << 40
+    assert fp8(L, k=1 << 62, ldx=1 << 62, ldq=1 << 62) == UNSUPPORTED    # m * k would overflow int64
+    assert fp8(L, ldx=big) == UNSUPPORTED
+    edge = (big - 256) // 3                                              # 3 rows of stride edge + 256 = 2^40
+    assert edge % 8 == 0 and 3 * edge + 256 == big
+    assert fp8(L, ldx=edge) == UNSUPPORTED
+    assert fp8(L, ldq=big) == UNSUPPORTED
+    assert fp8(L, sr=big) == UNSUPPORTED
+    assert fp8(L, sg=big) == UNSUPPORTED
+    assert swiglu(L, ldu=big) == UNSUPPORTED
+    assert swiglu(L, sg=big) == UNSUPPORTED
+    assert dsa(L, ld_nope=big) == UNSUPPORTED
+    assert dsa(L, ld_pe=big) == UNSUPPORTED
+    assert dsa4(L, ld_pe=big) == UNSUPPORTED
+    assert blockwise(L, col=(A, big, A, 2, 1)) == UNSUPPORTED
+    assert blockwise(L, row=(A, 256, A, big, 1)) == UNSUPPORTED
+    assert blockwise(L, col=(A, 256, A, 2, big)) == UNSUPPORTED
+    q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
+    assert q(1 << 40, 4096, 8, 3) == 0 and q(16384, 1 << 40, 8, 3) == 0
