@@ -343,24 +343,63 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
+def hip_runtime():
+    """The HIP runtime this process already runs on (torch's copy), opened without
+    loading another, for the event flags torch does not expose."""
+    import ctypes
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        raise RuntimeError("the HIP runtime is not loaded")
+    hip = ctypes.CDLL(path, mode=os.RTLD_NOLOAD | ctypes.RTLD_GLOBAL)
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000    # hip_runtime_api.h: no cache write-back at the event
+
+
 def kernel_times(mxq, torch, calls, n_sets, K, stream, names):
-    """Average duration (us) of each of the two kernels (`names`) of an NVFP4 call
-    over K steady-state calls, between HIP events the library records on the call's
-    stream just before, between and after them."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for trio in ev:
-        for e in trio:
-            e.record(stream)                                  # creates the event
-    torch.cuda.synchronize()
+    """Average duration (us) of each of the two kernels (`names`) of a call over K
+    steady-state calls, between HIP events the library records on the call's stream
+    just before, between and after them.  The events skip the system-scope fence
+    (hipEventDisableSystemFence): with it, each event writes back and invalidates
+    the caches and adds 3-4 us to the interval it closes."""
+    import ctypes
+    hip = hip_runtime()
+    ev = []
     try:
-        for i in range(K):
-            mxq.mxq_set_launch_marks(*ev[i])
-            calls[i % n_sets]()
+        for _ in range(3 * K):
+            h = ctypes.c_void_p()
+            if hip.hipEventCreateWithFlags(ctypes.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            ev.append(h)
+        torch.cuda.synchronize()
+        try:
+            for i in range(K):
+                mxq.mxq_set_launch_marks(*(e.value for e in ev[3 * i:3 * i + 3]))
+                calls[i % n_sets]()
+        finally:
+            mxq.mxq_set_launch_marks()
+        torch.cuda.synchronize()
+        t = ctypes.c_float()
+
+        def elapsed(a, b):
+            if hip.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            return t.value
+        first = sum(elapsed(ev[3 * i], ev[3 * i + 1]) for i in range(K)) / K
+        second = sum(elapsed(ev[3 * i + 1], ev[3 * i + 2]) for i in range(K)) / K
     finally:
-        mxq.mxq_set_launch_marks()
-    torch.cuda.synchronize()
-    first = sum(a.elapsed_time(b) for a, b, _ in ev) / K
-    second = sum(b.elapsed_time(c) for _, b, c in ev) / K
+        for e in ev:
+            hip.hipEventDestroy(e)
     return {names[0]: round(first * 1e3, 2), names[1]: round(second * 1e3, 2)}
 
 
