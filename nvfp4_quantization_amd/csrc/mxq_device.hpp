@@ -32,6 +32,7 @@ __device__ __forceinline__ float k_floor() { return __builtin_bit_cast(float, 0x
 __device__ __forceinline__ float k_inv448() { return __builtin_bit_cast(float, 0x3B124925u); }     // 1/448
 __device__ __forceinline__ float k_inv2688() { return __builtin_bit_cast(float, 0x39C30C31u); }    // 1/2688
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));   // for vector non-temporal accesses
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 
 // 16 bytes loaded non-temporally, for a kernel that is the data's last reader.  Not
 // a rule: it pays for wide tiles (the grouped quantize pass, the blockwise and SwiGLU

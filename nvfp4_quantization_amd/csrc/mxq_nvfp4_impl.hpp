@@ -727,14 +727,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
         }
-        // 128 rows x 8W bytes: W consecutive threads store one row's piece
+        // 128 rows x 8W bytes: W consecutive threads store one row's piece.  Pieces of 32
+        // bytes (W = 4) go non-temporally like the codes (1 us faster in this kernel);
+        // 8-byte pieces were much slower that way, as the column scales showed.
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int i = it * 64 * W + (int)threadIdx.x;
             const int r = i / W, part = i - r * W;
             const uint2 v = *reinterpret_cast<const uint2*>(lds_rsc + r * 8 * W + part * 8);
-            *reinterpret_cast<uint2*>(G.row_scales + ((int64_t)T * kTileRows + r) * (k >> 4) + (int64_t)(C - w) * 8 +
-                                      part * 8) = v;
+            uint8_t* const dst = G.row_scales + ((int64_t)T * kTileRows + r) * (k >> 4) + (int64_t)(C - w) * 8 + part * 8;
+            if (W >= 4)
+                __builtin_nontemporal_store(u32x2v{v.x, v.y}, reinterpret_cast<u32x2v*>(dst));
+            else
+                *reinterpret_cast<uint2*>(dst) = v;
         }
         if (AOUT && G.amax_out_row) {
             // supplied maxima: measure this call's for the caller's next step
@@ -798,7 +803,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             // Non-temporal: the codes (two thirds of the output bytes) stream out during
             // this kernel instead of staying dirty in the caches, where the next call's
             // amax kernel would have to write them back (-5 us there, +3 us here for
-            // C3).  The scales, small scattered pieces, are slower this way.
+            // C3).  The column scales, 8-byte pieces, are slower this way.
             __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w},
                                         reinterpret_cast<u32x4v*>(codes_s + ((int64_t)C * kTileCols + col) * (ms >> 1) +
                                                                   T_local * 64 + part * 16));
