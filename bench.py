@@ -10,7 +10,8 @@ configuration the headline metric is quoted on).  The timed steps run back to ba
 and cycle over several copies of the input and outputs, together far larger than
 the 256 MB Infinity Cache, so each call reads its input from HBM and pays for the
 write-back of earlier calls' outputs, as a stream of calls would; ms_per_step is
-the HIP-event time of the whole run on the kernels' stream divided by the steps.
+the HIP-event time of the whole run on the kernels' stream divided by the steps
+(two events around the K calls, nothing enqueued between them).
 Secondary figures: a single call after a 1 GiB read has cleared the caches of the
 input (without leaving dirty lines behind), and back-to-back calls on one input
 (warm caches).  Prints ONE JSON line.
