@@ -22,6 +22,7 @@ namespace mxq {
 namespace {
 
 constexpr int kRowDwords = 65;        // 128 BF16 + 2 of padding
+constexpr int kCodeDwords = 36;       // a column's 128 codes + 16 bytes of padding (16-byte aligned rows)
 
 // Bytes equal to 0xFF (the conversion's code for a NaN input) become 0x7F.
 __device__ __forceinline__ uint32_t nan_to_7f(uint32_t c) {
@@ -46,7 +47,7 @@ __device__ __forceinline__ float block_scale(float amax) {
 
 template <bool ROW, bool COL, bool UE8M0>
 __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs a) {
-    __shared__ uint32_t tile[128 * kRowDwords];
+    __shared__ __attribute__((aligned(16))) uint32_t tile[128 * kRowDwords];
     __shared__ uint32_t red[2][128];
     const int t = threadIdx.x;
     const int64_t n_ct = a.k >> 7;
@@ -133,6 +134,26 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
         }
         const int64_t r_first = row0 + half * 64;
         uint8_t* dst = a.cq + (c0 + c) * a.cld + r_first;
+        if (row0 + 128 <= a.m) {
+            // A whole row block (uniform over the work-group): the 128 x 128 codes go
+            // through LDS (over the input tile, which both passes have read by the
+            // barrier), so that 8 lanes store each column's 128 bytes as one line
+            // instead of every lane storing 16-byte pieces of its own column.
+            if (half == 0) a.cs[(c0 + c) * a.csc + rb * a.csb] = s;
+            __syncthreads();
+            uint32_t* stage = tile + c * kCodeDwords + half * 16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint4*>(stage + 4 * q) = make_uint4(code[4 * q], code[4 * q + 1], code[4 * q + 2], code[4 * q + 3]);
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int col = it * 32 + (t >> 3), part = t & 7;
+                const uint4 v = *reinterpret_cast<const uint4*>(tile + col * kCodeDwords + part * 4);
+                *reinterpret_cast<uint4*>(a.cq + (c0 + col) * a.cld + row0 + part * 16) = v;
+            }
+            return;
+        }
         if (r_first + 64 <= a.m) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
