@@ -69,6 +69,10 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
     }
     __syncthreads();
 
+    // A whole row block with both outputs: the row codes, too, leave through LDS once
+    // the column pass is done with it (kept in rc until then).
+    const bool stage_rows = ROW && COL && row0 + 128 <= a.m;
+    uint32_t rc[16];
     if (ROW) {
         const int r = t >> 1, half = t & 1;
         const uint32_t* src = tile + r * kRowDwords + half * 32;
@@ -95,7 +99,11 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
                               quotient<UE8M0>(lo_bf16(w1), sd, y), quotient<UE8M0>(hi_bf16(w1), sd, y));
             if (fix) c[j] = nan_to_7f(c[j]);
         }
-        if (row0 + r < a.m) {
+        if (stage_rows) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) rc[j] = c[j];
+            if (half == 0) a.rs[(row0 + r) * a.rsr + ct * a.rsg] = s;
+        } else if (row0 + r < a.m) {
             uint4* dst = reinterpret_cast<uint4*>(a.rq + (row0 + r) * a.rld + c0 + half * 64);
 #pragma unroll
             for (int q = 0; q < 4; ++q) dst[q] = make_uint4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
@@ -151,6 +159,20 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
                 const int col = it * 32 + (t >> 3), part = t & 7;
                 const uint4 v = *reinterpret_cast<const uint4*>(tile + col * kCodeDwords + part * 4);
                 *reinterpret_cast<uint4*>(a.cq + (c0 + col) * a.cld + row0 + part * 16) = v;
+            }
+            if (stage_rows) {
+                __syncthreads();                                  // the column lines are read
+                uint32_t* rstage = tile + (t >> 1) * kCodeDwords + (t & 1) * 16;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint4*>(rstage + 4 * q) = make_uint4(rc[4 * q], rc[4 * q + 1], rc[4 * q + 2], rc[4 * q + 3]);
+                __syncthreads();
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int row = it * 32 + (t >> 3), part = t & 7;
+                    const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kCodeDwords + part * 4);
+                    *reinterpret_cast<uint4*>(a.rq + (row0 + row) * a.rld + c0 + part * 16) = v;
+                }
             }
             return;
         }
