@@ -19,9 +19,6 @@ namespace mxq {
 namespace {
 
 __device__ __forceinline__ float f32(uint32_t b) { return __builtin_bit_cast(float, b); }
-// 2^j for an integer j in [-126, 127].
-__device__ __forceinline__ float pow2i(int j) { return f32((uint32_t)(j + 127) << 23); }
-
 // A NaN x stays NaN through every step (the clamps keep it, and it reaches p).
 __device__ __forceinline__ float exp_stated(float x) {
     x = x > 128.0f ? 128.0f : x;              // e^128 and e^-128 are beyond binary32
@@ -37,9 +34,11 @@ __device__ __forceinline__ float exp_stated(float x) {
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    const int ki = (int)k;
-    const int k1 = (int)__builtin_floorf(k * 0.5f), k2 = ki - k1;
-    return (p * pow2i(k1)) * pow2i(k2);
+    // The stated two halves, (p 2^k1) 2^k2 with k1 = floor(k / 2): for |k| <= 185 and
+    // p in [0.70, 1.42] the first product is an exact normal number, so the pair
+    // rounds once, to the binary32 nearest p 2^k (overflowing to infinity), which is
+    // what one ldexp gives.
+    return __builtin_amdgcn_ldexpf(p, (int)k);
 }
 
 __device__ __forceinline__ float silu(float g) {
