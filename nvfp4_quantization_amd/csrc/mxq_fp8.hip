@@ -83,8 +83,10 @@ hipError_t launch_quant_fp8_1x128(const Fp8Args& a, hipStream_t stream, bool ue8
 // elements each.  Butterfly stages h = 1..16 run inside a lane; h = 32 and 64
 // pair lanes (q ^ 1) and (q ^ 2).  A 256-thread block covers 64 rows.  UE8M0:
 // the scale is rounded up to a power of two.
+constexpr int kStageDwords = 36;      // a row's 128 codes + 16 bytes of padding
 template <bool UE8M0>
 __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t stage[64 * kStageDwords];
     const int quarter = threadIdx.x & 3;
     const int64_t r = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
     const bool live = r < a.m;
@@ -123,12 +125,25 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_fp8(const DsaArgs a) {
                            div_rn(lo_bf16(w[2 * j + 1]), sd, y), div_rn(hi_bf16(w[2 * j + 1]), sd, y));
         if (fix) cd[j] = fix_nan_codes(cd[j]);
     }
+    // The work-group's 64 x 128 codes leave through LDS, so that 8 lanes store each
+    // row's 128 bytes as one line (the computing lanes hold 32 bytes each).  They are
+    // stored non-temporally: they stream out now instead of being written back from
+    // the caches during the next call's reads (3 % faster in steady state).
+    uint32_t* st = stage + (threadIdx.x >> 2) * kStageDwords + quarter * 8;
+    *reinterpret_cast<uint4*>(st) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
+    *reinterpret_cast<uint4*>(st + 4) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = it * 256 + (int)threadIdx.x;
+        const int row = idx >> 3, part = idx & 7;
+        const int64_t rr = (int64_t)blockIdx.x * 64 + row;
+        if (rr < a.m) {
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kStageDwords + part * 4);
+            __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(a.q + rr * 128 + part * 16));
+        }
+    }
     if (live) {
-        uint4* dst = reinterpret_cast<uint4*>(a.q + r * 128 + quarter * 32);
-        // non-temporal: the codes stream out now instead of being written back from
-        // the caches during the next call's reads (3 % faster in steady state)
-        __builtin_nontemporal_store(u32x4v{cd[0], cd[1], cd[2], cd[3]}, reinterpret_cast<u32x4v*>(dst));
-        __builtin_nontemporal_store(u32x4v{cd[4], cd[5], cd[6], cd[7]}, reinterpret_cast<u32x4v*>(dst + 1));
         if (quarter == 0) {
             const int64_t token = r / a.heads, head = r - token * a.heads;
             a.scales[token * a.stride_token + head * a.stride_head] = s;
