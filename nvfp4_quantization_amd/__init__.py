@@ -390,11 +390,23 @@ def alloc_workspace(total_rows: int, k: int, num_sections: int, flags: int, devi
     return torch.zeros((max(n, 256),), dtype=torch.uint8, device=device)
 
 
+WORKSPACE_STATUS = WORKSPACE_COUNTERS * WORKSPACE_COUNTER_STRIDE   # byte offset of the error word
+WORKSPACE_SLOTS = WORKSPACE_STATUS + 512 + 32 * 2 * 128 * 16          # the single-read form's partial words
+WORKSPACE_SLOTS_BYTES = 4 * 1024
+
+
 def workspace_counters_clear(workspace: torch.Tensor) -> bool:
-    """After a finished call: True when every section counter is back at zero."""
+    """After a finished call: True when every section counter is back at zero, and so
+    are the single-read form's error word and partial words."""
     n = min(workspace.numel(), WORKSPACE_COUNTERS * WORKSPACE_COUNTER_STRIDE)
     words = workspace[:n].view(torch.int32)[:: WORKSPACE_COUNTER_STRIDE // 4]
-    return bool((words == 0).all().item())
+    if not bool((words == 0).all().item()):
+        return False
+    if workspace.numel() > WORKSPACE_STATUS and int(workspace[WORKSPACE_STATUS:WORKSPACE_STATUS + 4]
+                                                    .view(torch.int32).item()) != 0:
+        return False
+    slots = workspace[WORKSPACE_SLOTS:WORKSPACE_SLOTS + WORKSPACE_SLOTS_BYTES]
+    return bool((slots == 0).all().item())
 
 
 class GroupedNVFP4:

@@ -12,6 +12,15 @@ Compiled in-tree with hipcc; always rebuilds.  Flags:
                       kept loop would index register arrays dynamically and move
                       them to scratch memory
 FP32 denormals are kept and FP32 division is correctly rounded (hipcc defaults).
+The single-read kernels (mxq_nvfp4_fused_*.hip) are also built with
+  -mllvm -disable-machine-licm
+                      their per-item loop would otherwise keep loop-invariant lane
+                      addresses live through the quantizing passes, whose registers
+                      are at the limit, and spill a third of the tile
+A second library, _build/libmxq_defer0.so, is the same code with the single-read
+kernels built with MXQ_FUSED_DEFER_TICKS=0: every waiting item gives up at once and
+leaves its tiles to its section's last item, which the deferral test checks against
+the oracle (the condition only a device short of room produces otherwise).
 """
 import os
 import shutil
@@ -24,11 +33,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT, "libmxq.so")
+LIB_DEFER0 = os.path.join(OUT, "libmxq_defer0.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["mxq_fp8.hip", "mxq_fp8_block.hip", "mxq_swiglu_fp8.hip", "mxq_dsa_nvfp4.hip", "mxq_nvfp4.hip", "mxq_nvfp4_quant_rne.hip", "mxq_nvfp4_quant_sr.hip",
-               "mxq_nvfp4_quant_rne_aout.hip", "mxq_nvfp4_quant_sr_aout.hip"]
+               "mxq_nvfp4_quant_rne_aout.hip", "mxq_nvfp4_quant_sr_aout.hip",
+               "mxq_nvfp4_fused_rne.hip", "mxq_nvfp4_fused_sr.hip"]
 HOST_SOURCES = ["mxq_api.cpp"]
+FUSED_SOURCES = ("mxq_nvfp4_fused_rne.hip", "mxq_nvfp4_fused_sr.hip")
+EXTRA = {src: ["-mllvm", "-disable-machine-licm"] for src in FUSED_SOURCES}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Werror", "-I", "/opt/rocm/include",
           "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -61,7 +74,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(OUT, src + ".o")
-        cmd = [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd += ["-save-temps=obj"]
         jobs.append(cmd)
@@ -70,11 +83,23 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
         obj = os.path.join(OUT, src + ".o")
         jobs.append([cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # the deferral test build: the single-read units again, waits of zero ticks
+    defer_objs = []
+    for src in FUSED_SOURCES:
+        obj = os.path.join(OUT, src + ".defer0.o")
+        jobs.append([cc, *COMMON, *DEVICE, *EXTRA.get(src, []), "-DMXQ_FUSED_DEFER_TICKS=0", "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+        defer_objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    fused_objs = {os.path.join(OUT, src + ".o") for src in FUSED_SOURCES}
+    tmp = LIB_DEFER0 + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp,
+          *[o for o in objs if o not in fused_objs], *defer_objs], verbose)
+    os.replace(tmp, LIB_DEFER0)
     return LIB
 
 

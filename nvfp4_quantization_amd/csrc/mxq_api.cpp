@@ -275,8 +275,9 @@ size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k, i
     if (total_rows < 0 || k <= 0 || num_sections <= 0) return 0;
     if (total_rows > kMaxRows || k > kMaxGroupK) return 0;         // outside the supported profile
     if (!(flags & (MXQ_ROWWISE | MXQ_COLUMNWISE))) return 0;
-    // counters and scale tables of one launch group, then one 8-byte partial per
-    // 128 x 128 tile of the largest group (bounded by all rows)
+    // counters, status line, scale tables and the single-read form's partial words
+    // of one launch group, then one 8-byte partial per 128 x 128 tile of the largest
+    // group (bounded by all rows)
     const int64_t tiles = (total_rows / 128) * ceil_div(k, 128);
     return (size_t)round256(mxq::kPartialsOffset + 8 * tiles);
 }
@@ -407,7 +408,9 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
             g.amax_out_col = (col && amax->col_out) ? amax->col_out + s0 : nullptr;
         }
         g.total_tiles = (int32_t)(tt * n_ct);
-        if (mxq::launch_nvfp4_group(g, flags, st) != hipSuccess) return MXQ_ERR_HIP;
+        uint32_t* const slots = reinterpret_cast<uint32_t*>(ws + mxq::kSlotsOffset);
+        uint32_t* const status = reinterpret_cast<uint32_t*>(ws + mxq::kStatusOffset);
+        if (mxq::launch_nvfp4_group(g, flags, slots, status, st) != hipSuccess) return MXQ_ERR_HIP;
         row0 += rows_group;
     }
     return MXQ_OK;

@@ -129,7 +129,8 @@ struct Nvfp4Group {
     float* amax_out_row;
     float* amax_out_col;
 };
-hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
+// slots: the single-read form's partial words (zero between calls); status: its error word.
+hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, uint32_t* slots, uint32_t* status, hipStream_t stream);
 // Launch marks of the calling thread (mxq_set_launch_marks): records mark i
 // (0 before the first kernel, 1 between the scale and quantize kernels, 2 after)
 // on the stream when marks are set; hipSuccess otherwise.
@@ -141,17 +142,56 @@ hipError_t launch_quant_sr(const Nvfp4Group& g, uint32_t flags, hipStream_t stre
 hipError_t launch_quant_rne_aout(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
 hipError_t launch_quant_sr_aout(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);
 
+// The single-read form of a launch group (mxq_nvfp4_fused.hpp): one 4-wave
+// work-group per item (4 adjacent column tiles of one token tile).  Sections are
+// processed in the order `order`, the items of position i being istart[i] ..
+// istart[i + 1] - 1.
+constexpr int kFusedMaxItems = 1024;           // items of a launch group (partial words, deferred lists)
+struct Nvfp4Fused {
+    uint32_t* slots;                  // workspace: one partial word per item, zero between calls
+    uint32_t* err;                    // workspace: set to 1 when a wait gave up
+    int32_t n_items;
+    int32_t n_cgroups;                // items per token tile: k / 512
+    int32_t n_order;                  // non-empty sections of the group
+    int32_t istart[kGroupSections + 1];
+    uint8_t order[kGroupSections];
+};
+// A partial word: bit 31 present, bits 16..30 the BF16 bits of the item's column
+// maximum / 4, bits 0..14 those of its row maximum, bit 15 deferred.
+constexpr uint32_t kSlotPresent = 0x80000000u;
+constexpr uint32_t kSlotDeferred = 0x00008000u;
+// Waits of the single-read kernel, in ticks of the 100 MHz constant clock: an item
+// defers after kDeferTicks (about 0.66 ms; a call takes tens of microseconds), and
+// the last item's wait for its section's partials (which always ends) gives up
+// after kWaitTicks (about 21 ms) and sets the error word.
+#ifndef MXQ_FUSED_DEFER_TICKS
+#define MXQ_FUSED_DEFER_TICKS (1ull << 16)
+#endif
+constexpr uint64_t kDeferTicks = MXQ_FUSED_DEFER_TICKS;   // 0 in the deferral test build only
+constexpr uint64_t kWaitTicks = 1ull << 21;
+hipError_t launch_fused_rne(const Nvfp4Group& g, const Nvfp4Fused& f, uint32_t flags, hipStream_t stream);
+hipError_t launch_fused_sr(const Nvfp4Group& g, const Nvfp4Fused& f, uint32_t flags, hipStream_t stream);
+// Resident work-groups per CU of the single-read kernel for these flags.
+hipError_t fused_blocks_per_cu_rne(uint32_t flags, int* blocks);
+hipError_t fused_blocks_per_cu_sr(uint32_t flags, int* blocks);
+
 // Workspace layout (byte offsets):
 //   kCtrlOffset    section s: kCtrlGroups group counters and a top counter, each on
 //                  its own 256-byte line, at words kCtrlStride * ((kCtrlGroups + 1) * s + i)
+//   kStatusOffset  two 256-byte lines; word 0 is the single-read form's error word
 //   kTablesOffset  section s, direction dir (0 row, 1 column), scale code c:
 //                  float4 at index (s * 2 + dir) * 128 + c = (d, 1/d, multiplier, 0)
-//   kPartialsOffset  one 8-byte partial per 128 x 128 tile
+//   kSlotsOffset   the single-read form's partial words, one per item (at most
+//                  kFusedMaxItems), zero between calls; the two-kernel form never
+//                  touches them, so calls of either form can share a workspace
+//   kPartialsOffset  one 8-byte partial per 128 x 128 tile (two-kernel form)
 constexpr int kCtrlStride = 64;
 constexpr int kCtrlGroups = 16;
 constexpr int64_t kCtrlOffset = 0;
-constexpr int64_t kTablesOffset = (int64_t)kGroupSections * (kCtrlGroups + 1) * kCtrlStride * 4;
+constexpr int64_t kStatusOffset = (int64_t)kGroupSections * (kCtrlGroups + 1) * kCtrlStride * 4;
+constexpr int64_t kTablesOffset = kStatusOffset + 512;
 constexpr int64_t kTablesBytes = (int64_t)kGroupSections * 2 * 128 * 16;
-constexpr int64_t kPartialsOffset = kTablesOffset + kTablesBytes;
+constexpr int64_t kSlotsOffset = kTablesOffset + kTablesBytes;
+constexpr int64_t kPartialsOffset = kSlotsOffset + 4 * (int64_t)kFusedMaxItems;
 
 }  // namespace mxq

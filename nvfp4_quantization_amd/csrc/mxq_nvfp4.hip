@@ -49,7 +49,61 @@ hipError_t launch_sel(const Nvfp4Group& g, hipStream_t stream) {
 }
 }  // namespace
 
-hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, hipStream_t stream) {
+// Processing order of the single-read form: the non-empty sections in index order
+// (work-group b takes item b).
+static void fused_plan(const Nvfp4Group& g, Nvfp4Fused& f) {
+    const int per_tile_row = g.n_ctiles / 4;
+    f.n_cgroups = per_tile_row;
+    f.n_order = 0;
+    int32_t items = 0;
+    for (int s = 0; s < g.num_sections; ++s) {
+        const int n = (g.tt_start[s + 1] - g.tt_start[s]) * per_tile_row;
+        if (n == 0) continue;
+        f.order[f.n_order] = (uint8_t)s;
+        f.istart[f.n_order] = items;
+        ++f.n_order;
+        items += n;
+    }
+    f.istart[f.n_order] = items;
+    f.n_items = items;
+}
+
+// The single-read form applies when the measured maxima are wanted, the column tiles
+// come in fours, and every item of the group fits the resident grid at once.  Then
+// the whole input is read in one burst and each section is quantized as soon as its
+// last tile has arrived.  Larger groups would run as two or more batches in which
+// the loads of one batch and the quantizing of the previous one barely overlap; the
+// two-kernel form (whose second read comes partly from the Infinity Cache and
+// overlaps its arithmetic) is faster for them (measured on MI355X: 40.1 against
+// 46.6 us for 8192 x 4096 in 8 sections, 512 items; 78.9 against 74.0 us for 16384 x
+// 4096, 1024 items).
+static bool fused_eligible(const Nvfp4Group& g, uint32_t flags, hipStream_t stream, hipError_t* err) {
+    *err = hipSuccess;
+    if (g.amax_in_row || g.amax_in_col || g.total_tiles == 0 || g.n_ctiles % 4 != 0) return false;
+    int blocks = 0, dev = 0, cus = 0;
+    *err = (g.sr_row || g.sr_col) ? fused_blocks_per_cu_sr(flags, &blocks) : fused_blocks_per_cu_rne(flags, &blocks);
+    if (*err != hipSuccess) return false;
+    if ((*err = hipStreamGetDevice(stream, &dev)) != hipSuccess) return false;
+    if ((*err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return false;
+    const int64_t items = (int64_t)g.total_tiles / 4;
+    return items <= (int64_t)blocks * cus && items <= kFusedMaxItems;
+}
+
+hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, uint32_t* slots, uint32_t* status,
+                              hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    const bool fused = slots && fused_eligible(g, flags, stream, &e);
+    if (e != hipSuccess) return e;
+    if (fused) {
+        Nvfp4Fused f{};
+        f.slots = slots;
+        f.err = status;
+        fused_plan(g, f);
+        if ((e = launch_mark(0, stream)) != hipSuccess || (e = launch_mark(1, stream)) != hipSuccess) return e;
+        e = (g.sr_row || g.sr_col) ? launch_fused_sr(g, f, flags, stream) : launch_fused_rne(g, f, flags, stream);
+        if (e != hipSuccess) return e;
+        return launch_mark(2, stream);
+    }
     const bool row = flags & 1u, col = flags & 2u, fp8 = flags & 4u;
     switch ((row ? 1 : 0) | (col ? 2 : 0) | (fp8 ? 4 : 0)) {
         case 1: return launch_sel<true, false, false>(g, stream);

@@ -304,6 +304,9 @@ __device__ __forceinline__ void amax_quarter(const uint2 (&v)[16], uint32_t sign
 #define P(t, i) ((i) == 0 ? p[t][0].x : (i) == 1 ? p[t][0].y : (i) == 2 ? p[t][0].z : (i) == 3 ? p[t][0].w \
                : (i) == 4 ? p[t][1].x : (i) == 5 ? p[t][1].y : (i) == 6 ? p[t][1].z : p[t][1].w)
 
+// Packed BF16 pair i (columns 2i, 2i + 1 of the lane's 16) of row t of the lane's tile.
+__device__ __forceinline__ uint32_t tile_word(const uint4 (&p)[16][2], int t, int i) { return P(t, i); }
+
 // Hide the tile's provenance from the compiler (no instruction is emitted).
 // Otherwise it reuses values computed from the tile by an earlier pass in a later
 // one, keeping hundreds of them live across the passes.
@@ -409,10 +412,10 @@ __device__ __forceinline__ float row_absmax_nonan(const uint4 (&p)[16][2], int t
 template <bool SR, int RSTRIDE>
 __device__ __forceinline__ float row_pass(const Nvfp4Group& G, const uint4 (&p)[16][2], int s, int64_t c0,
                                           int64_t r_local0, float g_r, float yg_r, const float4* tab_r,
-                                          bool div_mode, uint8_t* rsc, uint8_t* rc_tile) {
+                                          bool div_mode, uint8_t* rsc, uint8_t* rc_tile, int tid) {
     const int64_t k = G.k;
     const u32x4 no_rnd = {0, 0, 0, 0};
-    const int lane_row = (threadIdx.x & 63) >> 3 << 4, cc = threadIdx.x & 7;
+    const int lane_row = (tid & 63) >> 3 << 4, cc = tid & 7;
     // the lane's offset in the tile fits 32 bits (k <= 2^26), so that each row's
     // store is a uniform base plus this offset, with no vector address arithmetic
     const uint32_t lane_off = (uint32_t)lane_row * (uint32_t)(k >> 1) + (uint32_t)cc * 8u;
@@ -652,60 +655,36 @@ __global__ __launch_bounds__(64) void k_nvfp4_given(const Nvfp4Group G) {
     build_tables<ROW, COL>(G, s, g_r, g_c);
 }
 
-// AOUT: the section maxima are supplied, and the measured ones are wanted out.
-// W waves per work-group take W adjacent column tiles of the same rows (k / 128 a
-// multiple of W), so that each row's W x 8 scale bytes leave as one piece: scattered
-// 8-byte pieces cost the memory system about three times as much per byte.
-template <bool ROW, bool COL, bool FP8, bool SR, bool AOUT, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void k_nvfp4_quant(const Nvfp4Group G) {
-    const int lane = threadIdx.x & 63;
-    const int w = W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;   // wave-uniform
-    const int b = (int)blockIdx.x * W + w;
-    const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
-    const int s = section_of(G, T);
-    const int tb = lane >> 3, cc = lane & 7;
-    const int64_t k = G.k;
-    const uint16_t* base = G.x + ((int64_t)T * kTileRows + tb * 16) * k + (int64_t)C * kTileCols + cc * 16;
-    // The section's scale tables are loaded before the tile: loads complete in order,
-    // so waiting for the table does not wait for the tile, and the first pass can
-    // start on the rows that have arrived.
-    const float4* src = G.tables + s * 256;
-    const float4 te0 = ROW ? src[lane] : float4{}, te1 = ROW ? src[64 + lane] : float4{};
-    const float4 te2 = COL ? src[128 + lane] : float4{}, te3 = COL ? src[192 + lane] : float4{};
-    __builtin_amdgcn_sched_barrier(0);
-    // Non-temporal without the FP8 output: this kernel is the input's last reader
-    // (quant 51.7 -> 45.6 us on 16384 x 4096, no worse at 65536 x 7168).  With the FP8
-    // output's non-temporal stores as well, the hint cost 10 % on 65536 x 7168 (461 ->
-    // 510 us) and nothing on 16384 x 4096: plain loads there.
-    uint4 p[16][2];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        if (FP8) {
-            p[t][0] = *reinterpret_cast<const uint4*>(base + t * k);
-            p[t][1] = *reinterpret_cast<const uint4*>(base + t * k + 8);
-        } else {
-            p[t][0] = nt_load16(base + t * k);
-            p[t][1] = nt_load16(base + t * k + 8);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    __shared__ float4 tab[2][128];
-    // Column codes / scales of the tile by (column, 16-row block): 64 + 8 bytes per
+// LDS of one work-group's quant passes (W waves, one tile each).
+template <int W>
+struct QuantLds {
+    float4 tab[2][128];                                 // the section's scale tables
+    // Column codes / scales of a tile by (column, 16-row block): 64 + 8 bytes per
     // column, with one more slot after every 16 columns so that the 8 lane groups
     // that write columns 16 apart use both halves of the LDS banks.
-    __shared__ uint2 lds_codes_w[W][kTileCols * 8 + 8 * 8];
-    __shared__ uint8_t lds_sc_w[W][kTileCols * 8 + 8 * 8];
-    __shared__ uint8_t lds_rsc[kTileRows * 8 * W];        // row scales of the work-group's tiles
-    uint2* const lds_codes = lds_codes_w[w];
-    uint8_t* const lds_sc = lds_sc_w[w];
-    // every wave writes the whole table (the same values): no wave reads an entry
-    // before its own write
-    if (ROW) { tab[0][lane] = te0; tab[0][64 + lane] = te1; }
-    if (COL) { tab[1][lane] = te2; tab[1][64 + lane] = te3; }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    uint2 codes[W][kTileCols * 8 + 8 * 8];
+    uint8_t sc[W][kTileCols * 8 + 8 * 8];
+    uint8_t rsc[kTileRows * 8 * W];                      // row scales of the work-group's tiles
+};
 
+// Every output of wave w's tile (token tile T, column tile C of section s), the tile
+// in p and the section's tables in L.tab: the row pass first (a row block needs only
+// its own row, so it starts on the rows that have arrived), then the column pass
+// (all 16 rows of each column block), then FP8.  The W waves of a work-group take
+// W adjacent column tiles of the same rows, so that each row's W x 8 scale bytes
+// leave as one piece: scattered 8-byte pieces cost the memory system about three
+// times as much per byte.  AOUT: the section maxima are supplied, and the measured
+// ones are wanted out.
+// tid: threadIdx.x (a caller that loops may pass it laundered, so that no address
+// derived from it is hoisted out of the loop and kept live through the passes).
+template <bool ROW, bool COL, bool FP8, bool SR, bool AOUT, int W>
+__device__ __forceinline__ void quant_passes(const Nvfp4Group& G, uint4 (&p)[16][2], QuantLds<W>& L, int w, int s,
+                                             int T, int C, int tid) {
+    const int lane = tid & 63;
+    const int tb = lane >> 3, cc = lane & 7;
+    const int64_t k = G.k;
+    uint2* const lds_codes = L.codes[w];
+    uint8_t* const lds_sc = L.sc[w];
     const int tt0 = G.tt_start[s];
     const int ms = (G.tt_start[s + 1] - tt0) * kTileRows;           // section rows
     const int T_local = T - tt0;
@@ -714,13 +693,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int64_t r_local0 = (int64_t)T_local * kTileRows + tb * 16;  // section-local
     const u32x4 no_rnd = {0, 0, 0, 0};
     if (ROW) {
-        const float g_r = tab[0][0].x, yg_r = tab[0][0].y;
-        const float4* tab_r = tab[0];
+        const float g_r = L.tab[0][0].x, yg_r = L.tab[0][0].y;
+        const float4* tab_r = L.tab[0];
         uint8_t* const rc_tile = G.row_codes + (int64_t)T * kTileRows * (k >> 1) + (int64_t)C * (kTileCols / 2);
-        // first, so that its rows can start as their loads arrive (each row block needs
-        // one row; the column pass needs all 16)
         const float ra = row_pass<SR, 8 * W>(G, p, s, c0, r_local0, g_r, yg_r, tab_r, tab_r[127].x != 0.0f,
-                                             lds_rsc + 8 * w, rc_tile);
+                                             L.rsc + 8 * w, rc_tile, tid);
         if (W > 1) {
             __syncthreads();
         } else {
@@ -732,9 +709,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         // 8-byte pieces were much slower that way, as the column scales showed.
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int i = it * 64 * W + (int)threadIdx.x;
+            const int i = it * 64 * W + tid;
             const int r = i / W, part = i - r * W;
-            const uint2 v = *reinterpret_cast<const uint2*>(lds_rsc + r * 8 * W + part * 8);
+            const uint2 v = *reinterpret_cast<const uint2*>(L.rsc + r * 8 * W + part * 8);
             uint8_t* const dst = G.row_scales + ((int64_t)T * kTileRows + r) * (k >> 4) + (int64_t)(C - w) * 8 + part * 8;
             if (W >= 4)
                 __builtin_nontemporal_store(u32x2v{v.x, v.y}, reinterpret_cast<u32x2v*>(dst));
@@ -743,17 +720,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         if (AOUT && G.amax_out_row) {
             // supplied maxima: measure this call's for the caller's next step
-            const float w = wave_max_f32(ra);
+            const float wm = wave_max_f32(ra);
             if (lane == 0)
-                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_row + s), __builtin_bit_cast(uint32_t, w),
+                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_row + s), __builtin_bit_cast(uint32_t, wm),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         launder(p);
     }
 
     if (COL) {
-        const float g_c = tab[1][0].x, yg_c = tab[1][0].y;
-        const float4* tab_c = tab[1];
+        const float g_c = L.tab[1][0].x, yg_c = L.tab[1][0].y;
+        const float4* tab_c = L.tab[1];
         const uint32_t mask = G.sign_mask;
         float col_amax = 0.0f;                       // max |H16 D x| of the lane's blocks (NaNs aside)
         auto put = [&](int j, const BlockOut& o) {
@@ -802,8 +779,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             const uint4 v = *reinterpret_cast<const uint4*>(&lds_codes[(col + (col >> 4)) * 8 + part * 2]);
             // Non-temporal: the codes (two thirds of the output bytes) stream out during
             // this kernel instead of staying dirty in the caches, where the next call's
-            // amax kernel would have to write them back (-5 us there, +3 us here for
-            // C3).  The column scales, 8-byte pieces, are slower this way.
+            // first kernel would have to write them back.  The column scales, 8-byte
+            // pieces, are slower this way.
             __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w},
                                         reinterpret_cast<u32x4v*>(codes_s + ((int64_t)C * kTileCols + col) * (ms >> 1) +
                                                                   T_local * 64 + part * 16));
@@ -816,9 +793,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         if (AOUT && G.amax_out_col) {
             // supplied maxima: measure this call's, max |BF16(y/4)| = BF16(max |y|) / 4
-            const float w = 0.25f * round_bf16(wave_max_f32(col_amax));
+            const float wm = 0.25f * round_bf16(wave_max_f32(col_amax));
             if (lane == 0)
-                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_col + s), __builtin_bit_cast(uint32_t, w),
+                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_col + s), __builtin_bit_cast(uint32_t, wm),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         launder(p);
@@ -870,6 +847,59 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+}
+
+// Lane (tb, cc) of a tile loads rows 16 tb .. 16 tb + 15, columns 16 cc .. 16 cc + 15
+// (two 16-byte loads per row).  NT: non-temporal, for the input's last reader.
+template <bool NT>
+__device__ __forceinline__ void load_tile(uint4 (&p)[16][2], const uint16_t* base, int64_t k) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        if (NT) {
+            p[t][0] = nt_load16(base + t * k);
+            p[t][1] = nt_load16(base + t * k + 8);
+        } else {
+            p[t][0] = *reinterpret_cast<const uint4*>(base + t * k);
+            p[t][1] = *reinterpret_cast<const uint4*>(base + t * k + 8);
+        }
+    }
+}
+
+// Phase B of the two-kernel call: one wave per tile, W waves per work-group over W
+// adjacent column tiles of the same rows (k / 128 a multiple of W).
+template <bool ROW, bool COL, bool FP8, bool SR, bool AOUT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void k_nvfp4_quant(const Nvfp4Group G) {
+    const int lane = threadIdx.x & 63;
+    const int w = W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;   // wave-uniform
+    const int b = (int)blockIdx.x * W + w;
+    const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
+    const int s = section_of(G, T);
+    const int tb = lane >> 3, cc = lane & 7;
+    const int64_t k = G.k;
+    const uint16_t* base = G.x + ((int64_t)T * kTileRows + tb * 16) * k + (int64_t)C * kTileCols + cc * 16;
+    // The section's scale tables are loaded before the tile: loads complete in order,
+    // so waiting for the table does not wait for the tile, and the first pass can
+    // start on the rows that have arrived.
+    const float4* src = G.tables + s * 256;
+    const float4 te0 = ROW ? src[lane] : float4{}, te1 = ROW ? src[64 + lane] : float4{};
+    const float4 te2 = COL ? src[128 + lane] : float4{}, te3 = COL ? src[192 + lane] : float4{};
+    __builtin_amdgcn_sched_barrier(0);
+    // Non-temporal without the FP8 output: this kernel is the input's last reader
+    // (quant 51.7 -> 45.6 us on 16384 x 4096, no worse at 65536 x 7168).  With the FP8
+    // output's non-temporal stores as well, the hint cost 10 % on 65536 x 7168 (461 ->
+    // 510 us) and nothing on 16384 x 4096: plain loads there.
+    uint4 p[16][2];
+    load_tile<!FP8>(p, base, k);
+    __builtin_amdgcn_sched_barrier(0);
+
+    __shared__ QuantLds<W> L;
+    // every wave writes the whole table (the same values): no wave reads an entry
+    // before its own write
+    if (ROW) { L.tab[0][lane] = te0; L.tab[0][64 + lane] = te1; }
+    if (COL) { L.tab[1][lane] = te2; L.tab[1][64 + lane] = te3; }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    quant_passes<ROW, COL, FP8, SR, AOUT, W>(G, p, L, w, s, T, C, (int)threadIdx.x);
 }
 
 #undef P

@@ -119,14 +119,16 @@ def test_grouped_argument_errors(L):
 def test_workspace_size_query(L):
     q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
     assert q(16384, 4096, 8, 4) == 0                              # FP8 only: no amax pass
-    # counters (32 x 256 B) and scale tables (32 sections x 2 directions x 128 x 16 B)
-    # of one launch group, then one 8-byte partial per 128 x 128 tile
-    fixed = 32 * 17 * 256 + 32 * 2 * 128 * 16
+    # counters (32 x 17 x 256 B), two status lines, scale tables (32 sections x 2
+    # directions x 128 x 16 B) and the single-read form's 1024 partial words of one
+    # launch group, then one 8-byte partial per 128 x 128 tile
+    fixed = 32 * 17 * 256 + 512 + 32 * 2 * 128 * 16 + 4 * 1024
     for total, k, S in [(0, 4096, 8), (16384, 4096, 8), (65536, 7168, 32), (128, 128, 1), (16384, 4096, 256)]:
         for flags in (1, 2, 3, 7):
             need = q(total, k, S, flags)
+            tiles = (total // 128) * (k // 128)
             assert need % 256 == 0
-            assert fixed + 8 * (total // 128) * (k // 128) <= need < fixed + 8 * (total // 128) * (k // 128) + 256
+            assert fixed + 8 * tiles <= need < fixed + 8 * tiles + 256
 
 
 def test_no_forbidden_calls_in_host_sources():

@@ -4,6 +4,7 @@ results of a fixed FP32 arithmetic, so no tolerance applies).  Sizes span severa
 tiles with ragged tails; edge cases cover NaN, subnormal, -0, all-zero and empty
 inputs.  Full-size workloads live in test_gpu_full_size.py."""
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -359,7 +360,8 @@ def compare_grouped(orc, x_dev, sections, mask, flags, seed=None, ro=None, co=No
     call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, out=out)
     res = call()
     torch.cuda.synchronize()
-    assert mxq.workspace_counters_clear(call.workspace), "a section counter was left nonzero"
+    assert mxq.workspace_counters_clear(call.workspace), \
+        "a section counter, the error word or a partial word was left nonzero"
     ref = orc.group_rht_quant_nvfp4(bits16(x_dev), sections, mask, flags, seed or 0, ro, co, threads=threads)
     if flags & 1:
         assert_same("row_global", host(res.row_global), ref.row_global)
@@ -404,6 +406,71 @@ def test_grouped_sr_small(orc, k):
                     None, p["col_offsets"])
     compare_grouped(orc, w.tensors["x"].to(dev), p["split_sections"], p["sign_mask"], 7, p["seed"],
                     p["row_offsets"], None)
+
+
+@pytest.mark.parametrize("flags,sr", [(3, False), (3, True), (7, False), (1, False), (2, True)])
+def test_grouped_single_read_reuse(orc, flags, sr):
+    """The single-read form (k a multiple of 512, every section within the resident
+    grid): one workspace through three calls, the second on other sections and
+    fewer rows; each matches the oracle and leaves the workspace's counters, error
+    word and partial words at zero."""
+    dev = device()
+    announce(f"grouped single-read reuse flags={flags} sr={sr}")
+    w = synth.grouped_nvfp4_sr(total_rows=3072, k=2048, parts=9, forced_empty=2, seed=40)
+    p = w.params
+    x = w.tensors["x"].to(dev)
+    seed, ro, co = (p["seed"], p["row_offsets"], p["col_offsets"]) if sr else (None, None, None)
+    ws = mxq.alloc_workspace(3072, 2048, 9, flags, dev)
+    for sections, rows in ((p["split_sections"], 3072), ([1024, 0, 512, 128, 384], 2048),
+                           (p["split_sections"], 3072)):
+        S = len(sections)
+        xi = x[:rows].contiguous()
+        call = mxq.GroupedNVFP4(xi, sections, p["sign_mask"], flags, seed, ro[:S] if ro else None,
+                                co[:S] if co else None, workspace=ws)
+        res = call()
+        torch.cuda.synchronize()
+        assert mxq.workspace_counters_clear(ws), "workspace left nonzero"
+        ref = orc.group_rht_quant_nvfp4(bits16(xi), sections, p["sign_mask"], flags, seed or 0,
+                                        ro[:S] if ro else None, co[:S] if co else None, threads=8)
+        for name in ("row_global", "row_scales", "row_codes", "col_global", "col_scales", "col_codes",
+                     "fp8_scales", "fp8_codes"):
+            got = getattr(res, name)
+            if got is not None:
+                assert_same(name, host(got), getattr(ref, name))
+
+
+@pytest.mark.parametrize("sr", [False, True])
+def test_grouped_single_read_deferred(orc, sr):
+    """The single-read form's fallback for a device short of room: in the test build
+    of the library every waiting item gives up at once, marks its partial deferred and
+    ends, and its section's last item reads and quantizes those tiles itself.  Every
+    output byte still matches the oracle, and the workspace is left clear."""
+    dev = device()
+    announce(f"grouped single-read deferred sr={sr}")
+    path = os.path.join(os.path.dirname(mxq.LIB_PATH), "libmxq_defer0.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} is missing: build the library")
+    w = synth.grouped_nvfp4_sr(total_rows=2048, k=2048, parts=7, forced_empty=2, seed=41)
+    p = w.params
+    seed, ro, co = (p["seed"], p["row_offsets"], p["col_offsets"]) if sr else (None, None, None)
+    x = w.tensors["x"].to(dev)
+    saved = mxq._lib
+    try:
+        mxq._lib = None
+        mxq.LIB_PATH, main_path = path, mxq.LIB_PATH
+        try:
+            call = mxq.GroupedNVFP4(x, p["split_sections"], p["sign_mask"], 3, seed, ro, co)
+            res = call()
+            torch.cuda.synchronize()
+        finally:
+            mxq.LIB_PATH = main_path
+    finally:
+        mxq._lib = saved
+    assert mxq.workspace_counters_clear(call.workspace), "workspace left nonzero"
+    ref = orc.group_rht_quant_nvfp4(bits16(x), p["split_sections"], p["sign_mask"], 3, seed or 0, ro, co,
+                                    threads=8)
+    for name in ("row_global", "row_scales", "row_codes", "col_global", "col_scales", "col_codes"):
+        assert_same(name, host(getattr(res, name)), getattr(ref, name))
 
 
 def test_grouped_large_moe_recipe_small(orc):
