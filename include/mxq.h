@@ -347,6 +347,30 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
                                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The grouped call for callers that cannot allocate: code under stream capture,
+ * tight serving loops, harnesses that forbid allocation.  Arguments, outputs,
+ * checks and results are those of mxq_group_rht_quant_nvfp4 without the workspace:
+ * the library's own device array of MXQ_NOALLOC_SCRATCH_BYTES bytes stands in for it
+ * (one per GPU, held until the process ends; its device address is looked up once
+ * per device, on the first call with that device current, and the words the call
+ * needs at zero are cleared then by a fill kernel on that call's stream).  A call
+ * whose workspace would exceed the array (mxq_group_rht_quant_nvfp4_workspace_size
+ * above MXQ_NOALLOC_SCRATCH_BYTES, e.g. more than 96,704 tiles of 128 x 128) gives
+ * MXQ_ERR_UNSUPPORTED before anything is enqueued.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine).  The stream must belong to
+ * the current device.  Every call on one GPU uses that GPU's array: calls that
+ * overlap on one GPU (other streams, or other host threads without ordering) race.
+ * ------------------------------------------------------------------------- */
+#define MXQ_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+mxq_status mxq_group_rht_quant_nvfp4_noalloc(const uint16_t* x_bf16, int64_t k,
+                                             const int64_t* split_sections, int64_t num_sections,
+                                             uint16_t rht_sign_mask, uint32_t flags, const mxq_sr* sr,
+                                             const mxq_nvfp4_out* rowwise,
+                                             const mxq_nvfp4_out* columnwise,
+                                             const mxq_fp8_out* fp8_rowwise, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Launch marks (measurement).  Not an operation of the method: a hook through
  * which a harness times each kernel of a grouped NVFP4 call on the call's own
  * stream, so that per-kernel times come from the same run as the call's time.

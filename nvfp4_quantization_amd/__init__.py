@@ -27,7 +27,7 @@ EXPORTED = ("mxq_status_string", "mxq_version", "mxq_quant_fp8_1x128", "mxq_hada
             "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4",
             "mxq_group_rht_quant_nvfp4_with_amax", "mxq_set_launch_marks",
             "mxq_hadamard_quant_nvfp4_workspace_size", "mxq_hadamard_quant_nvfp4", "mxq_swiglu_quant_fp8",
-            "mxq_quant_fp8_blockwise", "mxq_hadamard_quant_fp8_ex")
+            "mxq_quant_fp8_blockwise", "mxq_hadamard_quant_fp8_ex", "mxq_group_rht_quant_nvfp4_noalloc")
 MXQ_FP8_UE8M0 = 1
 
 
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.mxq_hadamard_quant_nvfp4.restype = ctypes.c_int
         L.mxq_hadamard_quant_nvfp4.argtypes = [p, i64, ctypes.c_int32, p, i64, i64, p, p, p, p, p, p,
                                                ctypes.c_size_t, p]
+        L.mxq_group_rht_quant_nvfp4_noalloc.restype = ctypes.c_int
+        L.mxq_group_rht_quant_nvfp4_noalloc.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
+                                                        p, p, p, p]
         L.mxq_set_launch_marks.restype = ctypes.c_int
         L.mxq_set_launch_marks.argtypes = [p, p, p]
         _lib = L
@@ -474,6 +477,43 @@ class GroupedNVFP4:
                 ctypes.addressof(self._amax), _ptr(self.workspace), self.workspace.numel(), _stream(stream))
             _check(st, "mxq_group_rht_quant_nvfp4_with_amax")
         return self.out
+
+
+def mxq_group_rht_quant_nvfp4_noalloc(x: torch.Tensor, split_sections: Sequence[int], rht_sign_mask: int,
+                                      flags: int, seed: Optional[int] = None,
+                                      row_offsets: Optional[Sequence[int]] = None,
+                                      col_offsets: Optional[Sequence[int]] = None,
+                                      out: NVFP4Result = None, stream=None) -> NVFP4Result:
+    """The grouped call without a workspace: the library's per-device scratch array
+    (MXQ_NOALLOC_SCRATCH_BYTES) stands in for it.  `out` must be allocated beforehand
+    (alloc_nvfp4_outputs) by a caller that cannot allocate during the call."""
+    x = _bf16_bits(x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous [total_rows][k]")
+    total, k = x.shape
+    S = len(split_sections)
+    if out is None:
+        out = alloc_nvfp4_outputs(total, k, S, flags, x.device)
+    sections = (ctypes.c_int64 * max(S, 1))(*[int(v) for v in split_sections])
+    row = _NVFP4Out(_addr(out.row_codes), _addr(out.row_scales), _addr(out.row_global))
+    col = _NVFP4Out(_addr(out.col_codes), _addr(out.col_scales), _addr(out.col_global))
+    fp8 = _FP8Out(_addr(out.fp8_codes), _addr(out.fp8_scales))
+    sr = ro = co = None
+    if seed is not None and (row_offsets is not None or col_offsets is not None):
+        ro = (ctypes.c_uint64 * S)(*row_offsets) if row_offsets is not None else None
+        co = (ctypes.c_uint64 * S)(*col_offsets) if col_offsets is not None else None
+        sr = _SR(seed & ((1 << 64) - 1), ctypes.addressof(ro) if ro is not None else None,
+                 ctypes.addressof(co) if co is not None else None)
+    st = lib().mxq_group_rht_quant_nvfp4_noalloc(
+        _ptr(x), k, ctypes.addressof(sections), S, rht_sign_mask & 0xFFFF, flags,
+        ctypes.addressof(sr) if sr is not None else None, ctypes.addressof(row), ctypes.addressof(col),
+        ctypes.addressof(fp8), _stream(stream))
+    _check(st, "mxq_group_rht_quant_nvfp4_noalloc")
+    return out
+
+
+def _addr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
 
 
 def mxq_group_rht_quant_nvfp4(x: torch.Tensor, split_sections: Sequence[int], rht_sign_mask: int, flags: int,

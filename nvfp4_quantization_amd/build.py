@@ -38,7 +38,7 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["mxq_fp8.hip", "mxq_fp8_block.hip", "mxq_swiglu_fp8.hip", "mxq_dsa_nvfp4.hip", "mxq_nvfp4.hip", "mxq_nvfp4_quant_rne.hip", "mxq_nvfp4_quant_sr.hip",
                "mxq_nvfp4_quant_rne_aout.hip", "mxq_nvfp4_quant_sr_aout.hip",
-               "mxq_nvfp4_fused_rne.hip", "mxq_nvfp4_fused_sr.hip"]
+               "mxq_nvfp4_fused_rne.hip", "mxq_nvfp4_fused_sr.hip", "mxq_noalloc.hip"]
 HOST_SOURCES = ["mxq_api.cpp"]
 FUSED_SOURCES = ("mxq_nvfp4_fused_rne.hip", "mxq_nvfp4_fused_sr.hip")
 EXTRA = {src: ["-mllvm", "-disable-machine-licm"] for src in FUSED_SOURCES}

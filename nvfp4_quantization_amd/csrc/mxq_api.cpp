@@ -51,6 +51,59 @@ hipError_t launch_mark(int i, hipStream_t stream) {
 }
 }  // namespace mxq
 
+namespace mxq {
+// The argument checks of the grouped call, everything but the workspace (which the
+// call without a workspace replaces by its own array): MXQ_OK and the total row
+// count, or the first error.  Nothing is enqueued.
+mxq_status grouped_check(const uint16_t* x_bf16, int64_t k, const int64_t* split_sections, int64_t num_sections,
+                         uint32_t flags, const mxq_nvfp4_out* rowwise, const mxq_nvfp4_out* columnwise,
+                         const mxq_fp8_out* fp8_rowwise, const mxq_amax* amax, int64_t* total_rows_out) {
+    if (k <= 0 || !split_sections || num_sections < 1) return MXQ_ERR_INVALID_ARGUMENT;
+    if (num_sections > MXQ_MAX_SECTIONS || k > kMaxGroupK) return MXQ_ERR_UNSUPPORTED;
+    if (flags == 0 || (flags & ~(uint32_t)(MXQ_ROWWISE | MXQ_COLUMNWISE | MXQ_FP8_ROWWISE)))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (k % 128 != 0) return MXQ_ERR_MISALIGNED;
+    int64_t total_rows = 0;
+    for (int64_t s = 0; s < num_sections; ++s) {
+        const int64_t ms = split_sections[s];
+        if (ms < 0) return MXQ_ERR_INVALID_ARGUMENT;
+        if (ms % 128 != 0) return MXQ_ERR_MISALIGNED;
+        total_rows += ms;
+        if (total_rows > kMaxRows) return MXQ_ERR_UNSUPPORTED;
+    }
+    if (total_rows * k >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    const bool row = flags & MXQ_ROWWISE, col = flags & MXQ_COLUMNWISE, fp8 = flags & MXQ_FP8_ROWWISE;
+    if (row && (!rowwise || !rowwise->global_scales || (total_rows > 0 && (!rowwise->codes || !rowwise->block_scales))))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (col && (!columnwise || !columnwise->global_scales ||
+                (total_rows > 0 && (!columnwise->codes || !columnwise->block_scales))))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (fp8 && total_rows > 0 && (!fp8_rowwise || !fp8_rowwise->codes || !fp8_rowwise->scales))
+        return MXQ_ERR_INVALID_ARGUMENT;
+    if (total_rows > 0 && !x_bf16) return MXQ_ERR_INVALID_ARGUMENT;
+    if (x_bf16 && !aligned(x_bf16, 16)) return MXQ_ERR_MISALIGNED;
+    if (row && (!aligned(rowwise->codes, 16) || !aligned(rowwise->block_scales, 16) ||
+                !aligned(rowwise->global_scales, 4)))
+        return MXQ_ERR_MISALIGNED;
+    if (col && (!aligned(columnwise->codes, 16) || !aligned(columnwise->block_scales, 16) ||
+                !aligned(columnwise->global_scales, 4)))
+        return MXQ_ERR_MISALIGNED;
+    if (fp8 && total_rows > 0 && (!aligned(fp8_rowwise->codes, 16) || !aligned(fp8_rowwise->scales, 4)))
+        return MXQ_ERR_MISALIGNED;
+    // caller-supplied maxima: all or none of the requested NVFP4 directions
+    const bool given = amax && (amax->row_in || amax->col_in);
+    if (given && ((row && !amax->row_in) || (col && !amax->col_in))) return MXQ_ERR_INVALID_ARGUMENT;
+    if (amax && (!aligned(amax->row_in, 4) || !aligned(amax->col_in, 4) || !aligned(amax->row_out, 4) ||
+                 !aligned(amax->col_out, 4)))
+        return MXQ_ERR_MISALIGNED;
+    const int64_t n_ct = k / 128;
+    if ((total_rows / 128) * n_ct * 2 * 64 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+    if (!row && !col && ceil_div(total_rows * (k / 128), 32) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
+    *total_rows_out = total_rows;
+    return MXQ_OK;
+}
+}  // namespace mxq
+
 extern "C" {
 
 const char* mxq_status_string(mxq_status s) {
@@ -300,44 +353,12 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
                                                const mxq_fp8_out* fp8_rowwise, const mxq_amax* amax,
                                                void* workspace, size_t workspace_bytes, void* stream) {
     // ---- checks (nothing is enqueued before all of them pass)
-    if (k <= 0 || !split_sections || num_sections < 1) return MXQ_ERR_INVALID_ARGUMENT;
-    if (num_sections > MXQ_MAX_SECTIONS || k > kMaxGroupK) return MXQ_ERR_UNSUPPORTED;
-    if (flags == 0 || (flags & ~(uint32_t)(MXQ_ROWWISE | MXQ_COLUMNWISE | MXQ_FP8_ROWWISE)))
-        return MXQ_ERR_INVALID_ARGUMENT;
-    if (k % 128 != 0) return MXQ_ERR_MISALIGNED;
     int64_t total_rows = 0;
-    for (int64_t s = 0; s < num_sections; ++s) {
-        const int64_t ms = split_sections[s];
-        if (ms < 0) return MXQ_ERR_INVALID_ARGUMENT;
-        if (ms % 128 != 0) return MXQ_ERR_MISALIGNED;
-        total_rows += ms;
-        if (total_rows > kMaxRows) return MXQ_ERR_UNSUPPORTED;
-    }
-    if (total_rows * k >= kMaxElems) return MXQ_ERR_UNSUPPORTED;
+    const mxq_status c = mxq::grouped_check(x_bf16, k, split_sections, num_sections, flags, rowwise, columnwise,
+                                            fp8_rowwise, amax, &total_rows);
+    if (c != MXQ_OK) return c;
     const bool row = flags & MXQ_ROWWISE, col = flags & MXQ_COLUMNWISE, fp8 = flags & MXQ_FP8_ROWWISE;
-    if (row && (!rowwise || !rowwise->global_scales || (total_rows > 0 && (!rowwise->codes || !rowwise->block_scales))))
-        return MXQ_ERR_INVALID_ARGUMENT;
-    if (col && (!columnwise || !columnwise->global_scales ||
-                (total_rows > 0 && (!columnwise->codes || !columnwise->block_scales))))
-        return MXQ_ERR_INVALID_ARGUMENT;
-    if (fp8 && total_rows > 0 && (!fp8_rowwise || !fp8_rowwise->codes || !fp8_rowwise->scales))
-        return MXQ_ERR_INVALID_ARGUMENT;
-    if (total_rows > 0 && !x_bf16) return MXQ_ERR_INVALID_ARGUMENT;
-    if (x_bf16 && !aligned(x_bf16, 16)) return MXQ_ERR_MISALIGNED;
-    if (row && (!aligned(rowwise->codes, 16) || !aligned(rowwise->block_scales, 16) ||
-                !aligned(rowwise->global_scales, 4)))
-        return MXQ_ERR_MISALIGNED;
-    if (col && (!aligned(columnwise->codes, 16) || !aligned(columnwise->block_scales, 16) ||
-                !aligned(columnwise->global_scales, 4)))
-        return MXQ_ERR_MISALIGNED;
-    if (fp8 && total_rows > 0 && (!aligned(fp8_rowwise->codes, 16) || !aligned(fp8_rowwise->scales, 4)))
-        return MXQ_ERR_MISALIGNED;
-    // caller-supplied maxima: all or none of the requested NVFP4 directions
     const bool given = amax && (amax->row_in || amax->col_in);
-    if (given && ((row && !amax->row_in) || (col && !amax->col_in))) return MXQ_ERR_INVALID_ARGUMENT;
-    if (amax && (!aligned(amax->row_in, 4) || !aligned(amax->col_in, 4) || !aligned(amax->row_out, 4) ||
-                 !aligned(amax->col_out, 4)))
-        return MXQ_ERR_MISALIGNED;
     const bool sr_row = row && sr && sr->row_offsets;
     const bool sr_col = col && sr && sr->col_offsets;
     const size_t need = mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags);
@@ -347,12 +368,10 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
         if (!aligned(workspace, 256)) return MXQ_ERR_MISALIGNED;
     }
     const int64_t n_ct = k / 128;
-    if ((total_rows / 128) * n_ct * 2 * 64 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!row && !col) {
         // the FP8 1x128 output alone needs no tensor scale: one plain FP8 launch
         if (total_rows == 0) return MXQ_OK;
-        if (ceil_div(total_rows * (k / 128), 32) * 256 > kMaxGridThreads) return MXQ_ERR_UNSUPPORTED;
         mxq::Fp8Args a{x_bf16, fp8_rowwise->codes, fp8_rowwise->scales, total_rows, k, k, k, k / 128, 1};
         return mxq::launch_quant_fp8_1x128(a, st) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
     }

@@ -131,6 +131,14 @@ struct Nvfp4Group {
 };
 // slots: the single-read form's partial words (zero between calls); status: its error word.
 hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, uint32_t* slots, uint32_t* status, hipStream_t stream);
+}  // namespace mxq
+#include "mxq.h"
+namespace mxq {
+// The grouped call's argument checks without the workspace (mxq_api.cpp): MXQ_OK and
+// the total rows, or the first error; nothing is enqueued.
+mxq_status grouped_check(const uint16_t* x_bf16, int64_t k, const int64_t* split_sections, int64_t num_sections,
+                         uint32_t flags, const mxq_nvfp4_out* rowwise, const mxq_nvfp4_out* columnwise,
+                         const mxq_fp8_out* fp8_rowwise, const mxq_amax* amax, int64_t* total_rows);
 // Launch marks of the calling thread (mxq_set_launch_marks): records mark i
 // (0 before the first kernel, 1 between the scale and quantize kernels, 2 after)
 // on the stream when marks are set; hipSuccess otherwise.

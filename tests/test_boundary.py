@@ -309,3 +309,26 @@ def test_extent_limits(L):
     q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
     assert q(1 << 40, 4096, 8, 3) == 0 and q(16384, 1 << 40, 8, 3) == 0
 
+
+@no_gpu
+def test_noalloc_rejects_beyond_scratch(L):
+    """The grouped call without a workspace refuses, before anything is enqueued, a
+    call whose workspace would exceed its scratch array (MXQ_NOALLOC_SCRATCH_BYTES)."""
+    text = open(os.path.join(ROOT, "include", "mxq.h")).read()
+    limit = int(eval(re.search(r"#define MXQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).expand(r"\1 << \2")))
+    q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
+    rows = 1 << 20                                      # 2^20 x 8192: 524288 tiles
+    assert q(rows, 8192, 1, 3) > limit
+    sections = (ctypes.c_int64 * 1)(rows)
+    out = mxq._NVFP4Out(A, A, A)
+    st = L.mxq_group_rht_quant_nvfp4_noalloc(ctypes.c_void_p(A), 8192, ctypes.addressof(sections), 1, 0, 3,
+                                             None, ctypes.addressof(out), ctypes.addressof(out), None, None)
+    assert st == UNSUPPORTED
+    # invalid arguments: the grouped call's own checks answer first
+    sections = (ctypes.c_int64 * 1)(100)                 # not a multiple of 128
+    assert L.mxq_group_rht_quant_nvfp4_noalloc(ctypes.c_void_p(A), 256, ctypes.addressof(sections), 1, 0, 3,
+                                               None, ctypes.addressof(out), ctypes.addressof(out), None,
+                                               None) == MISALIGNED
+    sections = (ctypes.c_int64 * 1)(128)
+    assert L.mxq_group_rht_quant_nvfp4_noalloc(ctypes.c_void_p(A), 8192, ctypes.addressof(sections), 1, 0, 3,
+                                               None, None, None, None, None) == INVALID        # no outputs
