@@ -10,8 +10,17 @@ configuration the headline metric is quoted on).  The timed steps run back to ba
 and cycle over several copies of the input and outputs, together far larger than
 the 256 MB Infinity Cache, so each call reads its input from HBM and pays for the
 write-back of earlier calls' outputs, as a stream of calls would; ms_per_step is
-the HIP-event time of the whole run on the kernels' stream divided by the steps
+the HIP-event time of the whole run on the calls' stream divided by the steps
 (two events around the K calls, nothing enqueued between them).
+
+`roofline` is the whole call's: its algorithmic bytes (input read once, every output
+written once) over the call time, against the 8 TB/s HBM peak.  A call of the
+two-kernel form runs two kernels, the second reading the input again; only the call
+as a whole moves the method's bytes, so no single kernel's rate stands for it (the
+per-kernel split is in the committed rocprofv3 summaries).  Beside it: the rate of a
+hand-written streaming read and copy over the same rotating buffer sizes
+(libmxq_ceiling.so; the measured ceilings: a read of the input's bytes, and the
+input read plus the outputs written) and torch's 1 GiB copy.
 Secondary figures: a single call after a 1 GiB read has cleared the caches of the
 input (without leaving dirty lines behind), and back-to-back calls on one input
 (warm caches).  Prints ONE JSON line.
@@ -31,12 +40,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="grouped_nvfp4_rht",
-                    choices=["grouped_nvfp4_rht", "grouped_nvfp4_rht_sr", "large_moe_nvfp4_fp8",
-                             "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8", "fp8_blockwise", "fp8_1x128"])
+                    choices=["grouped_nvfp4_rht", "grouped_nvfp4_rht_given", "grouped_nvfp4_rht_sr",
+                             "large_moe_nvfp4_fp8", "dsa_rotate_fp8", "dsa_rotate_nvfp4", "swiglu_fp8",
+                             "fp8_blockwise", "fp8_1x128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="steady-state steps only, then one 256 MiB device copy (the counter calibration "
-                         "for rocprofv3 runs); prints the JSON line without the secondary figures")
+                    help="steady-state steps only, then one 256 MiB device copy and one 128 MiB read twice "
+                         "(the counter calibrations for rocprofv3 runs); prints a short JSON line")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows of the workload the oracle baseline runs on (0: the whole workload, "
                          "capped at 16384 rows)")
@@ -128,18 +138,28 @@ def main():
         alg_bytes = in_bytes + m * 64 + m * 8 + 4
         desc = f"dsa cat+WHT128+nvfp4 row-wise (one tensor scale, measured), {m} rows (4096 tokens x 64 heads) bf16"
     else:
-        gen = {"grouped_nvfp4_rht": synth.grouped_nvfp4, "grouped_nvfp4_rht_sr": synth.grouped_nvfp4_sr,
-               "large_moe_nvfp4_fp8": synth.large_moe}[wl]
+        gen = {"grouped_nvfp4_rht": synth.grouped_nvfp4, "grouped_nvfp4_rht_given": synth.grouped_nvfp4,
+               "grouped_nvfp4_rht_sr": synth.grouped_nvfp4_sr, "large_moe_nvfp4_fp8": synth.large_moe}[wl]
         w = gen(device=dev)
         p = w.params
         x = w.tensors["x"]
         total, k = x.shape
         S = len(p["split_sections"])
         workspace = mxq.alloc_workspace(total, k, S, p["flags"], dev)
+        given = None
+        if wl == "grouped_nvfp4_rht_given":
+            # supplied section maxima (a single pass over x), here this input's own
+            # measured maxima, so the outputs equal the measured call's; the call also
+            # returns the maxima it measures, as a delayed-scaling caller needs
+            first = mxq.GroupedNVFP4(x, p["split_sections"], p["sign_mask"], p["flags"], workspace=workspace,
+                                     amax_out=True)()
+            given = (first.row_amax.clone(), first.col_amax.clone())
+            del first
 
         def make_call():
             return mxq.GroupedNVFP4(x.clone(), p["split_sections"], p["sign_mask"], p["flags"], p["seed"],
-                                    p["row_offsets"], p["col_offsets"], workspace=workspace)
+                                    p["row_offsets"], p["col_offsets"], workspace=workspace, amax_in=given,
+                                    amax_out=given is not None)
         call = make_call()
         in_bytes = total * k * 2
         alg_bytes = in_bytes
@@ -152,7 +172,10 @@ def main():
         outs = {1: "row", 2: "col", 4: "fp8"}
         desc = (f"{wl} {total}x{k} bf16, {S} sections, outputs "
                 f"{'+'.join(v for b, v in outs.items() if p['flags'] & b)}, "
-                f"{'stochastic rounding' if p['seed'] is not None else 'RNE'}")
+                f"{'stochastic rounding' if p['seed'] is not None else 'RNE'}"
+                f"{', supplied section maxima, measured maxima out' if given is not None else ''}")
+        if given is not None:
+            alg_bytes += 2 * S * 4 + 2 * S * 4       # the maxima in and out
 
     # ---------------------------------------------------------------- input / output sets
     # Steady state: the timed calls cycle over enough copies of the input and the
@@ -195,40 +218,6 @@ def main():
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
 
-    # per-kernel times of K more steady-state calls, from launch marks the library
-    # records on the call's stream around each of its kernels
-    kern = None
-    if grouped:
-        kern = kernel_times(mxq, torch, calls, n_sets, K, stream, ("k_nvfp4_amax", "k_nvfp4_quant"))
-    elif wl == "fp8_blockwise":
-        x = synth.grouped_nvfp4(device=dev).tensors["x"]
-        m, k = x.shape
-
-        def make_call(x=x):
-            xi = x.clone()
-            return lambda: mxq.mxq_quant_fp8_blockwise(xi, mxq.MXQ_FP8_UE8M0, rowwise=True, columnwise=True)
-        call = make_call()
-        in_bytes = m * k * 2
-        alg_bytes = in_bytes + 2 * (m * k + m * (k // 128) * 4)
-        desc = f"fp8 row-wise 1x128 + column-wise 128x1 (transposed), UE8M0 scales, {m}x{k} bf16"
-    elif wl == "swiglu_fp8":
-        w = synth.swiglu_fp8(device=dev)
-        gu = w.tensors["gate_up"]
-        m, n = gu.shape[0], gu.shape[1] // 2
-
-        def make_call():
-            gi = gu.clone()
-            q = torch.empty((m, n), dtype=torch.uint8, device=dev)
-            s = torch.empty((m, n // 128), dtype=torch.float32, device=dev)
-            return lambda: mxq.mxq_swiglu_quant_fp8(gi[:, :n], gi[:, n:], q=q, scales=s)
-        call = make_call()
-        in_bytes = m * n * 2 * 2
-        alg_bytes = in_bytes + m * n + m * (n // 128) * 4
-        desc = f"swiglu -> fp8_1x128, {m} tokens x {n} (fused gate|up bf16 buffer)"
-    elif wl == "dsa_rotate_nvfp4":
-        kern = kernel_times(mxq, torch, calls, n_sets, K, stream,
-                            ("k_dsa_nvfp4_amax", "k_dsa_nvfp4_quant"))
-
     if args.profile:
         del calls
         a = torch.ones(1 << 27, dtype=torch.int16, device=dev)
@@ -236,8 +225,16 @@ def main():
         torch.cuda.synchronize()
         b.copy_(a)                                        # 256 MiB read + 256 MiB written
         torch.cuda.synchronize()
+        ceil = ceiling_lib()
+        sink = torch.empty((ceil.mxq_ceiling_grid(),), dtype=torch.int32, device=dev)
+        c = torch.ones(1 << 26, dtype=torch.int16, device=dev)   # 128 MiB, read twice
+        for _ in range(2):
+            if ceil.mxq_ceiling_read(c.data_ptr(), 2 * c.numel(), sink.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("mxq_ceiling_read failed")
+        torch.cuda.synchronize()
         print(json.dumps({"profile_run": True, "workload": desc, "steps": K, "ms_per_step": round(ms, 5),
-                          "kernel_avg_us_live": kern, "copy_calibration_bytes": 2 * a.numel()}), flush=True)
+                          "copy_calibration_bytes": 2 * a.numel(), "read_calibration_bytes": 2 * c.numel()}),
+              flush=True)
         return
 
     # secondary figures: one call after reading a 1 GiB buffer (caches hold none of
@@ -277,21 +274,15 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * a.numel() * 2 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del a, b
+    # hand-written streaming read and copy over the workload's own sizes, cycling over
+    # as many buffers as the workload's sets (so they come from HBM, as its inputs do)
+    read_gbs, move_gbs = ceilings(torch, dev, stream, in_bytes, alg_bytes - in_bytes, n_sets, K)
 
     value = in_bytes / (ms * 1e-3) / 1e9
     achieved = alg_bytes / (ms * 1e-3) / 1e9              # the whole call (every kernel)
-    if kern is not None:
-        # the dominant kernel: the one with the longest average launch
-        dom = max(kern, key=kern.get)
-        dom_bytes = alg_bytes if dom.endswith("_quant") else in_bytes
-        dom_gbs = dom_bytes / (kern[dom] * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl, dom),
-                    "kernel": dom, "kernel_avg_us": round(kern[dom], 2), "kernel_alg_bytes": dom_bytes,
-                    "call_achieved": round(achieved, 1), "call_frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
+                "unit_of_work": "one whole call (every kernel it launches)", "call_us": round(ms * 1e3, 2)}
     line = {
         "metric": ("input GB/s and % of HBM peak, grouped NVFP4 RHT quant (row+col), 1 MI355X"
                    if wl == "grouped_nvfp4_rht" else f"input GB/s and % of HBM peak, {wl}, 1 MI355X"),
@@ -309,13 +300,14 @@ def main():
         "config": {"workload": desc, "timing": f"steady state: back-to-back calls over {n_sets} input/output sets"},
         "roofline": roofline,
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
-        "kernel_avg_us": kern,
         "algorithmic_bytes": alg_bytes,
         "input_bytes": in_bytes,
         "step_ms_p10_p50_p90": [round(per[int(0.1 * (K - 1))], 5), round(per[K // 2], 5), round(per[int(0.9 * (K - 1))], 5)],
         "cold_single_call_ms_p50": round(cold[len(cold) // 2], 5),
         "warm_ms_per_step": round(warm_ms, 5),
         "hbm_copy_gbs_measured": round(copy_gbs, 1),
+        "read_ceiling_gbs": round(read_gbs, 1),
+        "move_ceiling_gbs": round(move_gbs, 1),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline and wl.startswith("grouped"):
@@ -344,69 +336,9 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def hip_runtime():
-    """The HIP runtime this process already runs on (torch's copy), opened without
-    loading another, for the event flags torch does not expose."""
-    import ctypes
-    path = None
-    with open("/proc/self/maps") as f:
-        for line in f:
-            if "libamdhip64" in line:
-                path = line.split()[-1]
-                break
-    if path is None:
-        raise RuntimeError("the HIP runtime is not loaded")
-    hip = ctypes.CDLL(path, mode=os.RTLD_NOLOAD | ctypes.RTLD_GLOBAL)
-    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    return hip
-
-
-HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000    # hip_runtime_api.h: no cache write-back at the event
-
-
-def kernel_times(mxq, torch, calls, n_sets, K, stream, names):
-    """Average duration (us) of each of the two kernels (`names`) of a call over K
-    steady-state calls, between HIP events the library records on the call's stream
-    just before, between and after them.  The events skip the system-scope fence
-    (hipEventDisableSystemFence): with it, each event writes back and invalidates
-    the caches and adds 3-4 us to the interval it closes."""
-    import ctypes
-    hip = hip_runtime()
-    ev = []
-    try:
-        for _ in range(3 * K):
-            h = ctypes.c_void_p()
-            if hip.hipEventCreateWithFlags(ctypes.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
-                raise RuntimeError("hipEventCreateWithFlags failed")
-            ev.append(h)
-        torch.cuda.synchronize()
-        try:
-            for i in range(K):
-                mxq.mxq_set_launch_marks(*(e.value for e in ev[3 * i:3 * i + 3]))
-                calls[i % n_sets]()
-        finally:
-            mxq.mxq_set_launch_marks()
-        torch.cuda.synchronize()
-        t = ctypes.c_float()
-
-        def elapsed(a, b):
-            if hip.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            return t.value
-        first = sum(elapsed(ev[3 * i], ev[3 * i + 1]) for i in range(K)) / K
-        second = sum(elapsed(ev[3 * i + 1], ev[3 * i + 2]) for i in range(K)) / K
-    finally:
-        for e in ev:
-            hip.hipEventDestroy(e)
-    return {names[0]: round(first * 1e3, 2), names[1]: round(second * 1e3, 2)}
-
-
-def measured_traffic(wl, kernel):
-    """Bytes per launch of `kernel` read + written at HBM, or None when no summary
-    matches the current kernel sources."""
+def measured_traffic(wl):
+    """Bytes per call read + written at the memory side (every kernel of the call), or
+    None when no summary matches the current kernel sources."""
     name = TRAFFIC_SUMMARIES.get(wl)
     if name is None:
         return None
@@ -421,9 +353,76 @@ def measured_traffic(wl, kernel):
     if fields.get("kernel_source_sha256") != kernel_source_digest():
         return None
     try:
-        return int(fields[f"hbm_bytes_per_launch {kernel}"])
+        return int(fields["hbm_bytes_per_call"])
     except (KeyError, ValueError):
         return None
+
+
+_ceiling = None
+
+
+def ceiling_lib():
+    """libmxq_ceiling.so: the streaming read and copy kernels of the measured ceiling."""
+    global _ceiling
+    if _ceiling is None:
+        import ctypes
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_quantization_amd", "_build",
+                            "libmxq_ceiling.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build the library")
+        L = ctypes.CDLL(path)
+        p, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.mxq_ceiling_grid.restype = ctypes.c_int
+        L.mxq_ceiling_read.restype = ctypes.c_int
+        L.mxq_ceiling_read.argtypes = [p, i64, p, p]
+        L.mxq_ceiling_copy.restype = ctypes.c_int
+        L.mxq_ceiling_copy.argtypes = [p, p, i64, p]
+        _ceiling = L
+    return _ceiling
+
+
+def ceilings(torch, dev, stream, in_bytes, out_bytes, n_sets, K):
+    """The measured ceilings beside a workload: GB/s of a streaming read of in_bytes,
+    and of the workload's own data movement done by the plainest kernels, in_bytes read
+    and out_bytes written (a copy of the smaller and a read of the rest of the input),
+    counted as in + out.  Each cycles over n_sets buffers of that size with K launches
+    back to back, the workload's timing method."""
+    L = ceiling_lib()
+    nbytes = (in_bytes + 15) // 16 * 16
+    obytes = max((out_bytes + 15) // 16 * 16, 16)
+    srcs = [torch.ones((nbytes // 2,), dtype=torch.int16, device=dev) for _ in range(n_sets)]
+    dsts = [torch.empty((obytes,), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    sink = torch.empty((L.mxq_ceiling_grid(),), dtype=torch.int32, device=dev)
+    st = stream.cuda_stream
+
+    def run(fn):
+        for i in range(3):
+            fn(i % n_sets)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            fn(i % n_sets)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e-3
+
+    def rd(i):
+        if L.mxq_ceiling_read(srcs[i].data_ptr(), nbytes, sink.data_ptr(), st) != 0:
+            raise RuntimeError("mxq_ceiling_read failed")
+
+    def cp(i):
+        # read the input's bytes and write the outputs' bytes: the copy covers the
+        # smaller of the two, and a read of the rest completes the input
+        n = min(nbytes, obytes)
+        if L.mxq_ceiling_copy(srcs[i].data_ptr(), dsts[i].data_ptr(), n, st) != 0:
+            raise RuntimeError("mxq_ceiling_copy failed")
+        if nbytes > n and L.mxq_ceiling_read(srcs[i].data_ptr() + n, nbytes - n, sink.data_ptr(), st) != 0:
+            raise RuntimeError("mxq_ceiling_read failed")
+
+    t_read = run(rd)
+    t_copy = run(cp)
+    return nbytes / t_read / 1e9, (nbytes + min(nbytes, obytes)) / t_copy / 1e9   # (read, move)
 
 
 def host_threads() -> int:
@@ -435,11 +434,23 @@ def host_threads() -> int:
     return max(1, min(n, 16))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, sample_rows, threads=1):
     """The oracle as it stands (plain C; one host core, or `threads` workers over
     independent section and row-block ranges of the same functions) on the same
     input: the whole workload's sections (or the sections that fit in the first
-    `sample_rows` rows), all requested outputs, timed on this host."""
+    `sample_rows` rows), all requested outputs, timed on this host: the median of
+    three runs."""
     import numpy as np
     import torch
     import oracle
@@ -457,19 +468,19 @@ def cpu_baseline(w, sample_rows, threads=1):
     S = len(sections)
     x = w.tensors["x"][:rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     oracle.lib()
-    reps, t0 = 0, time.perf_counter()
-    while True:                        # repeat to about 10 s of CPU time
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
         oracle.group_rht_quant_nvfp4(x, sections, p["sign_mask"], p["flags"], p["seed"] or 0,
                                      p["row_offsets"][:S] if p["row_offsets"] else None,
                                      p["col_offsets"][:S] if p["col_offsets"] else None, threads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 10:
-            break
+        runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[1]
     what = "the whole workload" if rows == total else f"its first {S} sections ({rows} of {total} rows)"
     where = "on one core" if threads == 1 else f"on {threads} threads"
-    return {"value": round(reps * x.nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what}, all requested outputs, {reps} run(s) in {dt:.1f} s {where}"}
+    return {"value": round(x.nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, all requested outputs, median of 3 runs ({', '.join(f'{r:.2f}' for r in runs)} s) "
+                      f"{where}", "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":

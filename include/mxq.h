@@ -25,9 +25,9 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous: MXQ_OK means the work was enqueued.
  *  - The library never allocates, frees, memsets, synchronizes or reads the
- *    environment; it keeps no global state (the per-thread launch marks, a
- *    measurement hook, aside) and is re-entrant.  Calls in flight at the same time
- *    need distinct workspaces.
+ *    environment; it keeps no global state (the per-device scratch array of
+ *    mxq_group_rht_quant_nvfp4_noalloc aside) and is re-entrant.  Calls in flight
+ *    at the same time need distinct workspaces.
  *  - All argument checks run on the host before anything is enqueued; on an error
  *    nothing is launched and no output is touched.  A failed launch returns
  *    MXQ_ERR_HIP (outputs are then undefined).  There is no fallback path: an
@@ -370,25 +370,6 @@ mxq_status mxq_group_rht_quant_nvfp4_noalloc(const uint16_t* x_bf16, int64_t k,
                                              const mxq_nvfp4_out* columnwise,
                                              const mxq_fp8_out* fp8_rowwise, void* stream);
 
-/* ---------------------------------------------------------------------------
- * Launch marks (measurement).  Not an operation of the method: a hook through
- * which a harness times each kernel of a grouped NVFP4 call on the call's own
- * stream, so that per-kernel times come from the same run as the call's time.
- *
- * before, between, after: hipEvent_t handles owned by the caller (created on the
- * device the calls run on), or all NULL to turn the marks off.  While set, every
- * NVFP4 call (mxq_group_rht_quant_nvfp4*, mxq_hadamard_quant_nvfp4) made from the
- * calling thread records `before` ahead of its first kernel, `between` after the
- * kernel that forms the tensor scales (the amax kernel, or the table kernel when
- * maxima are supplied) and `after` behind the quantize kernel; with more than one
- * launch group per grouped call (more than 32 sections) the marks of the last
- * group are the ones left; a call without rows records `before` only.  The setting is per
- * thread and lasts until changed; the library never creates, waits on or
- * destroys the events.  Returns MXQ_ERR_INVALID_ARGUMENT when some but not all
- * of the three are NULL; a failed record makes the grouped call return
- * MXQ_ERR_HIP.
- * ------------------------------------------------------------------------- */
-mxq_status mxq_set_launch_marks(void* before, void* between, void* after);
 
 #ifdef __cplusplus
 }

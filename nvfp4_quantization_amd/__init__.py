@@ -25,7 +25,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_MISALIGNED",
 
 EXPORTED = ("mxq_status_string", "mxq_version", "mxq_quant_fp8_1x128", "mxq_hadamard_quant_fp8",
             "mxq_group_rht_quant_nvfp4_workspace_size", "mxq_group_rht_quant_nvfp4",
-            "mxq_group_rht_quant_nvfp4_with_amax", "mxq_set_launch_marks",
+            "mxq_group_rht_quant_nvfp4_with_amax",
             "mxq_hadamard_quant_nvfp4_workspace_size", "mxq_hadamard_quant_nvfp4", "mxq_swiglu_quant_fp8",
             "mxq_quant_fp8_blockwise", "mxq_hadamard_quant_fp8_ex", "mxq_group_rht_quant_nvfp4_noalloc")
 MXQ_FP8_UE8M0 = 1
@@ -101,8 +101,6 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_rht_quant_nvfp4_noalloc.restype = ctypes.c_int
         L.mxq_group_rht_quant_nvfp4_noalloc.argtypes = [p, i64, p, i64, ctypes.c_uint16, ctypes.c_uint32, p,
                                                         p, p, p, p]
-        L.mxq_set_launch_marks.restype = ctypes.c_int
-        L.mxq_set_launch_marks.argtypes = [p, p, p]
         _lib = L
     return _lib
 
@@ -143,25 +141,6 @@ def mxq_status_string(status: int) -> str:
 
 def mxq_version() -> str:
     return lib().mxq_version().decode()
-
-
-def mxq_set_launch_marks(before=None, between=None, after=None) -> None:
-    """Per-thread launch marks for timing the kernels of grouped NVFP4 calls: three
-    torch.cuda.Event objects (created with enable_timing=True, recorded once so that
-    the event exists), or all None to turn the marks off."""
-    evs = (before, between, after)
-    if any(e is None for e in evs):
-        if not all(e is None for e in evs):
-            raise ValueError("launch marks: give all three events or none")
-        _check(lib().mxq_set_launch_marks(None, None, None), "mxq_set_launch_marks")
-        return
-    handles = []
-    for e in evs:
-        h = e.cuda_event if hasattr(e, "cuda_event") else int(e)
-        if not h:
-            raise ValueError("launch marks: the event has not been created (record it once first)")
-        handles.append(ctypes.c_void_p(h))
-    _check(lib().mxq_set_launch_marks(*handles), "mxq_set_launch_marks")
 
 
 # ---------------------------------------------------------------------------- FP8 1x128

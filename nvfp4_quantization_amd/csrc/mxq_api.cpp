@@ -41,15 +41,7 @@ bool index2_ok(int64_t rows, int64_t s_r, int64_t cols, int64_t s_c) {
 
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
-thread_local hipEvent_t t_marks[3] = {nullptr, nullptr, nullptr};
-
 }  // namespace
-
-namespace mxq {
-hipError_t launch_mark(int i, hipStream_t stream) {
-    return t_marks[i] ? hipEventRecord(t_marks[i], stream) : hipSuccess;
-}
-}  // namespace mxq
 
 namespace mxq {
 // The argument checks of the grouped call, everything but the workspace (which the
@@ -119,15 +111,6 @@ const char* mxq_status_string(mxq_status s) {
 }
 
 const char* mxq_version(void) { return "mxq 0.1.0 gfx950"; }
-
-mxq_status mxq_set_launch_marks(void* before, void* between, void* after) {
-    const int set = (before != nullptr) + (between != nullptr) + (after != nullptr);
-    if (set != 0 && set != 3) return MXQ_ERR_INVALID_ARGUMENT;
-    t_marks[0] = static_cast<hipEvent_t>(before);
-    t_marks[1] = static_cast<hipEvent_t>(between);
-    t_marks[2] = static_cast<hipEvent_t>(after);
-    return MXQ_OK;
-}
 
 mxq_status mxq_quant_fp8_1x128(const uint16_t* x_bf16, int64_t m, int64_t k, int64_t ldx,
                                uint8_t* q_e4m3, int64_t ldq,

@@ -131,25 +131,40 @@ __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, SEL);
 }
 
-// Stochastic E2M1 rounding with 8 random bits r: grid spacing D = 0.5 / 1 / 2
-// below 2 / 4 / 6; with u = |q| / D = k + f the value rounds up iff
-// floor(256 f) + r >= 256; |q| >= 6 saturates.  Returns the 4-bit code.
-// gfx950's stochastic conversion does exactly this for the first value of a pair
-// when the random operand is r << 24 (its low 24 bits zero): checked against the
-// rule for every FP32 value with |q| in [2^-20, 16) and every r, and on sampled
-// smaller, subnormal and larger values.  (The pair's second value draws on the
-// random operand differently, so each value gets a conversion of its own.)
-__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t r) {
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{q, 0.0f}, r << 24, 1.0f, 0) & 0xFu;
+// The random byte t (0..3) of word w placed at bits 24..31 with the low 24 bits zero,
+// the form the stochastic conversion takes (one byte permute).
+template <int T>
+__device__ __forceinline__ uint32_t rbyte_hi(uint32_t w) {
+    return __builtin_amdgcn_perm(0u, w, ((uint32_t)T << 24) | 0x0C0C0Cu);
 }
 
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).
+// Stochastic E2M1 rounding with 8 random bits r: grid spacing D = 0.5 / 1 / 2
+// below 2 / 4 / 6; with u = |q| / D = k + f the value rounds up iff
+// floor(256 f) + r >= 256; |q| >= 6 saturates.  gfx950's stochastic conversion does
+// exactly this for the first value of a pair when the random operand is r << 24 (its
+// low 24 bits zero): checked against the rule for every FP32 value with |q| in
+// [2^-20, 16) and every r, and on sampled smaller, subnormal and larger values.  (The
+// pair's second value draws on the random operand differently, so each value gets a
+// conversion of its own.)
+//
+// The code of q alone (low nibble of the result, other bits cleared).  The builtin's
+// first operand does not reach the instruction: the compiler gives it a fresh
+// destination register and the bytes it does not write hold that register's earlier
+// contents, so the code is masked out of it and the pair is packed by shifts.
+__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t r_hi) {
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{q, 0.0f}, r_hi, 1.0f, 0) & 0xFu;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each round's two 32 x 32-bit
+// products are formed whole (64 bits), one v_mad_u64_u32 each: the separate low and
+// high multiplies would cost two quarter-rate instructions per product.
 struct u32x4 { uint32_t x, y, z, w; };
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
-        uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+        const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+        const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         u32x4 n;
         n.x = hi1 ^ c.y ^ k0;
         n.y = lo1;
@@ -162,11 +177,6 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
     return c;
 }
 
-// Random byte t (0..15) of a block's Philox output.
-__device__ __forceinline__ uint32_t rbyte(const u32x4& w, int t) {
-    uint32_t word = (t >> 2) == 0 ? w.x : (t >> 2) == 1 ? w.y : (t >> 2) == 2 ? w.z : w.w;
-    return (word >> (8 * (t & 3))) & 0xFFu;
-}
 
 // Cross-lane helpers (wave64).
 __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m) {

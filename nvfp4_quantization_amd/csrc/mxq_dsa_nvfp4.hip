@@ -172,20 +172,17 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_quant(const DsaNvfp4Args a) {
 
 hipError_t launch_hadamard_quant_nvfp4(const DsaNvfp4Args& a, hipStream_t stream) {
     const bool given = a.amax_in != nullptr;
-    hipError_t e = launch_mark(0, stream);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
     if (!given && a.m > 0)
         hipLaunchKernelGGL(k_dsa_nvfp4_amax, dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(k_dsa_nvfp4_scale, dim3(1), dim3(128), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess || a.m == 0) return e;
-    if ((e = launch_mark(1, stream)) != hipSuccess) return e;
     if (given && a.amax_out)
         hipLaunchKernelGGL((k_dsa_nvfp4_quant<true>), dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((k_dsa_nvfp4_quant<false>), dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_mark(2, stream);
+    return hipGetLastError();
 }
 
 }  // namespace mxq

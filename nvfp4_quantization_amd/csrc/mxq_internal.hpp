@@ -139,10 +139,6 @@ namespace mxq {
 mxq_status grouped_check(const uint16_t* x_bf16, int64_t k, const int64_t* split_sections, int64_t num_sections,
                          uint32_t flags, const mxq_nvfp4_out* rowwise, const mxq_nvfp4_out* columnwise,
                          const mxq_fp8_out* fp8_rowwise, const mxq_amax* amax, int64_t* total_rows);
-// Launch marks of the calling thread (mxq_set_launch_marks): records mark i
-// (0 before the first kernel, 1 between the scale and quantize kernels, 2 after)
-// on the stream when marks are set; hipSuccess otherwise.
-hipError_t launch_mark(int i, hipStream_t stream);
 // The quant kernel's variant families (one translation unit each): nearest-even or
 // stochastic rounding, with or without measured maxima out (supplied maxima).
 hipError_t launch_quant_rne(const Nvfp4Group& g, uint32_t flags, hipStream_t stream);

@@ -22,7 +22,6 @@ namespace {
 template <bool ROW, bool COL, bool FP8>
 hipError_t launch_sel(const Nvfp4Group& g, hipStream_t stream) {
     const bool given = g.amax_in_row || g.amax_in_col;
-    if (hipError_t m = launch_mark(0, stream); m != hipSuccess) return m;
     if (given) {
         hipLaunchKernelGGL((k_nvfp4_given<ROW, COL>), dim3(g.num_sections), dim3(64), 0, stream, g);
     } else if (g.total_tiles == 0) {
@@ -39,13 +38,10 @@ hipError_t launch_sel(const Nvfp4Group& g, hipStream_t stream) {
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    if ((e = launch_mark(1, stream)) != hipSuccess) return e;
     const uint32_t flags = (ROW ? 1u : 0u) | (COL ? 2u : 0u) | (FP8 ? 4u : 0u);
     const bool sr = g.sr_row || g.sr_col, aout = given && (g.amax_out_row || g.amax_out_col);
-    e = sr ? (aout ? launch_quant_sr_aout(g, flags, stream) : launch_quant_sr(g, flags, stream))
-           : (aout ? launch_quant_rne_aout(g, flags, stream) : launch_quant_rne(g, flags, stream));
-    if (e != hipSuccess) return e;
-    return launch_mark(2, stream);
+    return sr ? (aout ? launch_quant_sr_aout(g, flags, stream) : launch_quant_sr(g, flags, stream))
+              : (aout ? launch_quant_rne_aout(g, flags, stream) : launch_quant_rne(g, flags, stream));
 }
 }  // namespace
 
@@ -99,10 +95,7 @@ hipError_t launch_nvfp4_group(const Nvfp4Group& g, uint32_t flags, uint32_t* slo
         f.slots = slots;
         f.err = status;
         fused_plan(g, f);
-        if ((e = launch_mark(0, stream)) != hipSuccess || (e = launch_mark(1, stream)) != hipSuccess) return e;
-        e = (g.sr_row || g.sr_col) ? launch_fused_sr(g, f, flags, stream) : launch_fused_rne(g, f, flags, stream);
-        if (e != hipSuccess) return e;
-        return launch_mark(2, stream);
+        return (g.sr_row || g.sr_col) ? launch_fused_sr(g, f, flags, stream) : launch_fused_rne(g, f, flags, stream);
     }
     const bool row = flags & 1u, col = flags & 2u, fp8 = flags & 4u;
     switch ((row ? 1 : 0) | (col ? 2 : 0) | (fp8 ? 4 : 0)) {

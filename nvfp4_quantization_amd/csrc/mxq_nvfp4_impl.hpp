@@ -221,14 +221,15 @@ __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, co
         c = e2m1_pack2<2>(c, q[4], q[5]);
         c = e2m1_pack2<3>(c, q[6], q[7]);
     } else {
+        float q[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float q0 = IEEE ? div_ieee(u[2 * i], d, y) : div_rn(u[2 * i], d, y);
-            const float q1 = IEEE ? div_ieee(u[2 * i + 1], d, y) : div_rn(u[2 * i + 1], d, y);
-            const uint32_t c0 = e2m1_sr(q0, rbyte(rnd, r0 + 2 * i));
-            const uint32_t c1 = e2m1_sr(q1, rbyte(rnd, r0 + 2 * i + 1));
-            c |= (c0 | (c1 << 4)) << (8 * i);
-        }
+        for (int i = 0; i < 8; ++i) q[i] = IEEE ? div_ieee(u[i], d, y) : div_rn(u[i], d, y);
+        // random bytes r0 .. r0 + 7: word r0 / 4 and the next (r0 is 0 or 8)
+        const uint32_t wa = r0 == 0 ? rnd.x : rnd.z, wb = r0 == 0 ? rnd.y : rnd.w;
+        const uint32_t r[8] = {rbyte_hi<0>(wa), rbyte_hi<1>(wa), rbyte_hi<2>(wa), rbyte_hi<3>(wa),
+                               rbyte_hi<0>(wb), rbyte_hi<1>(wb), rbyte_hi<2>(wb), rbyte_hi<3>(wb)};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c |= e2m1_sr(q[i], r[i]) << (4 * i);
     }
     return c;
 }
@@ -435,10 +436,12 @@ __device__ __forceinline__ float row_pass(const Nvfp4Group& G, const uint4 (&p)[
         return block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
     };
     if (SR && G.sr_row) {
+        // two rows at a time, as below: their Philox chains (ten dependent rounds of
+        // quarter-rate multiplies each) overlap
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             put(t, row_block<Enc::Sr>(p, t, g_r, yg_r, tab_r, rnd_of(t)));
-            __builtin_amdgcn_sched_barrier(0);
+            if (t & 1) __builtin_amdgcn_sched_barrier(0);
         }
     } else if (div_mode) {
         // the section's row table has a scale code without a multiplier: exact division
@@ -665,6 +668,7 @@ struct QuantLds {
     uint2 codes[W][kTileCols * 8 + 8 * 8];
     uint8_t sc[W][kTileCols * 8 + 8 * 8];
     uint8_t rsc[kTileRows * 8 * W];                      // row scales of the work-group's tiles
+    uint32_t amax[2][W];                                 // AOUT: each wave's measured maxima (FP32 bits)
 };
 
 // Every output of wave w's tile (token tile T, column tile C of section s), the tile
@@ -718,12 +722,10 @@ __device__ __forceinline__ void quant_passes(const Nvfp4Group& G, uint4 (&p)[16]
             else
                 *reinterpret_cast<uint2*>(dst) = v;
         }
-        if (AOUT && G.amax_out_row) {
+        if (AOUT) {
             // supplied maxima: measure this call's for the caller's next step
             const float wm = wave_max_f32(ra);
-            if (lane == 0)
-                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_row + s), __builtin_bit_cast(uint32_t, wm),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) L.amax[0][w] = __builtin_bit_cast(uint32_t, wm);
         }
         launder(p);
     }
@@ -745,7 +747,7 @@ __device__ __forceinline__ void quant_passes(const Nvfp4Group& G, uint4 (&p)[16]
                 const BlockOut o = column_block<Enc::Sr>(p, j, mask, g_c, yg_c, tab_c, rnd);
                 put(j, o);
                 if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
-                __builtin_amdgcn_sched_barrier(0);
+                if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two columns' Philox chains overlap
             }
         } else if (tab_c[127].x != 0.0f) {
             // the section's column table has a scale code without a multiplier:
@@ -791,12 +793,10 @@ __device__ __forceinline__ void quant_passes(const Nvfp4Group& G, uint4 (&p)[16]
             const uint2 v = *reinterpret_cast<const uint2*>(&lds_sc[(col + (col >> 4)) * 8]);
             *reinterpret_cast<uint2*>(scales_s + ((int64_t)C * kTileCols + col) * (ms >> 4) + T_local * 8) = v;
         }
-        if (AOUT && G.amax_out_col) {
+        if (AOUT) {
             // supplied maxima: measure this call's, max |BF16(y/4)| = BF16(max |y|) / 4
             const float wm = 0.25f * round_bf16(wave_max_f32(col_amax));
-            if (lane == 0)
-                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_col + s), __builtin_bit_cast(uint32_t, wm),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) L.amax[1][w] = __builtin_bit_cast(uint32_t, wm);
         }
         launder(p);
     }
@@ -845,6 +845,32 @@ __device__ __forceinline__ void quant_passes(const Nvfp4Group& G, uint4 (&p)[16]
                                         reinterpret_cast<u32x4v*>(G.fp8_codes + row * k + c0));
             if (cc == 0) G.fp8_scales[row * (k >> 7) + C] = sf;
             __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    if (AOUT && (G.amax_out_row || G.amax_out_col)) {
+        // one atomic maximum per direction for the work-group (non-negative FP32 orders
+        // like its bits): same-address atomics are served one at a time, and one per
+        // wave cost the call about as much as its arithmetic
+        if (W > 1) {
+            __syncthreads();
+        } else {
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (tid == 0) {
+            uint32_t mr = 0, mc = 0;
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                mr = L.amax[0][i] > mr ? L.amax[0][i] : mr;
+                mc = L.amax[1][i] > mc ? L.amax[1][i] : mc;
+            }
+            if (ROW && G.amax_out_row)
+                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_row + s), mr, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (COL && G.amax_out_col)
+                __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(G.amax_out_col + s), mc, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

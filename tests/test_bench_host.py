@@ -1,6 +1,6 @@
 """Host logic of bench.py (no GPU): the one-GPU guard, and the lookup that attaches
-the counter-measured bytes of the dominant kernel to the JSON line only while the
-kernel sources still match the digest recorded with the counters."""
+the counter-measured bytes of a call to the JSON line only while the kernel sources
+still match the digest recorded with the counters, and the host facts it reports."""
 import os
 import subprocess
 import sys
@@ -22,21 +22,20 @@ def test_more_than_one_gpu_is_refused():
 
 def write_summary(path, digest, nbytes):
     path.write_text("# summary\n\n"
-                    f"- hbm_bytes_per_launch k_nvfp4_quant: {nbytes}\n"
+                    f"- hbm_bytes_per_call: {nbytes}\n"
                     f"- kernel_source_sha256: {digest}\n")
 
 
 def test_traffic_used_only_for_matching_sources(tmp_path, monkeypatch):
     f = tmp_path / "traffic.md"
     monkeypatch.setitem(bench.TRAFFIC_SUMMARIES, "grouped_nvfp4_rht", str(f))
-    write_summary(f, bench.kernel_source_digest(), 226627481)
-    assert bench.measured_traffic("grouped_nvfp4_rht", "k_nvfp4_quant") == 226627481
-    assert bench.measured_traffic("grouped_nvfp4_rht", "k_nvfp4_amax") is None      # no figure for it
-    write_summary(f, "0" * 64, 226627481)                                            # sources changed since
-    assert bench.measured_traffic("grouped_nvfp4_rht", "k_nvfp4_quant") is None
+    write_summary(f, bench.kernel_source_digest(), 361316864)
+    assert bench.measured_traffic("grouped_nvfp4_rht") == 361316864
+    write_summary(f, "0" * 64, 361316864)                                            # sources changed since
+    assert bench.measured_traffic("grouped_nvfp4_rht") is None
     f.unlink()
-    assert bench.measured_traffic("grouped_nvfp4_rht", "k_nvfp4_quant") is None
-    assert bench.measured_traffic("dsa_rotate_fp8", "k_nvfp4_quant") is None         # no summary at all
+    assert bench.measured_traffic("grouped_nvfp4_rht") is None
+    assert bench.measured_traffic("dsa_rotate_fp8") is None                          # no summary at all
 
 
 def test_digest_covers_the_kernel_sources():
@@ -47,3 +46,7 @@ def test_digest_covers_the_kernel_sources():
 
 def test_host_threads_is_a_one_gpu_share():
     assert 1 <= bench.host_threads() <= 16
+
+
+def test_cpu_model_is_named():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

@@ -179,15 +179,6 @@ def test_grouped_amax_argument_errors(L):
     assert grouped_amax(L, (A, A, None, None), flags=0) == INVALID
 
 
-@no_gpu
-def test_launch_marks_arguments(L):
-    """Launch marks are three events or none; a partial set is refused and leaves
-    the marks off."""
-    assert L.mxq_set_launch_marks(A, None, None) == INVALID
-    assert L.mxq_set_launch_marks(None, A, A) == INVALID
-    assert L.mxq_set_launch_marks(None, None, None) == 0
-
-
 def dsa4(L, pe=A, ld_pe=64, d_pe=64, nope=A, ld_nope=64, m=8, amax_in=None, amax_out=None, codes=A, scales=A,
          g=A, ws=A, ws_bytes=1 << 20):
     return L.mxq_hadamard_quant_nvfp4(pe, ld_pe, d_pe, nope, ld_nope, m, amax_in, amax_out, codes, scales, g,
