@@ -15,7 +15,8 @@ the HIP-event time of the whole run on the calls' stream divided by the steps
 
 `roofline` is the whole call's: its algorithmic bytes (input read once, every output
 written once) over the call time, against the 8 TB/s HBM peak.  A call of the
-two-kernel form runs two kernels, the second reading the input again; only the call
+three-kernel form runs an amax pass, a per-section scales pass and a quant pass that
+reads the input again; only the call
 as a whole moves the method's bytes, so no single kernel's rate stands for it (the
 per-kernel split is in the committed rocprofv3 summaries).  Beside it: the rate of a
 hand-written streaming read and copy over the same rotating buffer sizes

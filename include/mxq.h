@@ -210,10 +210,11 @@ mxq_status mxq_hadamard_quant_fp8(const uint16_t* pe, int64_t ld_pe, int32_t d_p
  *   global_scale  device float[1]: g (also written for m = 0: the floor scale, or
  *                 the scale of *amax_in)
  *   workspace     device memory of mxq_hadamard_quant_nvfp4_workspace_size(m)
- *                 bytes (16.25 KB of counters, 2 KB of scale table and 4 bytes per
- *                 64 rows, rounded up to 256), 256-byte aligned, ZERO-FILLED BEFORE
- *                 ITS FIRST USE; every call leaves its counters at zero again.  Calls
- *                 that share it must be ordered.  May be NULL when m = 0.
+ *                 bytes (2 KB of scale table and 4 bytes per 64 rows, rounded up
+ *                 to 256), 256-byte aligned; any contents (the call's kernels meet
+ *                 through it in stream order and keep nothing in it between
+ *                 calls).  Calls that share it must be ordered.  May be NULL when
+ *                 m = 0.
  * Requirements: as mxq_hadamard_quant_fp8; codes and block_scales 16-byte aligned,
  * global_scale, amax_in, amax_out 4-byte aligned; m <= 2^31 - 128.  Errors are
  * returned before anything is enqueued.
@@ -269,12 +270,14 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
  *
  * workspace: device memory of at least
  *   mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
- *   bytes (0 when only MXQ_FP8_ROWWISE is requested; otherwise 264 KB plus 8 bytes
- *   per 128 x 128 tile of x), 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE.
- *   It holds per-section counters, per-tile partial maxima and per-section scale
- *   tables through which the two kernels of a call meet; every call leaves the
- *   counters at zero again, so a workspace is zeroed once and then reused.  Calls
- *   that share a workspace must be ordered (same stream, or synchronized).
+ *   bytes (0 when only MXQ_FP8_ROWWISE is requested; otherwise 135,680 bytes plus
+ *   8 bytes per 128 x 128 tile of x, rounded up to 256), 256-byte aligned,
+ *   ZERO-FILLED BEFORE ITS FIRST USE.  It holds partial maxima and per-section
+ *   scale tables through which the kernels of a call meet in stream order, and the
+ *   single-read form's partial words and error word, which must start at zero;
+ *   every call leaves them at zero again, so a workspace is zeroed once and then
+ *   reused.  Calls that share a workspace must be ordered (same stream, or
+ *   synchronized).
  *
  * Requirements: k % 128 == 0, every m_s % 128 == 0 (else MXQ_ERR_MISALIGNED, with
  * no unfused fallback); 1 <= num_sections <= MXQ_MAX_SECTIONS; k <= 2^26,
@@ -355,7 +358,7 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
  * per device, on the first call with that device current, and the words the call
  * needs at zero are cleared then by a fill kernel on that call's stream).  A call
  * whose workspace would exceed the array (mxq_group_rht_quant_nvfp4_workspace_size
- * above MXQ_NOALLOC_SCRATCH_BYTES, e.g. more than 96,704 tiles of 128 x 128) gives
+ * above MXQ_NOALLOC_SCRATCH_BYTES, e.g. more than 114,112 tiles of 128 x 128) gives
  * MXQ_ERR_UNSUPPORTED before anything is enqueued.  The call itself allocates
  * nothing (no hipMalloc, no allocating library routine).  The stream must belong to
  * the current device.  Every call on one GPU uses that GPU's array: calls that

@@ -278,7 +278,7 @@ def mxq_hadamard_quant_nvfp4_workspace_size(m: int) -> int:
 
 
 class HadamardNVFP4:
-    """A prepared DSA rotate + NVFP4 call: outputs and a zero-filled workspace are
+    """A prepared DSA rotate + NVFP4 call: outputs and a workspace (any contents) are
     allocated once; each call runs the quantizer on `pe`, `nope` as they are then.
     pe: [m][d_pe], nope: [m][128-d_pe] BF16 with unit column stride (either may be
     None when empty).  amax_in: None (measure), a float, or a device float32 tensor
@@ -304,7 +304,7 @@ class HadamardNVFP4:
         self.amax_in = amax_in
         need = mxq_hadamard_quant_nvfp4_workspace_size(self.m)
         if workspace is None:
-            workspace = torch.zeros((max(need, 256),), dtype=torch.uint8, device=dev)
+            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
         self.workspace = workspace
 
     def __call__(self, stream=None) -> DsaNVFP4Result:
@@ -361,31 +361,24 @@ def alloc_nvfp4_outputs(total_rows: int, k: int, num_sections: int, flags: int, 
     return r
 
 
-WORKSPACE_COUNTERS = 32 * 17          # per launch group: 16 group counters and a top counter per section
-WORKSPACE_COUNTER_STRIDE = 256     # bytes between two counters
-
-
 def alloc_workspace(total_rows: int, k: int, num_sections: int, flags: int, device) -> torch.Tensor:
-    """Zero-filled workspace of the size the library asks for (the grouped call
-    needs its counters at zero before the first use and leaves them at zero)."""
+    """Zero-filled workspace of the size the library asks for (the single-read form
+    needs its partial words and error word at zero before the first use and leaves
+    them at zero)."""
     n = mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
     return torch.zeros((max(n, 256),), dtype=torch.uint8, device=device)
 
 
-WORKSPACE_STATUS = WORKSPACE_COUNTERS * WORKSPACE_COUNTER_STRIDE   # byte offset of the error word
-WORKSPACE_SLOTS = WORKSPACE_STATUS + 512 + 32 * 2 * 128 * 16          # the single-read form's partial words
+WORKSPACE_STATUS = 0                                  # byte offset of the single-read form's error word
+WORKSPACE_SLOTS = WORKSPACE_STATUS + 512 + 32 * 2 * 128 * 16   # the single-read form's partial words
 WORKSPACE_SLOTS_BYTES = 4 * 1024
+WORKSPACE_FIXED = WORKSPACE_SLOTS + WORKSPACE_SLOTS_BYTES      # then the amax pass's partials
 
 
-def workspace_counters_clear(workspace: torch.Tensor) -> bool:
-    """After a finished call: True when every section counter is back at zero, and so
-    are the single-read form's error word and partial words."""
-    n = min(workspace.numel(), WORKSPACE_COUNTERS * WORKSPACE_COUNTER_STRIDE)
-    words = workspace[:n].view(torch.int32)[:: WORKSPACE_COUNTER_STRIDE // 4]
-    if not bool((words == 0).all().item()):
-        return False
-    if workspace.numel() > WORKSPACE_STATUS and int(workspace[WORKSPACE_STATUS:WORKSPACE_STATUS + 4]
-                                                    .view(torch.int32).item()) != 0:
+def workspace_protocol_clear(workspace: torch.Tensor) -> bool:
+    """After a finished call: True when the single-read form's error word and partial
+    words are back at zero (the only workspace words a call needs at zero)."""
+    if int(workspace[WORKSPACE_STATUS:WORKSPACE_STATUS + 4].view(torch.int32).item()) != 0:
         return False
     slots = workspace[WORKSPACE_SLOTS:WORKSPACE_SLOTS + WORKSPACE_SLOTS_BYTES]
     return bool((slots == 0).all().item())

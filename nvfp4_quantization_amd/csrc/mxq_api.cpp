@@ -299,7 +299,6 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
     a.global_scale = global_scale;
     a.amax_in = amax_in;
     a.amax_out = amax_out;
-    a.ctrl = m > 0 ? reinterpret_cast<uint32_t*>(ws + mxq::kDsaCtrlOffset) : nullptr;
     a.table = m > 0 ? reinterpret_cast<float4*>(ws + mxq::kDsaTableOffset) : nullptr;
     a.partials = m > 0 ? reinterpret_cast<float*>(ws + mxq::kDsaPartialsOffset) : nullptr;
     return mxq::launch_hadamard_quant_nvfp4(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MXQ_OK
@@ -311,9 +310,9 @@ size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k, i
     if (total_rows < 0 || k <= 0 || num_sections <= 0) return 0;
     if (total_rows > kMaxRows || k > kMaxGroupK) return 0;         // outside the supported profile
     if (!(flags & (MXQ_ROWWISE | MXQ_COLUMNWISE))) return 0;
-    // counters, status line, scale tables and the single-read form's partial words
-    // of one launch group, then one 8-byte partial per 128 x 128 tile of the largest
-    // group (bounded by all rows)
+    // status line, scale tables and the single-read form's partial words of one
+    // launch group, then the amax pass's 8-byte partials (at most one per 128 x 128
+    // tile of the largest group, bounded by all rows)
     const int64_t tiles = (total_rows / 128) * ceil_div(k, 128);
     return (size_t)round256(mxq::kPartialsOffset + 8 * tiles);
 }
@@ -382,7 +381,6 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
             g.fp8_codes = fp8_rowwise->codes + row0 * k;
             g.fp8_scales = fp8_rowwise->scales + row0 * (k / 128);
         }
-        g.ctrl = reinterpret_cast<uint32_t*>(ws + mxq::kCtrlOffset);
         g.tables = reinterpret_cast<float4*>(ws + mxq::kTablesOffset);
         g.partials = reinterpret_cast<uint64_t*>(ws + mxq::kPartialsOffset);
         g.seed = sr ? sr->seed : 0;

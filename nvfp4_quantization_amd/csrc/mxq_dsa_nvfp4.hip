@@ -42,14 +42,9 @@ __device__ __forceinline__ void halves(const float (&v)[32], float (&h0)[16], fl
 
 }  // namespace
 
-// Phase A: max |y| of the work-group's 64 rows into its partial.  The work-group
-// that finishes last folds the partials into the tensor scale and writes the
-// table.  Which one that is comes from two levels of counters: work-group i counts
-// in at group counter i % 64, and the last of each group at the top counter, so
-// that no counter takes more than about n_wg / 64 atomics (a single counter for all
-// 4096 work-groups serialized them and cost 40 us).
+// Phase A: max |y| of the work-group's 64 rows into its partial (an ordinary
+// store; the scale kernel that follows on the stream folds the partials).
 __global__ __launch_bounds__(256) void k_dsa_nvfp4_amax(const DsaNvfp4Args a) {
-    __shared__ uint32_t last_s;
     __shared__ float red[4];
     const int quarter = threadIdx.x & 3;
     const int64_t r = (int64_t)blockIdx.x * kDsaRows + (threadIdx.x >> 2);
@@ -64,57 +59,44 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_amax(const DsaNvfp4Args a) {
     const float m = __builtin_fmaxf(absmax16(h0), absmax16(h1));
     const float lane = m != m ? 0.0f : round_bf16(m * k_inv_sqrt128());
     const float wg = wg_max(lane, red);
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.partials) + blockIdx.x, __builtin_bit_cast(uint32_t, wg),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): the partial is stored
-        const int grp = (int)(blockIdx.x % kDsaGroups);
-        const int n_grp = (a.n_wg - grp + kDsaGroups - 1) / kDsaGroups;
-        uint32_t last = 0;
-        if (__hip_atomic_fetch_add(a.ctrl + grp * kDsaCtrlStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            (uint32_t)(n_grp - 1)) {
-            const int groups = a.n_wg < kDsaGroups ? a.n_wg : kDsaGroups;
-            last = __hip_atomic_fetch_add(a.ctrl + kDsaGroups * kDsaCtrlStride, 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(groups - 1);
-        }
-        last_s = last;
-    }
-    __syncthreads();
-    if (!last_s) return;
-
-    // The last work-group: every partial is in.  Non-negative floats order like
-    // their bit patterns; 16 loads in flight per thread per round.
-    uint32_t A = 0;
-    for (int i0 = threadIdx.x; i0 < a.n_wg; i0 += 256 * 16) {
-        uint32_t v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-            v[u] = i0 + 256 * u < a.n_wg ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(a.partials) + i0 + 256 * u,
-                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                         : 0u;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) A = v[u] > A ? v[u] : A;
-    }
-    const float amax = wg_max(__builtin_bit_cast(float, A), red);
-    const float g = tensor_scale(amax);
-    if (threadIdx.x < 128) a.table[threadIdx.x] = table_entry((int)threadIdx.x, g, false);
-    if (threadIdx.x <= kDsaGroups)                                 // ready for the next call
-        __hip_atomic_store(a.ctrl + threadIdx.x * kDsaCtrlStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
-        *a.global_scale = g;
-        if (a.amax_out) *a.amax_out = amax;
-    }
+    if (threadIdx.x == 0) a.partials[blockIdx.x] = wg;
 }
 
-// The tensor scale and the scale table from the supplied amax, or from A = 0 for a
-// tensor without rows.  With a supplied amax the measured-amax output is zeroed
-// here and raised by the quantize kernel.
-__global__ __launch_bounds__(128) void k_dsa_nvfp4_scale(const DsaNvfp4Args a) {
-    const float g = tensor_scale(a.amax_in ? *a.amax_in : 0.0f);
-    if (a.m > 0) a.table[threadIdx.x] = table_entry((int)threadIdx.x, g, false);
-    if (threadIdx.x == 0) {
+// The tensor scale and the scale table (one 1024-thread work-group): from the
+// partials of phase A, or from the supplied amax (then the measured-amax output is
+// zeroed here and raised by the quantize kernel), or from A = 0 for a tensor
+// without rows.
+constexpr int kDsaScaleThreads = 1024;
+__global__ __launch_bounds__(kDsaScaleThreads) void k_dsa_nvfp4_scale(const DsaNvfp4Args a) {
+    __shared__ uint32_t red[kDsaScaleThreads / 64];
+    const int tid = (int)threadIdx.x;
+    float amax = 0.0f;
+    if (a.amax_in) {
+        amax = *a.amax_in;
+    } else if (a.m > 0) {
+        // non-negative floats order like their bit patterns; 8 loads in flight per
+        // thread per round
+        uint32_t A = 0;
+        const uint32_t* const p = reinterpret_cast<const uint32_t*>(a.partials);
+        for (int i0 = tid; i0 < a.n_wg; i0 += kDsaScaleThreads * 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = i0 + kDsaScaleThreads * u < a.n_wg ? p[i0 + kDsaScaleThreads * u] : 0u;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) A = v[u] > A ? v[u] : A;
+        }
+        A = wave_max_u32(A);
+        if ((tid & 63) == 0) red[tid >> 6] = A;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kDsaScaleThreads / 64; ++i) A = red[i] > A ? red[i] : A;
+        amax = __builtin_bit_cast(float, A);
+    }
+    const float g = tensor_scale(amax);
+    if (a.m > 0 && tid < 128) a.table[tid] = table_entry(tid, g, false);
+    if (tid == 0) {
         *a.global_scale = g;
-        if (a.amax_out) *a.amax_out = 0.0f;
+        if (a.amax_out) *a.amax_out = a.amax_in ? 0.0f : amax;
     }
 }
 
@@ -173,10 +155,11 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_quant(const DsaNvfp4Args a) {
 hipError_t launch_hadamard_quant_nvfp4(const DsaNvfp4Args& a, hipStream_t stream) {
     const bool given = a.amax_in != nullptr;
     hipError_t e = hipSuccess;
-    if (!given && a.m > 0)
+    if (!given && a.m > 0) {
         hipLaunchKernelGGL(k_dsa_nvfp4_amax, dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(k_dsa_nvfp4_scale, dim3(1), dim3(128), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_dsa_nvfp4_scale, dim3(1), dim3(kDsaScaleThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess || a.m == 0) return e;
     if (given && a.amax_out)
         hipLaunchKernelGGL((k_dsa_nvfp4_quant<true>), dim3((unsigned)a.n_wg), dim3(256), 0, stream, a);

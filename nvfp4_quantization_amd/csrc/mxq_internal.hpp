@@ -56,11 +56,12 @@ struct DsaArgs {
 hipError_t launch_hadamard_quant_fp8(const DsaArgs& a, hipStream_t stream, bool ue8m0 = false);
 
 // ---------------------------------------------------------------- DSA rotate + NVFP4
-// Two kernels: the first rotates 64 rows per 256-thread work-group and stores the
-// work-group's max |y| as a partial; the work-group that finishes last (two levels
-// of counters tell which) folds the partials into the tensor scale, writes the
-// scale table and resets the counters; the second rotates again and encodes.  With
-// a supplied amax a one-work-group kernel forms the scale and the table instead.
+// Three kernels on the caller's stream: the first rotates 64 rows per 256-thread
+// work-group and stores the work-group's max |y| as a partial; a one-work-group
+// kernel folds the partials into the tensor scale and writes the scale table; the
+// third rotates again and encodes.  With a supplied amax the first is skipped and
+// the second takes the supplied value.  The kernels meet only through the stream
+// order, so the workspace holds no state between calls.
 struct DsaNvfp4Args {
     const uint16_t* pe;
     const uint16_t* nope;
@@ -72,29 +73,27 @@ struct DsaNvfp4Args {
     float* global_scale;              // [1]
     const float* amax_in;             // [1] or null: measure
     float* amax_out;                  // [1] or null
-    uint32_t* ctrl;                   // workspace: kDsaGroups group counters and the top counter
     float4* table;                    // workspace: 128 scale-table entries
     float* partials;                  // workspace: one max per work-group
 };
 hipError_t launch_hadamard_quant_nvfp4(const DsaNvfp4Args& a, hipStream_t stream);
-// Workspace layout of the DSA NVFP4 call (byte offsets): counters (each on its own
-// 256-byte line: group counter g at word g * kDsaCtrlStride, the top counter after
-// them), the scale table, one partial per work-group.
-constexpr int kDsaGroups = 64;
-constexpr int kDsaCtrlStride = 64;
-constexpr int64_t kDsaCtrlOffset = 0;
-constexpr int64_t kDsaTableOffset = (int64_t)(kDsaGroups + 1) * kDsaCtrlStride * 4;
+// Workspace layout of the DSA NVFP4 call (byte offsets): the scale table, then one
+// partial per work-group.
+constexpr int64_t kDsaTableOffset = 0;
 constexpr int64_t kDsaPartialsOffset = kDsaTableOffset + 128 * 16;
 
 // ---------------------------------------------------------------- grouped NVFP4
-// One launch group per at most kGroupSections sections.  A group runs two kernels
-// on the caller's stream, one wave per 128 x 128 tile in each (with a caller-supplied
-// amax, a small per-section kernel that builds the tables replaces the first):
-//   amax    max |x| and max |H16 D x| of the tile into a per-tile partial; the
-//           section's last tile (a counter tells which) folds the partials into
-//           the two tensor scales, writes the section's (d, 1/d) tables and resets
-//           the counter for the next call;
-//   quant   every output of the tile.
+// One launch group per at most kGroupSections sections.  A group runs three kernels
+// on the caller's stream (with caller-supplied maxima, the last two):
+//   amax    one wave per 128 x 128 tile: max |x| and max |H16 D x| of the tile,
+//           one partial per work-group;
+//   scales  one work-group per section: folds the section's partials (or takes
+//           the supplied maxima) into the two tensor scales and writes the
+//           section's (d, 1/d, multiplier) tables;
+//   quant   one wave per tile: every output of the tile.
+// They meet only through the stream order, so the workspace holds no state between
+// calls of this form.  The single-read form (one kernel) replaces all three when
+// the whole group is resident on the chip at once.
 constexpr int kGroupSections = 32;
 constexpr int kTileRows = 128;        // token tile
 constexpr int kTileCols = 128;        // column tile
@@ -110,9 +109,8 @@ struct Nvfp4Group {
     uint8_t* col_scales;
     float* row_global;                // at the group's first section
     float* col_global;
-    uint32_t* ctrl;                   // workspace: per-section counters
     float4* tables;                   // workspace: per-section scale tables
-    uint64_t* partials;               // workspace: one (row, column) amax pair per tile
+    uint64_t* partials;               // workspace: one (row, column) amax pair per amax work-group
     uint64_t seed;
     uint32_t sign_mask;
     uint32_t sr_row, sr_col;
@@ -180,19 +178,15 @@ hipError_t fused_blocks_per_cu_rne(uint32_t flags, int* blocks);
 hipError_t fused_blocks_per_cu_sr(uint32_t flags, int* blocks);
 
 // Workspace layout (byte offsets):
-//   kCtrlOffset    section s: kCtrlGroups group counters and a top counter, each on
-//                  its own 256-byte line, at words kCtrlStride * ((kCtrlGroups + 1) * s + i)
 //   kStatusOffset  two 256-byte lines; word 0 is the single-read form's error word
 //   kTablesOffset  section s, direction dir (0 row, 1 column), scale code c:
 //                  float4 at index (s * 2 + dir) * 128 + c = (d, 1/d, multiplier, 0)
 //   kSlotsOffset   the single-read form's partial words, one per item (at most
-//                  kFusedMaxItems), zero between calls; the two-kernel form never
+//                  kFusedMaxItems), zero between calls; the three-kernel form never
 //                  touches them, so calls of either form can share a workspace
-//   kPartialsOffset  one 8-byte partial per 128 x 128 tile (two-kernel form)
-constexpr int kCtrlStride = 64;
-constexpr int kCtrlGroups = 16;
-constexpr int64_t kCtrlOffset = 0;
-constexpr int64_t kStatusOffset = (int64_t)kGroupSections * (kCtrlGroups + 1) * kCtrlStride * 4;
+//   kPartialsOffset  one 8-byte partial per amax work-group (at most one per 128 x 128
+//                  tile; three-kernel form)
+constexpr int64_t kStatusOffset = 0;
 constexpr int64_t kTablesOffset = kStatusOffset + 512;
 constexpr int64_t kTablesBytes = (int64_t)kGroupSections * 2 * 128 * 16;
 constexpr int64_t kSlotsOffset = kTablesOffset + kTablesBytes;

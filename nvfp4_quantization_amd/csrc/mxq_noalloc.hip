@@ -9,7 +9,7 @@
 // stand-in, not a device address): once per device, with that device current, the
 // first call on it looks up the device address with hipGetSymbolAddress and keeps
 // it, and uses only that address afterwards.  The same first call clears the words
-// the grouped call needs at zero (its completion counters, error word and partial
+// the grouped call needs at zero (the single-read form's error word and partial
 // words) with a fill kernel on the caller's stream; every finished call leaves them
 // at zero again.  All calls on one GPU share that GPU's array, so calls that
 // overlap on one GPU (different streams, or different host threads without
@@ -52,8 +52,8 @@ hipError_t device_scratch(hipStream_t stream, void** out) {
         void* ptr = nullptr;
         d.status = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
         if (d.status != hipSuccess) return;
-        // the counters, status lines, tables and partial words of the grouped call: the
-        // protocol words among them must start at zero
+        // the status lines, tables and single-read partial words of the grouped call:
+        // the protocol words among them must start at zero
         const int64_t words = mxq::kPartialsOffset / 4;
         hipLaunchKernelGGL(k_clear_words, dim3(64), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), words);
         d.status = hipGetLastError();

@@ -1,6 +1,6 @@
 // mxq_nvfp4.hip -- grouped NVFP4 quantization with a 16-point RHT on the
-// column-wise operand (gfx950): the amax, supplied-amax and empty-group kernels and
-// the launch plan; the quant kernel variants are instantiated in
+// column-wise operand (gfx950): the amax, scales and empty-group kernels and the
+// launch plan; the quant kernel variants are instantiated in
 // mxq_nvfp4_quant_*.hip.  The method and the kernels' design are described in
 // mxq_nvfp4_impl.hpp.
 #include "mxq_nvfp4_impl.hpp"
@@ -22,22 +22,26 @@ namespace {
 template <bool ROW, bool COL, bool FP8>
 hipError_t launch_sel(const Nvfp4Group& g, hipStream_t stream) {
     const bool given = g.amax_in_row || g.amax_in_col;
-    if (given) {
-        hipLaunchKernelGGL((k_nvfp4_given<ROW, COL>), dim3(g.num_sections), dim3(64), 0, stream, g);
-    } else if (g.total_tiles == 0) {
+    if (!given && g.total_tiles == 0) {
         hipLaunchKernelGGL((k_nvfp4_empty<ROW, COL>), dim3(1), dim3(64), 0, stream, g);
         return hipGetLastError();
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || g.total_tiles == 0) return e;
-    if (!given) {
-        if (g.total_tiles % 4 == 0)
+    hipError_t e = hipSuccess;
+    if (given) {
+        hipLaunchKernelGGL((k_nvfp4_scales<ROW, COL, true>), dim3(g.num_sections), dim3(kScalesThreads), 0, stream,
+                           g, 1);
+    } else {
+        // four column tiles per work-group when they always share a token tile
+        const int tpp = g.n_ctiles % 4 == 0 ? 4 : 1;
+        if (tpp == 4)
             hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL, 4>), dim3((unsigned)(g.total_tiles / 4)), dim3(256), 0, stream, g);
         else
             hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL, 1>), dim3((unsigned)g.total_tiles), dim3(64), 0, stream, g);
-        e = hipGetLastError();
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_nvfp4_scales<ROW, COL, false>), dim3(g.num_sections), dim3(kScalesThreads), 0, stream,
+                           g, tpp);
     }
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || g.total_tiles == 0) return e;
     const uint32_t flags = (ROW ? 1u : 0u) | (COL ? 2u : 0u) | (FP8 ? 4u : 0u);
     const bool sr = g.sr_row || g.sr_col, aout = given && (g.amax_out_row || g.amax_out_col);
     return sr ? (aout ? launch_quant_sr_aout(g, flags, stream) : launch_quant_sr(g, flags, stream))
@@ -69,7 +73,7 @@ static void fused_plan(const Nvfp4Group& g, Nvfp4Fused& f) {
 // the whole input is read in one burst and each section is quantized as soon as its
 // last tile has arrived.  Larger groups would run as two or more batches in which
 // the loads of one batch and the quantizing of the previous one barely overlap; the
-// two-kernel form (whose second read comes partly from the Infinity Cache and
+// three-kernel form (whose second read comes partly from the Infinity Cache and
 // overlaps its arithmetic) is faster for them (measured on MI355X: 40.1 against
 // 46.6 us for 8192 x 4096 in 8 sections, 512 items; 78.9 against 74.0 us for 16384 x
 // 4096, 1024 items).

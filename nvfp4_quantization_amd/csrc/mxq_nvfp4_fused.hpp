@@ -113,57 +113,6 @@ __device__ __forceinline__ void tile_maxima(const uint4 (&p)[16][2], uint32_t si
     cmax = mc;
 }
 
-// The section's scale tables built by a 256-thread work-group, one entry per
-// thread (direction threadIdx >> 7, scale code threadIdx & 127), into the
-// workspace and into tab.  The entries are those of build_tables: every nonzero
-// E4M3 value is (1 + m/8) 2^e, so lanes 0..7 of each wave search the multiplier of
-// the representative 1 + m/8 of their direction once, and each entry takes it
-// scaled by 2^-e when its own d and fl(1/d) are the representative's scaled exactly
-// and g < 2^100 keeps the search's values normal; it searches on its own otherwise.
-// Entry 127's first word flags a direction with a code that has no multiplier.
-template <bool ROW, bool COL>
-__device__ __forceinline__ void build_tables_wg(const Nvfp4Group& G, int s, float g_r, float g_c,
-                                                float4 (&tab)[2][128], uint32_t* sh_none, int tid) {
-    const int e = tid, lane = e & 63;
-    const int dir = e >> 7, code = e & 127;                     // dir is wave-uniform
-    const bool active = dir == 0 ? ROW : COL;
-    const float g = dir ? g_c : g_r;
-    float rep_ym = 0.0f;
-    if (active && lane < 8) {
-        float d = (1.0f + (float)lane * 0.125f) * g;
-        float y = 1.0f / d;
-        if (dir) { d *= 4.0f; y *= 0.25f; }
-        rep_ym = product_multiplier(d, y);
-    }
-    float4 ent = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    bool none = false;
-    if (active) {
-        const float v = e4m3_value((uint32_t)code);
-        const uint32_t vb = __builtin_bit_cast(uint32_t, v);
-        const int m = (int)((vb >> 20) & 7), ex = (int)((vb >> 23) & 0xFF) - 127;
-        const float cls_ym = __shfl(rep_ym, m, 64);
-        if (code == 0 || code == 127) {
-            ent = table_entry(code, g, dir == 1);
-        } else {
-            float d = v * g, y = 1.0f / d;
-            float rd = (1.0f + (float)m * 0.125f) * g, ry = 1.0f / rd;
-            if (dir == 1) { d *= 4.0f; y *= 0.25f; rd *= 4.0f; ry *= 0.25f; }
-            const bool scaled = g < 0x1p100f && d == __builtin_ldexpf(rd, ex) && y == __builtin_ldexpf(ry, -ex);
-            const float ym = scaled ? __builtin_ldexpf(cls_ym, -ex) : product_multiplier(d, y);
-            ent = make_float4(d, y, ym, k_keep_codes());
-        }
-        none = ent.z < 0.0f;
-    }
-    const bool any = __ballot(none) != 0;
-    if (lane == 0) sh_none[e >> 6] = any ? 1u : 0u;
-    __syncthreads();
-    if (active) {
-        if (code == 127) ent.x = (sh_none[2 * dir] | sh_none[2 * dir + 1]) ? 1.0f : 0.0f;
-        G.tables[(s * 2 + dir) * 128 + code] = ent;
-        tab[dir][code] = ent;
-    }
-}
-
 }  // namespace
 
 // LDS of the single-read kernel.

@@ -9,15 +9,16 @@
 // has the input dtype; a separate column-wise RNG).
 //
 // The FP32 tensor scale of a section needs the section's amax before any code is
-// final, so a call runs two kernels per group of sections, one wave per 128 x 128
-// tile in each:
+// final, so a call runs three kernels per group of sections:
 //
-//   k_nvfp4_amax   max |x| and max |H16 D x| of the tile (a per-tile partial).
-//                  The last tile of a section to finish (an agent-scope counter
-//                  tells which) folds the section's partials into the two tensor
-//                  scales, writes the section's scale tables and puts the counter
-//                  back to zero, so the workspace is ready for the next call.
-//   k_nvfp4_quant  re-reads the tile (partly from the Infinity Cache) and writes
+//   k_nvfp4_amax   one wave per 128 x 128 tile: max |x| and max |H16 D x| of the
+//                  tile, one partial per work-group (ordinary stores).
+//   k_nvfp4_scales one work-group per section: folds the section's partials into
+//                  the two tensor scales and writes the section's scale tables.
+//                  The kernels meet only through the stream order: no counters,
+//                  no waits, and nothing in the workspace outlives the call.
+//   k_nvfp4_quant  one wave per tile: re-reads the tile (partly from the Infinity
+//                  Cache) and writes
 //                  every requested output: the row pass first (a row block needs
 //                  only its own row, so it starts as the rows arrive), then the
 //                  column pass (all 16 rows of each column block), then FP8.
@@ -48,13 +49,6 @@
 namespace mxq {
 
 namespace {
-
-__device__ __forceinline__ uint64_t ws_load64(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ws_store64(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Tensor scale g = fl(max(A, F(1e-10)) * F(1/2688)).
 __device__ __forceinline__ float tensor_scale(float amax) {
@@ -290,11 +284,25 @@ __device__ __forceinline__ void amax_quarter(const uint2 (&v)[16], uint32_t sign
 #pragma unroll
                 for (int t = 0; t < 16; ++t) rmax = __builtin_fmaxf(rmax, __builtin_fabsf(f[t]));
             }
-            butterfly16(f);
-            nan |= f[0] != f[0];                    // a NaN input reaches every output
-            // NaN outputs are quiet, and max ignores them
+            // stages h = 1, 2, 4; the last stage is not formed: for its pair (a, b) the
+            // larger of |fl(a + b)| and |fl(a - b)| is fl(|a| + |b|) (rounding is
+            // monotone and symmetric)
 #pragma unroll
-            for (int t = 0; t < 16; ++t) mc = __builtin_fmaxf(mc, __builtin_fabsf(f[t]));
+            for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i & h) continue;
+                    const float x0 = f[i], x1 = f[i + h];
+                    f[i] = x0 + x1;
+                    f[i + h] = x0 - x1;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float m = __builtin_fabsf(f[i]) + __builtin_fabsf(f[i + 8]);
+                if (i == 0) nan |= m != m;          // depends on all 16 inputs: a NaN input reaches it
+                mc = __builtin_fmaxf(mc, m);        // NaN values are quiet, and max ignores them
+            }
         }
     }
 }
@@ -477,80 +485,84 @@ __device__ __forceinline__ float4 table_entry(int code, float g, bool quarter) {
     return make_float4(d, y, product_multiplier(d, y), k_keep_codes());
 }
 
-// Scale tables of section s (row-wise, then column-wise), built by one wave.  Entry
-// 127's first word flags a direction with a scale code that has no multiplier (its
-// exact ties need opposite roundings): that direction's pass then divides exactly.
+}  // namespace
+
+// ---------------------------------------------------------------- the kernels
+// Scale tables of section s (row-wise, then column-wise), one entry per thread
+// (direction tid >> 7, scale code tid & 127; threads 256 and up take no entry),
+// into the workspace and, when tab is given, into it as well.  Entry 127's first
+// word flags a direction with a scale code that has no multiplier (its exact ties
+// need opposite roundings): that direction's pass then divides exactly.
 //
 // Every nonzero E4M3 value is (1 + m/8) 2^e, so the divisors d of codes that share
 // m differ by exact powers of two, and so do their critical inputs, reciprocals and
-// candidate multipliers, with the same quotients and products.  Lanes 0..15 search
-// the multiplier of the representative 1 + m/8 (m = lane & 7, direction lane >> 3)
-// once; each entry takes it scaled by 2^-e when its own d and fl(1/d) are the
-// representative's scaled exactly and g < 2^100 keeps every intermediate value of
-// the search normal and finite, and searches on its own otherwise.
+// candidate multipliers, with the same quotients and products.  Lanes 0..7 of each
+// direction's first wave search the multiplier of the representative 1 + m/8
+// (m = lane) once; each entry takes it scaled by 2^-e when its own d and fl(1/d)
+// are the representative's scaled exactly and g < 2^100 keeps every intermediate
+// value of the search normal and finite, and searches on its own otherwise.
+// Every thread of the work-group calls it (it holds a barrier).  sh_none: 4 words
+// of LDS.
 template <bool ROW, bool COL>
-__device__ __forceinline__ void build_tables(const Nvfp4Group& G, int s, float g_r, float g_c) {
-    const int lane = threadIdx.x & 63;
-    const float rep_m = 1.0f + (float)(lane & 7) * 0.125f;
+__device__ __forceinline__ void build_tables_wg(const Nvfp4Group& G, int s, float g_r, float g_c,
+                                                float4 (*tab)[128], uint32_t* sh_none, int tid) {
+    const int lane = tid & 63;
+    const bool in = tid < 256;
+    const int dir = (tid >> 7) & 1, code = tid & 127;           // dir is wave-uniform
+    const bool active = in && (dir == 0 ? ROW : COL);
+    const float g = dir ? g_c : g_r;
     float rep_ym = 0.0f;
-    if (lane < 16) {
-        const bool quarter = lane >= 8;
-        float d = rep_m * (quarter ? g_c : g_r);
+    if (active && lane < 8) {
+        float d = (1.0f + (float)lane * 0.125f) * g;
         float y = 1.0f / d;
-        if (quarter) { d *= 4.0f; y *= 0.25f; }
+        if (dir) { d *= 4.0f; y *= 0.25f; }
         rep_ym = product_multiplier(d, y);
     }
-    float4 ent[4];
-    bool none[2] = {false, false};
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int e = lane + 64 * it;
-        const int dir = e >> 7, code = e & 127;
-        if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
-        const float g = dir ? g_c : g_r;
+    float4 ent = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    bool none = false;
+    if (active) {
         const float v = e4m3_value((uint32_t)code);
         const uint32_t vb = __builtin_bit_cast(uint32_t, v);
         const int m = (int)((vb >> 20) & 7), ex = (int)((vb >> 23) & 0xFF) - 127;
-        const float cls_ym = __shfl(rep_ym, dir * 8 + m, 64);
+        const float cls_ym = __shfl(rep_ym, m, 64);
         if (code == 0 || code == 127) {
-            ent[it] = table_entry(code, g, dir == 1);
+            ent = table_entry(code, g, dir == 1);
         } else {
             float d = v * g, y = 1.0f / d;
             float rd = (1.0f + (float)m * 0.125f) * g, ry = 1.0f / rd;
             if (dir == 1) { d *= 4.0f; y *= 0.25f; rd *= 4.0f; ry *= 0.25f; }
             const bool scaled = g < 0x1p100f && d == __builtin_ldexpf(rd, ex) && y == __builtin_ldexpf(ry, -ex);
-            float ym;
-            if (scaled) ym = __builtin_ldexpf(cls_ym, -ex);
-            else ym = product_multiplier(d, y);
-            ent[it] = make_float4(d, y, ym, k_keep_codes());
+            const float ym = scaled ? __builtin_ldexpf(cls_ym, -ex) : product_multiplier(d, y);
+            ent = make_float4(d, y, ym, k_keep_codes());
         }
-        none[dir] |= ent[it].z < 0.0f;
+        none = ent.z < 0.0f;
     }
-    const bool flag_r = __ballot(none[0]) != 0, flag_c = __ballot(none[1]) != 0;
-    if (lane == 63) {                                // entries 127 (rounds 1 and 3) carry the flags
-        ent[1].x = flag_r ? 1.0f : 0.0f;
-        ent[3].x = flag_c ? 1.0f : 0.0f;
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int e = lane + 64 * it;
-        const int dir = e >> 7, code = e & 127;
-        if ((dir == 0 && !ROW) || (dir == 1 && !COL)) continue;
-        G.tables[(s * 2 + dir) * 128 + code] = ent[it];
+    const bool any = __ballot(none) != 0;
+    if (in && lane == 0) sh_none[tid >> 6] = any ? 1u : 0u;
+    __syncthreads();
+    if (active) {
+        if (code == 127) ent.x = (sh_none[2 * dir] | sh_none[2 * dir + 1]) ? 1.0f : 0.0f;
+        G.tables[(s * 2 + dir) * 128 + code] = ent;
+        if (tab) tab[dir][code] = ent;
     }
 }
 
-}  // namespace
-
-// ---------------------------------------------------------------- the kernels
-// W waves per work-group, one tile each (no interaction between them): fewer, larger
-// work-groups dispatch faster (4096 one-wave work-groups cost about 7 us to dispatch).
+// The amax pass: W waves per work-group, one tile each, over W adjacent column
+// tiles of one token tile (so of one section: W divides the column tile count).
+// The work-group writes one partial, the (row, column) maxima of its W tiles, to
+// the workspace with an ordinary store; nothing in this kernel reads them (the
+// scales kernel that follows on the stream does), so no work-group waits for
+// another and the kernel leaves no state behind.  Fewer, larger work-groups
+// dispatch faster (4096 one-wave work-groups cost about 7 us to dispatch).
+// Partial word: bits 16..31 the BF16 bits of max |x| (NaN-free), bits 32..63 the
+// FP32 bits of max |H16 D x| (NaN-free, before the 1/4 and the BF16 rounding).
 template <bool ROW, bool COL, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) void k_nvfp4_amax(const Nvfp4Group G) {
-    const int lane = threadIdx.x & 63;
-    const int b = (int)blockIdx.x * W + (W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0);
+    __shared__ uint32_t red[2][W];
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int w = W > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;
+    const int b = (int)blockIdx.x * W + w;
     const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
-    const int s = section_of(G, T);
     const uint16_t* base = G.x + ((int64_t)T * kTileRows + (lane >> 5) * 16) * G.k + (int64_t)C * kTileCols + (lane & 31) * 4;
 
     uint32_t mr = 0;
@@ -574,88 +586,81 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
         asm volatile("" : "+v"(mr), "+v"(mc));
         if (__ballot(nan) != 0) mr = wave_max_u32(lane_absmax_nonan(base, G.k));
     }
-
-    if (b == 0) {
-        // empty sections: the tensor scale of an all-zero section
-        for (int i = lane; i < G.num_sections; i += 64) {
-            if (G.tt_start[i + 1] != G.tt_start[i]) continue;
-            if (ROW) G.row_global[i] = tensor_scale(0.0f);
-            if (COL) G.col_global[i] = tensor_scale(0.0f);
-            if (ROW && G.amax_out_row) G.amax_out_row[i] = 0.0f;
-            if (COL && G.amax_out_col) G.amax_out_col[i] = 0.0f;
-        }
+    if (W == 1) {
+        if (lane == 0) G.partials[blockIdx.x] = (uint64_t)(mr << 16) | ((uint64_t)__builtin_bit_cast(uint32_t, mc) << 32);
+        return;
     }
-
-    const int first = G.tt_start[s] * G.n_ctiles;                 // first tile of the section
-    const int n = (G.tt_start[s + 1] - G.tt_start[s]) * G.n_ctiles;
-    // Which tile of the section finishes last comes from two levels of counters: the
-    // tile counts in at group counter (b - first) % kCtrlGroups, the last of each
-    // group at the section's top counter, so that no counter takes more than about
-    // n / kCtrlGroups atomics (same-address atomics are served one at a time).
-    uint32_t* const ctrl_s = G.ctrl + kCtrlStride * (kCtrlGroups + 1) * s;
-    uint32_t last = 0;
     if (lane == 0) {
-        ws_store64(G.partials + b, (uint64_t)(mr << 16) | ((uint64_t)__builtin_bit_cast(uint32_t, mc) << 32));
-        __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): the partial is stored
-        const int grp = (b - first) % kCtrlGroups;
-        const int n_grp = (n - grp + kCtrlGroups - 1) / kCtrlGroups;
-        if (__hip_atomic_fetch_add(ctrl_s + kCtrlStride * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            (uint32_t)(n_grp - 1)) {
-            const int groups = n < kCtrlGroups ? n : kCtrlGroups;
-            last = __hip_atomic_fetch_add(ctrl_s + kCtrlStride * kCtrlGroups, 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(groups - 1);
-        }
+        red[0][w] = mr;
+        red[1][w] = __builtin_bit_cast(uint32_t, mc);
     }
-    if (!__shfl((int)last, 0, 64)) return;
-
-    // The section's last tile: every partial is in.
-    uint32_t ar = 0, ac = 0;
-    // 16 loads in flight per lane per round: one at a time would cost a memory round
-    // trip per 64 partials at the very end of the kernel
-    for (int i0 = lane; i0 < n; i0 += 64 * 16) {
-        uint64_t v[16];
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t r = 0, c = 0;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = i0 + 64 * u < n ? ws_load64(G.partials + first + i0 + 64 * u) : 0;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            ar = (uint32_t)v[u] > ar ? (uint32_t)v[u] : ar;
-            ac = (uint32_t)(v[u] >> 32) > ac ? (uint32_t)(v[u] >> 32) : ac;
+        for (int i = 0; i < W; ++i) {
+            r = red[0][i] > r ? red[0][i] : r;
+            c = red[1][i] > c ? red[1][i] : c;                    // non-negative FP32: ordered as integers
         }
-    }
-    ar = wave_max_u32(ar);
-    ac = wave_max_u32(ac);
-    // max |BF16(y/4)| over the section = BF16(max |y| / 4) (rounding is monotone)
-    const float g_r = tensor_scale(__builtin_bit_cast(float, ar));
-    const float g_c = tensor_scale(lo_bf16(pack_bf16(__builtin_bit_cast(float, ac) * 0.25f, 0.0f)));
-    if (lane == 0) {
-        if (ROW) G.row_global[s] = g_r;
-        if (COL) G.col_global[s] = g_c;
-    }
-    for (int i = lane; i <= kCtrlGroups; i += 64)                 // ready for the next call
-        __hip_atomic_store(ctrl_s + kCtrlStride * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    build_tables<ROW, COL>(G, s, g_r, g_c);
-    if (lane == 0) {
-        // the measured maxima for a caller's next-step scaling
-        if (ROW && G.amax_out_row) G.amax_out_row[s] = __builtin_bit_cast(float, ar);
-        if (COL && G.amax_out_col) G.amax_out_col[s] = lo_bf16(pack_bf16(__builtin_bit_cast(float, ac) * 0.25f, 0.0f));
+        G.partials[blockIdx.x] = (uint64_t)(r << 16) | ((uint64_t)c << 32);
     }
 }
 
-// Tensor scales and tables of every section from caller-supplied maxima (one
-// work-group per section); zeroes the measured-maxima outputs the quant kernel
-// then raises.
-template <bool ROW, bool COL>
-__global__ __launch_bounds__(64) void k_nvfp4_given(const Nvfp4Group G) {
-    const int s = blockIdx.x;
-    const float g_r = ROW ? tensor_scale(G.amax_in_row[s]) : 0.0f;
-    const float g_c = COL ? tensor_scale(G.amax_in_col[s]) : 0.0f;
-    if (threadIdx.x == 0) {
+// Tensor scales and tables of every section (one 1024-thread work-group per
+// section), from the partials of the amax pass (tpp tiles per partial) or, GIVEN,
+// from the caller-supplied maxima.  Measured: the maxima out are the measured
+// ones (an empty section: 0).  GIVEN: they are zeroed here, and the quant kernel
+// raises them.
+constexpr int kScalesThreads = 1024;
+template <bool ROW, bool COL, bool GIVEN>
+__global__ __launch_bounds__(kScalesThreads) void k_nvfp4_scales(const Nvfp4Group G, int tpp) {
+    __shared__ uint32_t red[2][kScalesThreads / 64];
+    __shared__ uint32_t sh_none[4];
+    const int s = blockIdx.x, tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+    float a_r = 0.0f, a_c = 0.0f;
+    if (GIVEN) {
+        a_r = ROW ? G.amax_in_row[s] : 0.0f;
+        a_c = COL ? G.amax_in_col[s] : 0.0f;
+    } else {
+        const int first = G.tt_start[s] * G.n_ctiles / tpp;
+        const int n = (G.tt_start[s + 1] - G.tt_start[s]) * G.n_ctiles / tpp;
+        uint32_t ar = 0, ac = 0;
+        // 8 loads in flight per thread per round
+        for (int i0 = tid; i0 < n; i0 += kScalesThreads * 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = i0 + kScalesThreads * u < n ? G.partials[first + i0 + kScalesThreads * u] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                ar = (uint32_t)v[u] > ar ? (uint32_t)v[u] : ar;
+                ac = (uint32_t)(v[u] >> 32) > ac ? (uint32_t)(v[u] >> 32) : ac;
+            }
+        }
+        ar = wave_max_u32(ar);
+        ac = wave_max_u32(ac);
+        if (lane == 0) {
+            red[0][w] = ar;
+            red[1][w] = ac;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kScalesThreads / 64; ++i) {
+            ar = red[0][i] > ar ? red[0][i] : ar;
+            ac = red[1][i] > ac ? red[1][i] : ac;
+        }
+        // max |BF16(y/4)| over the section = BF16(max |y| / 4) (both roundings are
+        // monotone)
+        a_r = __builtin_bit_cast(float, ar);
+        a_c = lo_bf16(pack_bf16(__builtin_bit_cast(float, ac) * 0.25f, 0.0f));
+    }
+    const float g_r = ROW ? tensor_scale(a_r) : 0.0f, g_c = COL ? tensor_scale(a_c) : 0.0f;
+    if (tid == 0) {
         if (ROW) G.row_global[s] = g_r;
         if (COL) G.col_global[s] = g_c;
-        if (ROW && G.amax_out_row) G.amax_out_row[s] = 0.0f;
-        if (COL && G.amax_out_col) G.amax_out_col[s] = 0.0f;
+        if (ROW && G.amax_out_row) G.amax_out_row[s] = GIVEN ? 0.0f : a_r;
+        if (COL && G.amax_out_col) G.amax_out_col[s] = GIVEN ? 0.0f : a_c;
     }
-    build_tables<ROW, COL>(G, s, g_r, g_c);
+    build_tables_wg<ROW, COL>(G, s, g_r, g_c, nullptr, sh_none, tid);
 }
 
 // LDS of one work-group's quant passes (W waves, one tile each).
@@ -891,7 +896,7 @@ __device__ __forceinline__ void load_tile(uint4 (&p)[16][2], const uint16_t* bas
     }
 }
 
-// Phase B of the two-kernel call: one wave per tile, W waves per work-group over W
+// The quant pass of the three-kernel call: one wave per tile, W waves per work-group over W
 // adjacent column tiles of the same rows (k / 128 a multiple of W).
 template <bool ROW, bool COL, bool FP8, bool SR, bool AOUT, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void k_nvfp4_quant(const Nvfp4Group G) {

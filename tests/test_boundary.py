@@ -134,10 +134,11 @@ def test_grouped_argument_errors(L):
 def test_workspace_size_query(L):
     q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
     assert q(16384, 4096, 8, 4) == 0                              # FP8 only: no amax pass
-    # counters (32 x 17 x 256 B), two status lines, scale tables (32 sections x 2
-    # directions x 128 x 16 B) and the single-read form's 1024 partial words of one
-    # launch group, then one 8-byte partial per 128 x 128 tile
-    fixed = 32 * 17 * 256 + 512 + 32 * 2 * 128 * 16 + 4 * 1024
+    # two status lines, scale tables (32 sections x 2 directions x 128 x 16 B) and
+    # the single-read form's 1024 partial words of one launch group, then one 8-byte
+    # partial per 128 x 128 tile (the most the amax pass writes)
+    fixed = 512 + 32 * 2 * 128 * 16 + 4 * 1024
+    assert fixed == mxq.WORKSPACE_FIXED == 135680
     for total, k, S in [(0, 4096, 8), (16384, 4096, 8), (65536, 7168, 32), (128, 128, 1), (16384, 4096, 256)]:
         for flags in (1, 2, 3, 7):
             need = q(total, k, S, flags)
@@ -208,10 +209,9 @@ def test_dsa_nvfp4_argument_errors(L):
 
 
 def test_dsa_nvfp4_workspace_size(L):
-    """65 counters on their own 256-byte lines, 128 table entries, then 4 bytes per
-    64 rows, rounded to 256."""
+    """128 table entries, then 4 bytes per 64 rows, rounded to 256."""
     q = L.mxq_hadamard_quant_nvfp4_workspace_size
-    fixed = 65 * 256 + 2048
+    fixed = 2048
     assert q(0) == 0 and q(-5) == 0
     assert q(1) == fixed + 256
     assert q(64 * 64) == fixed + 256

@@ -279,9 +279,6 @@ def compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_in=None, amax_out=False, ca
     assert_same("codes", host(res.codes), ref.codes)
     if amax_out:
         assert_same("amax", host(res.amax), np.array([ref.amax], np.float32))
-    if pe_np.shape[0] > 0:
-        ctr = host(call.workspace)[:65 * 256].view(np.uint32)[::64]
-        assert not ctr.any(), "a completion counter was left nonzero"
     return res, ref
 
 
@@ -340,15 +337,18 @@ def test_dsa_nvfp4_empty(orc):
 
 
 def test_dsa_nvfp4_reuse(orc):
-    """One prepared call run twice, then a smaller input through the same workspace
-    (left over partials and table from the larger call): every run matches and
-    leaves the counters at zero."""
+    """One prepared call on a workspace of arbitrary contents (every byte 0xA5) run
+    twice, then a smaller input through the same workspace (left over partials and
+    table from the larger call): every run matches (the call's kernels meet in
+    stream order and keep no state in the workspace)."""
     dev = device()
     announce("dsa nvfp4 reuse")
     w = synth.dsa_rotate_fp8(tokens=100, heads=8, seed=78)
     pe, nope = w.tensors["pe"].to(dev), w.tensors["nope"].to(dev)
     pe_np, nope_np = bits16(w.tensors["pe"]), bits16(w.tensors["nope"])
-    call = mxq.HadamardNVFP4(pe, nope, amax_out=True)
+    need = mxq.mxq_hadamard_quant_nvfp4_workspace_size(800)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev)
+    call = mxq.HadamardNVFP4(pe, nope, amax_out=True, workspace=ws)
     compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_out=True, call=call)
     compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_out=True, call=call)
     small = mxq.HadamardNVFP4(pe[:300], nope[:300], workspace=call.workspace)
@@ -356,12 +356,13 @@ def test_dsa_nvfp4_reuse(orc):
 
 
 # ============================================================== grouped NVFP4
-def compare_grouped(orc, x_dev, sections, mask, flags, seed=None, ro=None, co=None, out=None, threads=8):
-    call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, out=out)
+def compare_grouped(orc, x_dev, sections, mask, flags, seed=None, ro=None, co=None, out=None, threads=8,
+                    workspace=None):
+    call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, out=out, workspace=workspace)
     res = call()
     torch.cuda.synchronize()
-    assert mxq.workspace_counters_clear(call.workspace), \
-        "a section counter, the error word or a partial word was left nonzero"
+    assert mxq.workspace_protocol_clear(call.workspace), \
+        "the single-read form's error word or a partial word was left nonzero"
     ref = orc.group_rht_quant_nvfp4(bits16(x_dev), sections, mask, flags, seed or 0, ro, co, threads=threads)
     if flags & 1:
         assert_same("row_global", host(res.row_global), ref.row_global)
@@ -412,8 +413,8 @@ def test_grouped_sr_small(orc, k):
 def test_grouped_single_read_reuse(orc, flags, sr):
     """The single-read form (k a multiple of 512, every section within the resident
     grid): one workspace through three calls, the second on other sections and
-    fewer rows; each matches the oracle and leaves the workspace's counters, error
-    word and partial words at zero."""
+    fewer rows; each matches the oracle and leaves the workspace's error word and
+    partial words at zero."""
     dev = device()
     announce(f"grouped single-read reuse flags={flags} sr={sr}")
     w = synth.grouped_nvfp4_sr(total_rows=3072, k=2048, parts=9, forced_empty=2, seed=40)
@@ -429,7 +430,7 @@ def test_grouped_single_read_reuse(orc, flags, sr):
                                 co[:S] if co else None, workspace=ws)
         res = call()
         torch.cuda.synchronize()
-        assert mxq.workspace_counters_clear(ws), "workspace left nonzero"
+        assert mxq.workspace_protocol_clear(ws), "workspace left nonzero"
         ref = orc.group_rht_quant_nvfp4(bits16(xi), sections, p["sign_mask"], flags, seed or 0,
                                         ro[:S] if ro else None, co[:S] if co else None, threads=8)
         for name in ("row_global", "row_scales", "row_codes", "col_global", "col_scales", "col_codes",
@@ -437,6 +438,60 @@ def test_grouped_single_read_reuse(orc, flags, sr):
             got = getattr(res, name)
             if got is not None:
                 assert_same(name, host(got), getattr(ref, name))
+
+
+def dirty_workspace(total_rows, k, num_sections, flags, dev):
+    """A workspace whose bytes are all 0xA5 except the single-read form's error word
+    and partial words (the only words a call needs at zero)."""
+    n = mxq.mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device=dev)
+    ws[mxq.WORKSPACE_STATUS:mxq.WORKSPACE_STATUS + 512] = 0
+    ws[mxq.WORKSPACE_SLOTS:mxq.WORKSPACE_SLOTS + mxq.WORKSPACE_SLOTS_BYTES] = 0
+    return ws
+
+
+@pytest.mark.parametrize("case", ["one_wave_amax", "supplied"])
+def test_grouped_any_workspace_contents(orc, case):
+    """The multi-kernel form's kernels meet only through the stream order: partials
+    and tables left as arbitrary bytes (0xA5) change nothing, on the amax pass with one
+    tile per work-group (k / 128 odd) and with supplied maxima; the workspace is then
+    used again for a smaller call."""
+    dev = device()
+    announce(f"grouped dirty workspace {case}")
+    if case == "one_wave_amax":
+        w = synth.grouped_nvfp4(total_rows=1280, k=640, parts=4, seed=55)
+        x, p = w.tensors["x"].to(dev), w.params
+        ws = dirty_workspace(1280, 640, 4, 3, dev)
+        compare_grouped(orc, x, p["split_sections"], p["sign_mask"], 3, workspace=ws)
+        compare_grouped(orc, x[:512].contiguous(), [256, 0, 256], p["sign_mask"], 3, workspace=ws)
+    else:
+        w = synth.grouped_nvfp4(total_rows=1280, k=640, parts=5, seed=57)
+        x, p = w.tensors["x"].to(dev), w.params
+        sec, mask = p["split_sections"], p["sign_mask"]
+        meas = orc.group_rht_quant_nvfp4(bits16(x), sec, mask, 3, threads=8)
+        ws = dirty_workspace(1280, 640, 5, 3, dev)
+        compare_grouped_amax(orc, x, sec, mask, 3, (meas.row_amax * np.float32(0.5), meas.col_amax),
+                             workspace=ws)
+        compare_grouped_amax(orc, x, sec, mask, 3, None, workspace=ws)
+
+
+def test_grouped_any_workspace_contents_four_wave_amax():
+    """The amax pass with four tiles per work-group, on a group too large for the
+    single-read form (1056 four-tile items, above its 1024): a workspace of 0xA5 bytes
+    (but the single-read words) gives the same bytes as a zeroed one, with stochastic
+    rounding and FP8 (a property of the call, compared call against call; parity of
+    this shape against the oracle is the full-size tests' part)."""
+    dev = device()
+    announce("grouped dirty workspace: four-tile amax work-groups, 4224 x 16384")
+    w = synth.grouped_nvfp4_sr(total_rows=4224, k=16384, parts=3, forced_empty=0, seed=56)
+    x, p = w.tensors["x"].to(dev), w.params
+    args = (x, p["split_sections"], p["sign_mask"], 7, p["seed"], p["row_offsets"], p["col_offsets"])
+    clean = mxq.GroupedNVFP4(*args)()
+    dirty = mxq.GroupedNVFP4(*args, workspace=dirty_workspace(4224, 16384, 3, 7, dev))()
+    torch.cuda.synchronize()
+    for n in ("row_global", "row_scales", "row_codes", "col_global", "col_scales", "col_codes",
+              "fp8_scales", "fp8_codes"):
+        assert torch.equal(getattr(clean, n), getattr(dirty, n)), n
 
 
 @pytest.mark.parametrize("sr", [False, True])
@@ -466,7 +521,7 @@ def test_grouped_single_read_deferred(orc, sr):
             mxq.LIB_PATH = main_path
     finally:
         mxq._lib = saved
-    assert mxq.workspace_counters_clear(call.workspace), "workspace left nonzero"
+    assert mxq.workspace_protocol_clear(call.workspace), "workspace left nonzero"
     ref = orc.group_rht_quant_nvfp4(bits16(x), p["split_sections"], p["sign_mask"], 3, seed or 0, ro, co,
                                     threads=8)
     for name in ("row_global", "row_scales", "row_codes", "col_global", "col_scales", "col_codes"):
@@ -676,14 +731,16 @@ def test_grouped_hand_case_b9(orc):
 
 
 # ============================================================== supplied amax (single pass)
-def compare_grouped_amax(orc, x_dev, sections, mask, flags, amax_in, seed=None, ro=None, co=None):
+def compare_grouped_amax(orc, x_dev, sections, mask, flags, amax_in, seed=None, ro=None, co=None,
+                         workspace=None):
     """The call with supplied maxima (device tensors, or None) and measured maxima out,
     against the oracle given the same maxima."""
     dev = x_dev.device
     ain = None
     if amax_in is not None:
         ain = tuple(None if a is None else torch.tensor(np.asarray(a, np.float32), device=dev) for a in amax_in)
-    call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, amax_in=ain, amax_out=True)
+    call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, amax_in=ain, amax_out=True,
+                            workspace=workspace)
     res = call()
     torch.cuda.synchronize()
     ref = orc.group_rht_quant_nvfp4(bits16(x_dev), sections, mask, flags, seed or 0, ro, co, threads=8,

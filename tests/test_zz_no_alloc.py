@@ -31,8 +31,8 @@ def _both(x, sections, mask, flags, seed=None, ro=None, co=None):
 
 @pytest.mark.parametrize("first,second", [
     # (rows, k, parts, empties, flags, sr) of the first and the smaller second call
-    ((4096, 2048, 9, 2, 7, True), (1024, 512, 3, 1, 3, False)),      # two-kernel, then single-read
-    ((2048, 1024, 5, 1, 3, False), (512, 384, 2, 0, 7, True)),       # single-read, then two-kernel
+    ((4096, 2048, 9, 2, 7, True), (1024, 512, 3, 1, 3, False)),      # SR + FP8, then RNE row + col
+    ((2048, 1024, 5, 1, 3, False), (512, 384, 2, 0, 7, True)),       # single-read form, then k / 128 odd
 ])
 def test_noalloc_matches_workspace_call(first, second):
     dev = device()
