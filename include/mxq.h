@@ -88,6 +88,11 @@ const char* mxq_version(void);
 
 /* ---------------------------------------------------------------------------
  * FP8 E4M3 (OCP E4M3FN), one FP32 scale per 1x128 group along k.
+ * onnxruntime PR #33644, Description: the QMoE dynamic activation quantizer's
+ * K128 groups, its scale max(amax, 1e-10) * float32(1/448), the FP32 division of
+ * each element by its group's scale and the saturating nearest-even E4M3FN encode;
+ * the one-ulp differences at E4M3 midpoints it reports are why the division is
+ * exact IEEE here, never a reciprocal multiply.
  *
  *   x_bf16   [m][ldx] BF16 bit patterns, row-major, ldx >= k
  *   q_e4m3   [m][ldq] E4M3 codes, ldq >= k
@@ -175,7 +180,10 @@ mxq_status mxq_swiglu_quant_fp8(const uint16_t* gate_bf16, int64_t ld_gate, cons
                                 float* scales, int64_t scale_stride_row, int64_t scale_stride_group, void* stream);
 
 /* ---------------------------------------------------------------------------
- * DSA-indexer rotate + quantize.  For each row r:
+ * DSA-indexer rotate + quantize.  TensorRT-LLM PR #15158, Summary: the indexer
+ * concatenates qk_pe and qk_nope, applies rotate_activation (the normalized
+ * 128-point Hadamard transform) and then fp8_quantize_1x128; the discussion's
+ * (Hq).(Hk) = q.k is why the rotation changes no attention score.  For each row r:
  *   v = cat(pe[r][0:d_pe], nope[r][0:128-d_pe])           (qk_pe first)
  *   y = BF16(fl(WHT_128(v) * F(1/sqrt(128))))            (Sylvester order, butterfly
  *        stages h = 1, 2, 4, ..., 64; (v_i, v_i+h) <- (v_i + v_i+h, v_i - v_i+h))
@@ -229,7 +237,13 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
 
 /* ---------------------------------------------------------------------------
  * Grouped NVFP4 quantization with a 16-point random Hadamard transform (RHT) on
- * the column-wise operand.
+ * the column-wise operand.  TransformerEngine PR #2564, Greptile summary and
+ * sequence diagram: the grouped row-wise + column-wise RHT cast over MoE split
+ * sections with a caller-provided workspace and no allocation per call (review
+ * thread: the workspace-size query); PR #2555, review comments on cast.cpp and
+ * quantizer.cpp: split sections in multiples of 128, the RHT on the column-wise
+ * (transposed) operand only, its BF16 intermediate, and a separate column-wise RNG
+ * with deterministic per-call offsets for stochastic rounding.
  *
  * x_bf16 is [total_rows][k] BF16 (row stride k), total_rows = sum(split_sections).
  * Section s covers rows [R_s, R_s + m_s), m_s = split_sections[s] (m_s may be 0).

@@ -590,7 +590,8 @@ def test_grouped_edges(orc, k):
 @pytest.mark.parametrize("k", [256, 1024])
 def test_grouped_section_shapes(orc, sections, k):
     """One section, all-empty-but-one, many 128-row sections, more than one launch
-    group (> 64 sections), and an all-empty call (only the floor scales are written)."""
+    group of 32 sections (71 and 150 sections: three and five groups), and an
+    all-empty call (only the floor scales are written)."""
     dev = device()
     total = sum(sections)
     announce(f"grouped sections n={len(sections)} total={total} k={k}")
