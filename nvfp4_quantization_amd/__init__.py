@@ -370,7 +370,8 @@ def alloc_workspace(total_rows: int, k: int, num_sections: int, flags: int, devi
 
 
 WORKSPACE_STATUS = 0                                  # byte offset of the single-read form's error word
-WORKSPACE_SLOTS = WORKSPACE_STATUS + 512 + 32 * 2 * 128 * 16   # the single-read form's partial words
+WORKSPACE_TABLES = WORKSPACE_STATUS + 512            # float4 (d, 1/d, multiplier, mask) at (s * 2 + dir) * 128 + code
+WORKSPACE_SLOTS = WORKSPACE_TABLES + 32 * 2 * 128 * 16         # the single-read form's partial words
 WORKSPACE_SLOTS_BYTES = 4 * 1024
 WORKSPACE_FIXED = WORKSPACE_SLOTS + WORKSPACE_SLOTS_BYTES      # then the amax pass's partials
 

@@ -19,6 +19,9 @@ The single-read kernels (mxq_nvfp4_fused_*.hip) are also built with
                       are at the limit, and spill a third of the tile
 _build/libmxq_ceiling.so holds the benchmark's streaming read and copy kernels (the
 measured HBM ceilings; not part of the quantization ABI).
+_build/libmxq_selftest.so holds test-only kernels (tests/hip/mxq_selftest.hip) that
+sweep the hardware conversions over their whole input range; nothing in the package
+loads it.
 A further library, _build/libmxq_defer0.so, is the same code with the single-read
 kernels built with MXQ_FUSED_DEFER_TICKS=0: every waiting item gives up at once and
 leaves its tiles to its section's last item, which the deferral test checks against
@@ -37,6 +40,8 @@ OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT, "libmxq.so")
 LIB_DEFER0 = os.path.join(OUT, "libmxq_defer0.so")
 LIB_CEILING = os.path.join(OUT, "libmxq_ceiling.so")     # the benchmark's HBM read / copy ceilings
+LIB_SELFTEST = os.path.join(OUT, "libmxq_selftest.so")   # the tests' conversion sweeps
+SELFTEST_SRC = os.path.join(ROOT, "tests", "hip", "mxq_selftest.hip")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["mxq_fp8.hip", "mxq_fp8_block.hip", "mxq_swiglu_fp8.hip", "mxq_dsa_nvfp4.hip", "mxq_nvfp4.hip", "mxq_nvfp4_quant_rne.hip", "mxq_nvfp4_quant_sr.hip",
@@ -95,11 +100,16 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
         defer_objs.append(obj)
     ceiling_obj = os.path.join(OUT, "mxq_ceiling.hip.o")
     jobs.append([cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "mxq_ceiling.hip"), "-o", ceiling_obj])
+    selftest_obj = os.path.join(OUT, "mxq_selftest.hip.o")
+    jobs.append([cc, *COMMON, *DEVICE, "-c", SELFTEST_SRC, "-o", selftest_obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB_CEILING + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, ceiling_obj], verbose)
     os.replace(tmp, LIB_CEILING)
+    tmp = LIB_SELFTEST + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, selftest_obj], verbose)
+    os.replace(tmp, LIB_SELFTEST)
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

@@ -6,16 +6,19 @@
 //  * BF16 -> FP32 widening is a 16-bit shift (exact).
 //  * div_rn(x, d, y) returns fl(x / d) given y = fl(1 / d): q0 = fl(x*y) is within
 //    one ulp, the FMA residual r = x - q0*d is exact, and fl(q0 + r*y) is the
-//    correctly rounded quotient (Markstein's correction step).  The identity was
-//    checked exhaustively for every BF16 significand x against every FP32
-//    significand d, and for every numerator of the form fl(a * F(1/6)) with a a
-//    BF16 value, which are the only numerators the kernels divide.
+//    correctly rounded quotient (Markstein's correction step, a theorem for every
+//    x and d whose values stay normal).  tests/test_exactness_cpu.py checks it
+//    exhaustively for every BF16 numerator significand and every numerator
+//    fl(a * F(1/6)) (a BF16) against every FP32 divisor significand, and for
+//    arbitrary FP32 numerators (the SwiGLU path's) on random pairs and on pairs
+//    whose quotient lies next to a rounding midpoint.
 //  * The E4M3 / E2M1 / BF16 conversions use gfx950's hardware conversions.  Over
 //    all 2^32 FP32 inputs they equal nearest-even with saturation for every
-//    finite input below 464 (E4M3) and every non-NaN input (E2M1, BF16); the
-//    kernels clamp to 448 (or never exceed 464) before the E4M3 conversion.  A NaN
-//    converts to 0xFF: FP8 element codes turn it into 0x7F, block scales mask it
-//    to the NaN code 0x7F.
+//    finite input below 464 (E4M3) and every non-NaN input (E2M1, BF16)
+//    (tests/test_gpu_exactness.py sweeps them on the device); the kernels clamp
+//    to 448 (or never exceed 464) before the E4M3 conversion.  A NaN converts to
+//    a NaN code: FP8 element codes turn it into 0x7F, block scales mask it to the
+//    NaN code 0x7F.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -142,10 +145,9 @@ __device__ __forceinline__ uint32_t rbyte_hi(uint32_t w) {
 // below 2 / 4 / 6; with u = |q| / D = k + f the value rounds up iff
 // floor(256 f) + r >= 256; |q| >= 6 saturates.  gfx950's stochastic conversion does
 // exactly this for the first value of a pair when the random operand is r << 24 (its
-// low 24 bits zero): checked against the rule for every FP32 value with |q| in
-// [2^-20, 16) and every r, and on sampled smaller, subnormal and larger values.  (The
-// pair's second value draws on the random operand differently, so each value gets a
-// conversion of its own.)
+// low 24 bits zero): tests/test_gpu_exactness.py checks it against the rule for every
+// non-NaN FP32 value and every r.  (The pair's second value draws on the random
+// operand differently, so each value gets a conversion of its own.)
 //
 // The code of q alone (low nibble of the result, other bits cleared).  The builtin's
 // first operand does not reach the instruction: the compiler gives it a fresh
