@@ -31,15 +31,13 @@ hipError_t launch_sel(const Nvfp4Group& g, hipStream_t stream) {
         hipLaunchKernelGGL((k_nvfp4_scales<ROW, COL, true>), dim3(g.num_sections), dim3(kScalesThreads), 0, stream,
                            g, 1);
     } else {
-        // four column tiles per work-group when they always share a token tile
-        const int tpp = g.n_ctiles % 4 == 0 ? 4 : 1;
-        if (tpp == 4)
-            hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL, 4>), dim3((unsigned)(g.total_tiles / 4)), dim3(256), 0, stream, g);
-        else
-            hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL, 1>), dim3((unsigned)g.total_tiles), dim3(64), 0, stream, g);
+        const int n_chunks = (int)((g.k + kAmaxCols - 1) / kAmaxCols);
+        const int bands = g.tt_start[g.num_sections] * (kTileRows / kAmaxRows);
+        hipLaunchKernelGGL((k_nvfp4_amax<ROW, COL>), dim3((unsigned)(bands * n_chunks)), dim3(256), 0, stream, g,
+                           n_chunks);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((k_nvfp4_scales<ROW, COL, false>), dim3(g.num_sections), dim3(kScalesThreads), 0, stream,
-                           g, tpp);
+                           g, (kTileRows / kAmaxRows) * n_chunks);
     }
     if ((e = hipGetLastError()) != hipSuccess || g.total_tiles == 0) return e;
     const uint32_t flags = (ROW ? 1u : 0u) | (COL ? 2u : 0u) | (FP8 ? 4u : 0u);

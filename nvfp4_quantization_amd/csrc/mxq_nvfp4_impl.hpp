@@ -11,8 +11,8 @@
 // The FP32 tensor scale of a section needs the section's amax before any code is
 // final, so a call runs three kernels per group of sections:
 //
-//   k_nvfp4_amax   one wave per 128 x 128 tile: max |x| and max |H16 D x| of the
-//                  tile, one partial per work-group (ordinary stores).
+//   k_nvfp4_amax   one work-group per 16-row band and 2048 columns: max |x| and
+//                  max |H16 D x| of the band, one partial each (ordinary stores).
 //   k_nvfp4_scales one work-group per section: folds the section's partials into
 //                  the two tensor scales and writes the section's scale tables.
 //                  The kernels meet only through the stream order: no counters,
@@ -547,49 +547,79 @@ __device__ __forceinline__ void build_tables_wg(const Nvfp4Group& G, int s, floa
     }
 }
 
-// The amax pass: W waves per work-group, one tile each, over W adjacent column
-// tiles of one token tile (so of one section: W divides the column tile count).
-// The work-group writes one partial, the (row, column) maxima of its W tiles, to
-// the workspace with an ordinary store; nothing in this kernel reads them (the
-// scales kernel that follows on the stream does), so no work-group waits for
-// another and the kernel leaves no state behind.  Fewer, larger work-groups
-// dispatch faster (4096 one-wave work-groups cost about 7 us to dispatch).
-// Partial word: bits 16..31 the BF16 bits of max |x| (NaN-free), bits 32..63 the
-// FP32 bits of max |H16 D x| (NaN-free, before the 1/4 and the BF16 rounding).
-template <bool ROW, bool COL, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) void k_nvfp4_amax(const Nvfp4Group G) {
-    __shared__ uint32_t red[2][W];
-    const int tid = (int)threadIdx.x, lane = tid & 63;
-    const int w = W > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;
-    const int b = (int)blockIdx.x * W + w;
-    const int T = b / G.n_ctiles, C = b - T * G.n_ctiles;
-    const uint16_t* base = G.x + ((int64_t)T * kTileRows + (lane >> 5) * 16) * G.k + (int64_t)C * kTileCols + (lane & 31) * 4;
-
+// The amax pass over bands of kAmaxRows = 16 rows: a 256-thread work-group takes
+// 16 rows x kAmaxCols = 2048 columns, each thread 8 adjacent columns of all 16 rows, so a
+// wave's load instruction reads 1 KB of one row and the 16-point RHT of a column
+// block runs inside the lane.  The work-group writes one partial, the (row, column)
+// maxima of its band, with an ordinary store; nothing in this kernel reads them
+// (the scales kernel that follows on the stream does), so no work-group waits for
+// another and the kernel leaves no state behind.  Partial p = band * n_chunks +
+// chunk: bits 16..31 the BF16 bits of max |x| (NaN-free), bits 32..63 the FP32 bits
+// of max |H16 D x| (NaN-free, before the 1/4 and the BF16 rounding).  Columns at
+// or past k (the last chunk when k % 2048 != 0) are not read.  The loads are
+// ordinary ones, not non-temporal: this pass alone is faster with the non-temporal
+// hint (23.6 against 28 us on the 16384 x 4096 call, MI355X), but the input then
+// does not stay in the Infinity Cache, and the quant pass's second read costs
+// 9 us more (the call: 84 against 76.5 us).
+template <bool ROW, bool COL>
+__global__ __launch_bounds__(256) void k_nvfp4_amax(const Nvfp4Group G, int n_chunks) {
+    __shared__ uint32_t red[2][4];
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int band = (int)blockIdx.x / n_chunks, chunk = (int)blockIdx.x - band * n_chunks;
+    const int64_t c0 = (int64_t)chunk * kAmaxCols + tid * 8;
     uint32_t mr = 0;
-    float rmax = 0.0f, mc = 0.0f;
-    bool nan = false;
-    uint2 q0[16], q1[16];
-    load_quarter(q0, base, G.k, 0);
-    load_quarter(q1, base, G.k, 1);
-    amax_quarter<ROW, COL>(q0, G.sign_mask, mr, rmax, mc, nan);
-    load_quarter(q0, base, G.k, 2);
-    amax_quarter<ROW, COL>(q1, G.sign_mask, mr, rmax, mc, nan);
-    load_quarter(q1, base, G.k, 3);
-    amax_quarter<ROW, COL>(q0, G.sign_mask, mr, rmax, mc, nan);
-    amax_quarter<ROW, COL>(q1, G.sign_mask, mr, rmax, mc, nan);
-    if (ROW && COL) mr = __builtin_bit_cast(uint32_t, rmax) >> 16;
+    float mc = 0.0f;
+    if (c0 < G.k) {
+        const uint16_t* base = G.x + (int64_t)band * 16 * G.k + c0;
+        uint4 v[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) v[t] = *reinterpret_cast<const uint4*>(base + (int64_t)t * G.k);
+        if (ROW) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                m = absmax_pk(absmax_pk(absmax_pk(absmax_pk(m, v[t].x), v[t].y), v[t].z), v[t].w);
+            m = fold_pk(m);
+            if (m > 0x7F80u) {                       // a NaN: the maximum without it
+                m = 0;
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    m = absmax_nonan_pairs(absmax_nonan_pairs(absmax_nonan_pairs(absmax_nonan_pairs(m, v[t].x), v[t].y),
+                                                              v[t].z), v[t].w);
+            }
+            mr = m;
+        }
+        if (COL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float f[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const uint32_t wd = (j >> 1) == 0 ? v[t].x : (j >> 1) == 1 ? v[t].y : (j >> 1) == 2 ? v[t].z : v[t].w;
+                    const uint32_t neg = sign_of_row(G.sign_mask, t);
+                    f[t] = (j & 1) ? hi_signed(wd, neg) : lo_signed(wd, neg);
+                }
+                // stages h = 1, 2, 4; the last stage is not formed: for its pair (a, b)
+                // the larger of |fl(a + b)| and |fl(a - b)| is fl(|a| + |b|) (rounding is
+                // monotone and symmetric)
+#pragma unroll
+                for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        if (i & h) continue;
+                        const float x0 = f[i], x1 = f[i + h];
+                        f[i] = x0 + x1;
+                        f[i + h] = x0 - x1;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)      // NaN values are quiet here, and max ignores them
+                    mc = __builtin_fmaxf(mc, __builtin_fabsf(f[i]) + __builtin_fabsf(f[i + 8]));
+            }
+        }
+    }
     mr = wave_max_u32(mr);
     mc = wave_max_f32(mc);
-    if (ROW && COL) {
-        // pin the main path's results before the rare branch, so that none of its
-        // work is scheduled after it
-        asm volatile("" : "+v"(mr), "+v"(mc));
-        if (__ballot(nan) != 0) mr = wave_max_u32(lane_absmax_nonan(base, G.k));
-    }
-    if (W == 1) {
-        if (lane == 0) G.partials[blockIdx.x] = (uint64_t)(mr << 16) | ((uint64_t)__builtin_bit_cast(uint32_t, mc) << 32);
-        return;
-    }
     if (lane == 0) {
         red[0][w] = mr;
         red[1][w] = __builtin_bit_cast(uint32_t, mc);
@@ -598,7 +628,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
     if (tid == 0) {
         uint32_t r = 0, c = 0;
 #pragma unroll
-        for (int i = 0; i < W; ++i) {
+        for (int i = 0; i < 4; ++i) {
             r = red[0][i] > r ? red[0][i] : r;
             c = red[1][i] > c ? red[1][i] : c;                    // non-negative FP32: ordered as integers
         }
@@ -607,13 +637,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 }
 
 // Tensor scales and tables of every section (one 1024-thread work-group per
-// section), from the partials of the amax pass (tpp tiles per partial) or, GIVEN,
+// section), from the partials of the amax pass (ppt partials per 128-row token
+// tile, in row order) or, GIVEN,
 // from the caller-supplied maxima.  Measured: the maxima out are the measured
 // ones (an empty section: 0).  GIVEN: they are zeroed here, and the quant kernel
 // raises them.
 constexpr int kScalesThreads = 1024;
 template <bool ROW, bool COL, bool GIVEN>
-__global__ __launch_bounds__(kScalesThreads) void k_nvfp4_scales(const Nvfp4Group G, int tpp) {
+__global__ __launch_bounds__(kScalesThreads) void k_nvfp4_scales(const Nvfp4Group G, int ppt) {
     __shared__ uint32_t red[2][kScalesThreads / 64];
     __shared__ uint32_t sh_none[4];
     const int s = blockIdx.x, tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -622,8 +653,8 @@ __global__ __launch_bounds__(kScalesThreads) void k_nvfp4_scales(const Nvfp4Grou
         a_r = ROW ? G.amax_in_row[s] : 0.0f;
         a_c = COL ? G.amax_in_col[s] : 0.0f;
     } else {
-        const int first = G.tt_start[s] * G.n_ctiles / tpp;
-        const int n = (G.tt_start[s + 1] - G.tt_start[s]) * G.n_ctiles / tpp;
+        const int first = G.tt_start[s] * ppt;
+        const int n = (G.tt_start[s + 1] - G.tt_start[s]) * ppt;
         uint32_t ar = 0, ac = 0;
         // 8 loads in flight per thread per round
         for (int i0 = tid; i0 < n; i0 += kScalesThreads * 8) {
