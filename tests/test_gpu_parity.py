@@ -355,6 +355,16 @@ def test_dsa_nvfp4_reuse(orc):
     compare_dsa4(orc, pe_np[:300], nope_np[:300], pe[:300], nope[:300], call=small)
 
 
+def test_dsa_nvfp4_large(orc):
+    """524,352 rows (8193 tokens x 64 heads, a ragged last work-group): 8193
+    amax partials folded in two rounds of the scale kernel's loads."""
+    dev = device()
+    announce("dsa nvfp4, 524352 rows")
+    w = synth.dsa_rotate_fp8(tokens=8193, heads=64, d_pe=64, seed=80)
+    pe, nope = w.tensors["pe"].to(dev), w.tensors["nope"].to(dev)
+    compare_dsa4(orc, bits16(w.tensors["pe"]), bits16(w.tensors["nope"]), pe, nope, amax_out=True)
+
+
 # ============================================================== grouped NVFP4
 def compare_grouped(orc, x_dev, sections, mask, flags, seed=None, ro=None, co=None, out=None, threads=8,
                     workspace=None):
@@ -733,14 +743,14 @@ def test_grouped_hand_case_b9(orc):
 
 # ============================================================== supplied amax (single pass)
 def compare_grouped_amax(orc, x_dev, sections, mask, flags, amax_in, seed=None, ro=None, co=None,
-                         workspace=None):
+                         workspace=None, amax_out=True):
     """The call with supplied maxima (device tensors, or None) and measured maxima out,
     against the oracle given the same maxima."""
     dev = x_dev.device
     ain = None
     if amax_in is not None:
         ain = tuple(None if a is None else torch.tensor(np.asarray(a, np.float32), device=dev) for a in amax_in)
-    call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, amax_in=ain, amax_out=True,
+    call = mxq.GroupedNVFP4(x_dev, sections, mask, flags, seed, ro, co, amax_in=ain, amax_out=amax_out,
                             workspace=workspace)
     res = call()
     torch.cuda.synchronize()
@@ -748,9 +758,9 @@ def compare_grouped_amax(orc, x_dev, sections, mask, flags, amax_in, seed=None, 
                                     amax_in=amax_in)
     names = []
     if flags & 1:
-        names += ["row_global", "row_scales", "row_codes", "row_amax"]
+        names += ["row_global", "row_scales", "row_codes"] + (["row_amax"] if amax_out else [])
     if flags & 2:
-        names += ["col_global", "col_scales", "col_codes", "col_amax"]
+        names += ["col_global", "col_scales", "col_codes"] + (["col_amax"] if amax_out else [])
     if flags & 4:
         names += ["fp8_scales", "fp8_codes"]
     for n in names:
@@ -785,6 +795,34 @@ def test_grouped_supplied_amax(orc, scale):
         torch.cuda.synchronize()
         for n in ("row_codes", "row_scales", "row_global", "col_codes", "col_scales", "col_global"):
             assert torch.equal(getattr(res, n), getattr(plain, n)), n
+
+
+@pytest.mark.parametrize("flags,sr", [(3, False), (7, True), (2, False)])
+def test_grouped_supplied_amax_no_out(orc, flags, sr):
+    """Supplied maxima with no maxima out, with stochastic rounding and FP8 too
+    (empty sections included: their scales come from their supplied maxima)."""
+    dev = device()
+    announce(f"grouped supplied amax, none out: flags={flags} sr={sr}")
+    w = synth.grouped_nvfp4_sr(total_rows=2048, k=1024, parts=7, forced_empty=2, seed=58)
+    x, p = w.tensors["x"].to(dev), w.params
+    sec, mask = p["split_sections"], p["sign_mask"]
+    rng = np.random.default_rng(59)
+    amax_in = (rng.uniform(0.5, 8, 7).astype(np.float32), rng.uniform(0.5, 8, 7).astype(np.float32))
+    if not flags & 1:
+        amax_in = (None, amax_in[1])
+    seed, ro, co = (p["seed"], p["row_offsets"], p["col_offsets"]) if sr else (None, None, None)
+    compare_grouped_amax(orc, x, sec, mask, flags, amax_in, seed=seed, ro=ro, co=co, amax_out=False)
+
+
+def test_grouped_large_section_scales_kernel(orc):
+    """A section of 8320 x 4096 (1040 amax partials, a fold over several rounds of
+    the scales kernel's loads) beside small and empty ones; the measured maxima out
+    as well."""
+    dev = device()
+    announce("grouped: a large section (8320 rows x 4096) beside small ones")
+    w = synth.grouped_nvfp4(total_rows=8576, k=4096, parts=1, seed=60)
+    x = w.tensors["x"].to(dev)
+    compare_grouped_amax(orc, x, [128, 8320, 0, 128], 0x6A95, 3, None)
 
 
 def test_grouped_supplied_amax_sr_fp8_edges(orc):
