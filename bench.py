@@ -46,7 +46,7 @@ def parse():
                              "fp8_blockwise", "fp8_1x128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="steady-state steps only, then one 256 MiB device copy and one 128 MiB read twice "
+                    help="steady-state steps only, then the hand-written 256 MiB copy and 128 MiB read (twice) "
                          "(the counter calibrations for rocprofv3 runs); prints a short JSON line")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows of the workload the oracle baseline runs on (0: the whole workload, "
@@ -221,12 +221,15 @@ def main():
 
     if args.profile:
         del calls
+        ceil = ceiling_lib()
         a = torch.ones(1 << 27, dtype=torch.int16, device=dev)
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        b.copy_(a)                                        # 256 MiB read + 256 MiB written
+        # the counters' calibration: a hand-written copy of 256 MiB (256 MiB read, 256
+        # MiB written), then a 128 MiB streaming read, twice
+        if ceil.mxq_ceiling_copy(a.data_ptr(), b.data_ptr(), 2 * a.numel(), stream.cuda_stream) != 0:
+            raise RuntimeError("mxq_ceiling_copy failed")
         torch.cuda.synchronize()
-        ceil = ceiling_lib()
         sink = torch.empty((ceil.mxq_ceiling_grid(),), dtype=torch.int32, device=dev)
         c = torch.ones(1 << 26, dtype=torch.int16, device=dev)   # 128 MiB, read twice
         for _ in range(2):
@@ -321,19 +324,27 @@ def main():
 
 # HBM bytes per call from the committed counter summaries (rocprofv3 --pmc), used
 # only while the kernel sources they were taken on are unchanged.
+# Counter summaries under profiles/ holding a line "- hbm_bytes_per_call[<workload>]: N"
+# (bytes read + written at the memory side per call, every kernel of the call) and the
+# digest of the kernel sources they were measured with.
 TRAFFIC_SUMMARIES = {"grouped_nvfp4_rht": "profiles/grouped_nvfp4_rht_16384x4096_hbm_traffic.md"}
-KERNEL_SOURCES = ["nvfp4_quantization_amd/csrc/mxq_nvfp4.hip", "nvfp4_quantization_amd/csrc/mxq_nvfp4_impl.hpp",
-                  "nvfp4_quantization_amd/csrc/mxq_nvfp4_quant_rne.hip",
-                  "nvfp4_quantization_amd/csrc/mxq_device.hpp", "nvfp4_quantization_amd/csrc/mxq_internal.hpp"]
+for _wl in ("grouped_nvfp4_rht_sr", "grouped_nvfp4_rht_given", "large_moe_nvfp4_fp8", "dsa_rotate_nvfp4",
+            "dsa_rotate_fp8", "swiglu_fp8", "fp8_blockwise", "fp8_1x128"):
+    TRAFFIC_SUMMARIES[_wl] = "profiles/other_workloads_hbm_traffic.md"
+KERNEL_SOURCE_DIR = "nvfp4_quantization_amd/csrc"
 
 
 def kernel_source_digest() -> str:
+    """SHA-256 over every kernel and host source of the library, in name order (a
+    change to any of them makes the stored counter figures stale)."""
     import hashlib
-    here = os.path.dirname(os.path.abspath(__file__))
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), KERNEL_SOURCE_DIR)
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(here, f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(here)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(here, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()
 
 
@@ -354,7 +365,7 @@ def measured_traffic(wl):
     if fields.get("kernel_source_sha256") != kernel_source_digest():
         return None
     try:
-        return int(fields["hbm_bytes_per_call"])
+        return int(fields[f"hbm_bytes_per_call[{wl}]"])
     except (KeyError, ValueError):
         return None
 
