@@ -149,12 +149,34 @@ __device__ __forceinline__ uint32_t rbyte_hi(uint32_t w) {
 // non-NaN FP32 value and every r.  (The pair's second value draws on the random
 // operand differently, so each value gets a conversion of its own.)
 //
-// The code of q alone (low nibble of the result, other bits cleared).  The builtin's
-// first operand does not reach the instruction: the compiler gives it a fresh
-// destination register and the bytes it does not write hold that register's earlier
-// contents, so the code is masked out of it and the pair is packed by shifts.
-__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t r_hi) {
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{q, 0.0f}, r_hi, 1.0f, 0) & 0xFu;
+// Eight such codes packed (nibble i = code of q[i] with random byte rb[i], each given
+// as r << 24).  The conversion writes one byte of its destination and keeps the other
+// three, but the builtin's first operand does not reach the instruction (the compiler
+// gives it a fresh destination whose other bytes are stale), so the eight conversions
+// are written out with the destinations kept: even elements into bytes 0..3 of e, odd
+// ones into o, each code in the low nibble of its byte.  A pair's second slot holds
+// the random operand itself, which already sits in the register after q, so forming
+// the pair costs no move; its code fills the byte's high nibble and is masked off.  A
+// byte-select write needs one wait state before the next instruction reads that
+// register; the order alternates e and o so no conversion reads the one just before
+// (after the block the compiler inserts the wait itself).
+__device__ __forceinline__ uint32_t e2m1_sr8(const float (&q)[8], const uint32_t (&rb)[8]) {
+    uint32_t e, o;
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %2, %10, 1.0\n\t"
+        "v_cvt_scalef32_sr_pk_fp4_f32 %1, %3, %11, 1.0\n\t"
+        "v_cvt_scalef32_sr_pk_fp4_f32 %0, %4, %12, 1.0 op_sel:[0,0,1,0]\n\t"
+        "v_cvt_scalef32_sr_pk_fp4_f32 %1, %5, %13, 1.0 op_sel:[0,0,1,0]\n\t"
+        "v_cvt_scalef32_sr_pk_fp4_f32 %0, %6, %14, 1.0 op_sel:[0,0,0,1]\n\t"
+        "v_cvt_scalef32_sr_pk_fp4_f32 %1, %7, %15, 1.0 op_sel:[0,0,0,1]\n\t"
+        "v_cvt_scalef32_sr_pk_fp4_f32 %0, %8, %16, 1.0 op_sel:[0,0,1,1]\n\t"
+        "v_cvt_scalef32_sr_pk_fp4_f32 %1, %9, %17, 1.0 op_sel:[0,0,1,1]"
+        : "=&v"(e), "=&v"(o)
+        : "v"(f32x2{q[0], __builtin_bit_cast(float, rb[0])}), "v"(f32x2{q[1], __builtin_bit_cast(float, rb[1])}),
+          "v"(f32x2{q[2], __builtin_bit_cast(float, rb[2])}), "v"(f32x2{q[3], __builtin_bit_cast(float, rb[3])}),
+          "v"(f32x2{q[4], __builtin_bit_cast(float, rb[4])}), "v"(f32x2{q[5], __builtin_bit_cast(float, rb[5])}),
+          "v"(f32x2{q[6], __builtin_bit_cast(float, rb[6])}), "v"(f32x2{q[7], __builtin_bit_cast(float, rb[7])}),
+          "v"(rb[0]), "v"(rb[1]), "v"(rb[2]), "v"(rb[3]), "v"(rb[4]), "v"(rb[5]), "v"(rb[6]), "v"(rb[7]));
+    return (e & 0x0F0F0F0Fu) | ((o << 4) & 0xF0F0F0F0u);
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each round's two 32 x 32-bit

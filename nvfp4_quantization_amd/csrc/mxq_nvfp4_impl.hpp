@@ -222,8 +222,7 @@ __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, co
         const uint32_t wa = r0 == 0 ? rnd.x : rnd.z, wb = r0 == 0 ? rnd.y : rnd.w;
         const uint32_t r[8] = {rbyte_hi<0>(wa), rbyte_hi<1>(wa), rbyte_hi<2>(wa), rbyte_hi<3>(wa),
                                rbyte_hi<0>(wb), rbyte_hi<1>(wb), rbyte_hi<2>(wb), rbyte_hi<3>(wb)};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c |= e2m1_sr(q[i], r[i]) << (4 * i);
+        c = e2m1_sr8(q, r);
     }
     return c;
 }

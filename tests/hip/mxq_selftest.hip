@@ -12,16 +12,21 @@
 //          exceed that); a NaN gives a NaN code (low 7 bits 0x7F).
 //   E2M1   v_cvt_scalef32_pk_fp4_f32 with scale 1, both nibbles of bytes 0 and 3:
 //          nearest-even with saturation to 6 for every non-NaN input, the sign kept.
-//   E2M1 stochastic   v_cvt_scalef32_sr_pk_fp4_f32 with scale 1, the value in the
-//          pair's first slot and the random operand r << 24: for grid spacing D
-//          (0.5 / 1 / 2 below 2 / 4 / 6) and |q| / D = k + f, the code rounds up iff
-//          floor(256 f) + r >= 256; |q| >= 6 saturates; swept over every non-NaN q
-//          and every r (in two classes: |q| in [2^-20, 16), and the rest).
+//   E2M1 stochastic   v_cvt_scalef32_sr_pk_fp4_f32 with scale 1 as the quantizers
+//          issue it (mxq::e2m1_sr8: eight conversions, the value in the pair's first
+//          slot, the random operand r << 24 in both the second slot and the random
+//          operand, each code written into one byte of a kept destination, then
+//          packed): for grid spacing D (0.5 / 1 / 2 below 2 / 4 / 6) and
+//          |q| / D = k + f, the code rounds up iff floor(256 f) + r >= 256; |q| >= 6
+//          saturates; swept over every non-NaN q, both signs, every r and every
+//          nibble position (in two classes: |q| in [2^-20, 16), and the rest).
 //
 // Every kernel is a grid-stride loop over a fixed index range whose only memory
 // accesses are one atomic per wave into its result words at the end.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "mxq_device.hpp"
 
 namespace {
 
@@ -157,14 +162,22 @@ __global__ __launch_bounds__(256) void k_sweep_sr(u64* out) {
     const u64 stride = (u64)gridDim.x * blockDim.x;
     for (u64 m = (u64)blockIdx.x * blockDim.x + threadIdx.x; m <= 0x7F800000ull; m += stride) {
         const bool in = m >= 0x35800000ull && m < 0x41800000ull;
+        // nibble i holds sign s ^ (i & 1) with random byte r0 + i: over both s, every
+        // (sign, r) pair is checked once
         for (uint32_t s = 0; s < 2; ++s) {
-            const uint32_t b = (uint32_t)m | (s << 31);
-            const float q = __builtin_bit_cast(float, b);
-            for (uint32_t r = 0; r < 256; ++r) {
-                const uint32_t got = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{q, 0.0f}, r << 24, 1.0f, 0) & 0xFu;
-                if (got != ref_e2m1_sr(b, r)) {
-                    if (in) { ++bad_in; keep_min(first_in, ((u64)b << 8) | r); }
-                    else { ++bad_out; keep_min(first_out, ((u64)b << 8) | r); }
+            const uint32_t b0 = (uint32_t)m | (s << 31);
+            float q[8];
+            for (int i = 0; i < 8; ++i) q[i] = __builtin_bit_cast(float, b0 ^ ((uint32_t)(i & 1) << 31));
+            for (uint32_t r0 = 0; r0 < 256; r0 += 8) {
+                uint32_t rb[8];
+                for (int i = 0; i < 8; ++i) rb[i] = (r0 + i) << 24;
+                const uint32_t got = mxq::e2m1_sr8(q, rb);
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t b = b0 ^ ((uint32_t)(i & 1) << 31), r = r0 + i;
+                    if (((got >> (4 * i)) & 0xFu) != ref_e2m1_sr(b, r)) {
+                        if (in) { ++bad_in; keep_min(first_in, ((u64)b << 8) | r); }
+                        else { ++bad_out; keep_min(first_out, ((u64)b << 8) | r); }
+                    }
                 }
             }
             seen += 256;
