@@ -109,10 +109,24 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, *tensors) -> ctypes.c_void_p:
+    """Handle of the stream a call is enqueued on: torch's current stream by default,
+    else a torch stream or a raw HIP stream handle.  The binding allocates outputs and
+    workspaces (and fills workspaces) on the current stream, so a call on another stream
+    first makes that stream wait for the current one, and records on it every tensor
+    the call reads or writes: torch's caching allocator then keeps their memory from
+    other work until the call has ended."""
+    cur = torch.cuda.current_stream()
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return ctypes.c_void_p(cur.cuda_stream)
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    if stream.cuda_stream != cur.cuda_stream:
+        stream.wait_stream(cur)
+        for t in tensors:
+            if isinstance(t, torch.Tensor) and t.is_cuda:
+                t.record_stream(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _check(status: int, what: str):
@@ -161,7 +175,7 @@ def mxq_quant_fp8_1x128(x: torch.Tensor, q: Optional[torch.Tensor] = None, scale
     srow, sgroup = (1, m) if scale_transposed else (k // 128, 1)
     ldq = q.stride(0) if m > 0 else k
     _check(lib().mxq_quant_fp8_1x128(_ptr(x), m, k, ldx, _ptr(q), ldq, _ptr(scales), srow, sgroup,
-                                     _stream(stream)), "mxq_quant_fp8_1x128")
+                                     _stream(stream, x, q, scales)), "mxq_quant_fp8_1x128")
     return q, scales
 
 
@@ -184,7 +198,7 @@ def mxq_hadamard_quant_fp8(pe: Optional[torch.Tensor], nope: Optional[torch.Tens
     ld_pe = _row_stride(pe)
     ld_nope = _row_stride(nope)
     _check(lib().mxq_hadamard_quant_fp8(_ptr(pe), ld_pe, d_pe, _ptr(nope), ld_nope, m, _ptr(q), _ptr(scales),
-                                        _stream(stream)), "mxq_hadamard_quant_fp8")
+                                        _stream(stream, pe, nope, q, scales)), "mxq_hadamard_quant_fp8")
     return q, scales
 
 
@@ -211,7 +225,8 @@ def mxq_quant_fp8_blockwise(x: torch.Tensor, options: int = 0, rowwise: bool = T
         co = _FP8BlockOut(_ptr(cq), ld, _ptr(cs), nb, 1)
     _check(lib().mxq_quant_fp8_blockwise(_ptr(x), m, k, _row_stride(x), options,
                                          ctypes.byref(ro) if ro is not None else None,
-                                         ctypes.byref(co) if co is not None else None, _stream(stream)),
+                                         ctypes.byref(co) if co is not None else None,
+                                         _stream(stream, x, rq, rs, cq, cs)),
            "mxq_quant_fp8_blockwise")
     return rq, rs, (cq[:, :m] if cq is not None else None), cs
 
@@ -234,7 +249,8 @@ def mxq_hadamard_quant_fp8_ex(pe: Optional[torch.Tensor], nope: Optional[torch.T
     if scales is None:
         scales = torch.empty((m,), dtype=torch.float32, device=ref.device)
     _check(lib().mxq_hadamard_quant_fp8_ex(_ptr(pe), _row_stride(pe), d_pe, _ptr(nope), _row_stride(nope), m,
-                                           options, heads, _ptr(q), _ptr(scales), st, sh, _stream(stream)),
+                                           options, heads, _ptr(q), _ptr(scales), st, sh,
+                                           _stream(stream, pe, nope, q, scales)),
            "mxq_hadamard_quant_fp8_ex")
     return q, scales
 
@@ -259,7 +275,8 @@ def mxq_swiglu_quant_fp8(gate: torch.Tensor, up: torch.Tensor, q: Optional[torch
         scales = torch.empty(shape, dtype=torch.float32, device=gate.device)
     sr, sg = (1, m) if scale_transposed else (n // 128, 1)
     _check(lib().mxq_swiglu_quant_fp8(_ptr(gate), _row_stride(gate), _ptr(up), _row_stride(up), m, n,
-                                      _ptr(q), _row_stride(q), _ptr(scales), sr, sg, _stream(stream)),
+                                      _ptr(q), _row_stride(q), _ptr(scales), sr, sg,
+                                      _stream(stream, gate, up, q, scales)),
            "mxq_swiglu_quant_fp8")
     return q, scales
 
@@ -312,7 +329,9 @@ class HadamardNVFP4:
         _check(lib().mxq_hadamard_quant_nvfp4(
             _ptr(self.pe), _row_stride(self.pe), self.d_pe, _ptr(self.nope), _row_stride(self.nope), self.m,
             _ptr(self.amax_in), _ptr(o.amax), _ptr(o.codes), _ptr(o.scales), _ptr(o.global_scale),
-            _ptr(self.workspace), self.workspace.numel(), _stream(stream)), "mxq_hadamard_quant_nvfp4")
+            _ptr(self.workspace), self.workspace.numel(),
+            _stream(stream, self.pe, self.nope, self.amax_in, o.amax, o.codes, o.scales, o.global_scale,
+                    self.workspace)), "mxq_hadamard_quant_nvfp4")
         return o
 
 
@@ -434,20 +453,25 @@ class GroupedNVFP4:
                            ctypes.addressof(self._ro) if self._ro is not None else None,
                            ctypes.addressof(self._co) if self._co is not None else None)
 
+    def _tensors(self) -> list:
+        return [self.x, self.workspace, *_out_tensors(self.out),
+                *(self._amax_in if self._amax is not None else ())]
+
     def __call__(self, stream=None) -> NVFP4Result:
         if self._amax is None:
             st = lib().mxq_group_rht_quant_nvfp4(
                 _ptr(self.x), self.k, ctypes.addressof(self.sections), self.S, self.mask, self.flags,
                 ctypes.addressof(self._sr) if self._sr is not None else None,
                 ctypes.addressof(self._row), ctypes.addressof(self._col), ctypes.addressof(self._fp8),
-                _ptr(self.workspace), self.workspace.numel(), _stream(stream))
+                _ptr(self.workspace), self.workspace.numel(), _stream(stream, *self._tensors()))
             _check(st, "mxq_group_rht_quant_nvfp4")
         else:
             st = lib().mxq_group_rht_quant_nvfp4_with_amax(
                 _ptr(self.x), self.k, ctypes.addressof(self.sections), self.S, self.mask, self.flags,
                 ctypes.addressof(self._sr) if self._sr is not None else None,
                 ctypes.addressof(self._row), ctypes.addressof(self._col), ctypes.addressof(self._fp8),
-                ctypes.addressof(self._amax), _ptr(self.workspace), self.workspace.numel(), _stream(stream))
+                ctypes.addressof(self._amax), _ptr(self.workspace), self.workspace.numel(),
+                _stream(stream, *self._tensors()))
             _check(st, "mxq_group_rht_quant_nvfp4_with_amax")
         return self.out
 
@@ -480,9 +504,14 @@ def mxq_group_rht_quant_nvfp4_noalloc(x: torch.Tensor, split_sections: Sequence[
     st = lib().mxq_group_rht_quant_nvfp4_noalloc(
         _ptr(x), k, ctypes.addressof(sections), S, rht_sign_mask & 0xFFFF, flags,
         ctypes.addressof(sr) if sr is not None else None, ctypes.addressof(row), ctypes.addressof(col),
-        ctypes.addressof(fp8), _stream(stream))
+        ctypes.addressof(fp8), _stream(stream, x, *_out_tensors(out)))
     _check(st, "mxq_group_rht_quant_nvfp4_noalloc")
     return out
+
+
+def _out_tensors(o: NVFP4Result) -> list:
+    return [o.row_codes, o.row_scales, o.row_global, o.col_codes, o.col_scales, o.col_global, o.fp8_codes,
+            o.fp8_scales, o.row_amax, o.col_amax]
 
 
 def _addr(t: Optional[torch.Tensor]):

@@ -181,7 +181,9 @@ __device__ __forceinline__ uint32_t e2m1_sr8(const float (&q)[8], const uint32_t
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each round's two 32 x 32-bit
 // products are formed whole (64 bits), one v_mad_u64_u32 each: the separate low and
-// high multiplies would cost two quarter-rate instructions per product.
+// high multiplies would cost two quarter-rate instructions per product.  After the
+// first round each three-way XOR is one v_bitop3_b32 (truth table 0x96), which the
+// compiler does not form from the two XORs by itself.
 struct u32x4 { uint32_t x, y, z, w; };
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -190,9 +192,14 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
         const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
         const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         u32x4 n;
-        n.x = hi1 ^ c.y ^ k0;
+        if (i == 0) {                            // c.y, c.w may be uniform: let the compiler pair them
+            n.x = hi1 ^ (c.y ^ k0);
+            n.z = hi0 ^ (c.w ^ k1);
+        } else {
+            n.x = __builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96);
+            n.z = __builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96);
+        }
         n.y = lo1;
-        n.z = hi0 ^ c.w ^ k1;
         n.w = lo0;
         c = n;
         k0 += 0x9E3779B9u;

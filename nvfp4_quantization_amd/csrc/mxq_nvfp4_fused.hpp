@@ -119,7 +119,7 @@ __device__ __forceinline__ void tile_maxima(const uint4 (&p)[16][2], uint32_t si
 struct FusedLds {
     QuantLds<4> q;
     uint32_t max[2][4];                               // per-wave maxima: BF16 bits of max |x|, FP32 max |H16 D x|
-    uint32_t none[4];
+    uint32_t none[kTableLdsWords];
     float amax[2];
     int ok;                                           // 0: give up (error), 1: go on, 2: deferred
     uint64_t deferred[kFusedMaxItems / 64];         // the last item's list of deferred items of its section

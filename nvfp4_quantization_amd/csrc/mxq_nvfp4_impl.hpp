@@ -31,10 +31,12 @@
 // lies within about 2^-21 (relative) of one of the seven E2M1 rounding boundaries
 // 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; BF16 values are 2^-8 apart, so only the two
 // BF16 neighbours of each boundary times d can, and those fourteen are checked
-// against the exact division for ym = y and its nearest neighbours.  A pass (one
-// direction of one section) takes one multiply per element when every scale code
-// of its table has a multiplier, else (and always with stochastic rounding, which
-// needs the exact quotient) the exact division.  Codes without a multiplier come
+// against the exact division for ym = y and its nearest neighbours.  With
+// stochastic rounding the rule reads more of the quotient (its grid spacing and
+// floor(256 f)), and the table holds a multiplier that keeps that part of the exact
+// quotient for every BF16 u (build_tables_wg).  A pass (one direction of one
+// section) takes one multiply per element when every scale code of its table has a
+// multiplier, else the exact division.  Codes without a nearest-even multiplier come
 // from short divisors whose exact boundary ties need opposite roundings; they arise
 // when the section amax carries a factor of 3 (2688 = 2^7 * 3 * 7).  Column values enter unscaled: BF16(x/4) =
 // BF16(x)/4 and fl((u/4)/d) = fl(u/(4d)) whenever x/4 is a normal number, and
@@ -109,6 +111,12 @@ __device__ float product_multiplier(float d, float y) {
 __device__ __forceinline__ uint32_t absmax_nonan_pairs(uint32_t acc, uint32_t w) {
     return absmax_pk_nonan(acc, w);
 }
+
+// Blocks whose random words are drawn together under stochastic rounding.
+#ifndef MXQ_SR_CHAINS
+#define MXQ_SR_CHAINS 4
+#endif
+constexpr int kSrChains = MXQ_SR_CHAINS;
 
 __device__ __forceinline__ u32x4 block_random(uint64_t seed, uint64_t off, uint64_t beta) {
     u32x4 c = {(uint32_t)off, (uint32_t)(off >> 32), (uint32_t)beta, (uint32_t)(beta >> 32)};
@@ -196,10 +204,15 @@ __device__ __forceinline__ float absmax16_nan(const float (&v)[16]) {
 }
 
 // E2M1 codes of 8 values u[0..7] (element 2i in the low nibble of byte i):
-// nearest-even of u * y (MUL), of fl(u / d), or stochastic with random bytes
-// r0 .. r0+7 of rnd.  IEEE: the quotients with IEEE's special cases (an infinite u,
-// or an overflowing quotient), which only a block whose scale saturated can meet.
-enum class Enc { Mul, Div, Sr };
+// nearest-even of u * y (MUL) or of fl(u / d) (DIV), or stochastic with random bytes
+// r0 .. r0+7 of rnd, of fl(u / d) (SR) or of u * y (SR_MUL).  IEEE: the quotients
+// with IEEE's special cases (an infinite u, or an overflowing quotient), which only a
+// block whose scale saturated can meet.
+enum class Enc { Mul, Div, Sr, SrMul };
+template <Enc E>
+struct EncTag {
+    static constexpr Enc value = E;
+};
 template <Enc E, bool IEEE = false>
 __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, const u32x4& rnd, int r0) {
     uint32_t c = 0;
@@ -217,7 +230,8 @@ __device__ __forceinline__ uint32_t encode8(const float* u, float d, float y, co
     } else {
         float q[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = IEEE ? div_ieee(u[i], d, y) : div_rn(u[i], d, y);
+        for (int i = 0; i < 8; ++i)
+            q[i] = E == Enc::SrMul ? u[i] * y : IEEE ? div_ieee(u[i], d, y) : div_rn(u[i], d, y);
         // random bytes r0 .. r0 + 7: word r0 / 4 and the next (r0 is 0 or 8)
         const uint32_t wa = r0 == 0 ? rnd.x : rnd.z, wb = r0 == 0 ? rnd.y : rnd.w;
         const uint32_t r[8] = {rbyte_hi<0>(wa), rbyte_hi<1>(wa), rbyte_hi<2>(wa), rbyte_hi<3>(wa),
@@ -339,14 +353,15 @@ template <Enc E>
 __device__ __forceinline__ BlockOut encode_block(const float (&u)[16], uint32_t sc, const float4* tab,
                                                  const u32x4& rnd) {
     const float4 e = tab[sc];
-    const float d = e.x, y = E == Enc::Mul ? __builtin_fabsf(e.z) : e.y;
+    const float d = e.x, y = (E == Enc::Mul || E == Enc::SrMul) ? __builtin_fabsf(e.z) : e.y;
     const uint32_t keep = __builtin_bit_cast(uint32_t, e.w);
     BlockOut o;
     // Only a saturated scale lets a value be infinite or a quotient overflow (below it
     // |u / d| stays near 6 or less, where div_rn is exact).  The division path takes
     // the IEEE quotients throughout (one more operation per element, cheaper than a
-    // branch per block); stochastic rounding, where the division is on every element,
-    // branches.
+    // branch per block); stochastic rounding by division, where the division is on
+    // every element, branches.  (A product is infinite exactly where the quotient is,
+    // and saturates the same way.)
     if (E == Enc::Sr && sc == 0x7Eu) {
         o.codes = make_uint2(encode8<E, true>(u, d, y, rnd, 0) & keep, encode8<E, true>(u + 8, d, y, rnd, 8) & keep);
     } else {
@@ -443,13 +458,27 @@ __device__ __forceinline__ float row_pass(const Nvfp4Group& G, const uint4 (&p)[
         return block_random(G.seed, G.row_off[s], (uint64_t)((r_local0 + t) * (k >> 4) + (c0 >> 4)));
     };
     if (SR && G.sr_row) {
-        // two rows at a time, as below: their Philox chains (ten dependent rounds of
-        // quarter-rate multiplies each) overlap
+        // kSrChains rows at a time, their Philox chains (ten dependent rounds of
+        // quarter-rate multiplies each) all drawn before the first is used, so that
+        // they overlap (the dividing encode branches on a saturated scale, and no
+        // chain drawn after a branch would overlap one drawn before it).  By product
+        // when every scale code of the row table has a stochastic multiplier.
+        auto rows = [&](auto enc) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            put(t, row_block<Enc::Sr>(p, t, g_r, yg_r, tab_r, rnd_of(t)));
-            if (t & 1) __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int t0 = 0; t0 < 16; t0 += kSrChains) {
+                u32x4 rnd[kSrChains];
+#pragma unroll
+                for (int i = 0; i < kSrChains; ++i) rnd[i] = rnd_of(t0 + i);
+#pragma unroll
+                for (int i = 0; i < kSrChains; ++i)
+                    put(t0 + i, row_block<decltype(enc)::value>(p, t0 + i, g_r, yg_r, tab_r, rnd[i]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (div_mode)
+            rows(EncTag<Enc::Sr>{});
+        else
+            rows(EncTag<Enc::SrMul>{});
     } else if (div_mode) {
         // the section's row table has a scale code without a multiplier: exact division
 #pragma unroll
@@ -500,18 +529,74 @@ __device__ __forceinline__ float4 table_entry(int code, float g, bool quarter) {
 // (m = lane) once; each entry takes it scaled by 2^-e when its own d and fl(1/d)
 // are the representative's scaled exactly and g < 2^100 keeps every intermediate
 // value of the search normal and finite, and searches on its own otherwise.
-// Every thread of the work-group calls it (it holds a barrier).  sh_none: 4 words
-// of LDS.
+// A direction with stochastic rounding takes stochastic multipliers instead: ym
+// such that fl(u * ym) and fl(u / d) give the stochastic rule the same grid spacing
+// and the same floor(256 f), hence the same code for every random byte, for every
+// BF16 u.  Every grid point of the rule (the multiples of D/256 below 6, and 6) is
+// a multiple of 2^(E-9) in the binade [2^E, 2^(E+1)) of the quotient it bounds, so
+// two positive quotients that agree in exponent and in the top 9 mantissa bits fall
+// in the same cell of every binade.  Scaling u by a power of two scales both
+// quotients exactly (while they stay normal), so the 128 BF16 significands
+// u = 1 + k/128 decide it for every BF16 u: a candidate (y, y - 1 ulp, y + 1 ulp)
+// qualifies when for each of them fl(u * ym) and the exact fl(u / d) share their bits
+// above the 14th.  Each (direction, m) representative is checked this way by the
+// whole work-group (2048 pairs), and an entry takes its representative's multiplier
+// scaled by 2^-e under the same condition as above, else none.
+// Every thread of the work-group calls it (it holds barriers).  sh: kTableLdsWords
+// words of LDS.
+constexpr int kTableLdsWords = 4 + 16 + 16;
 template <bool ROW, bool COL>
 __device__ __forceinline__ void build_tables_wg(const Nvfp4Group& G, int s, float g_r, float g_c,
-                                                float4 (*tab)[128], uint32_t* sh_none, int tid) {
+                                                float4 (*tab)[128], uint32_t* sh, int tid) {
     const int lane = tid & 63;
     const bool in = tid < 256;
     const int dir = (tid >> 7) & 1, code = tid & 127;           // dir is wave-uniform
     const bool active = in && (dir == 0 ? ROW : COL);
+    const bool sr_r = ROW && G.sr_row, sr_c = COL && G.sr_col;
+    const bool sr_dir = dir == 0 ? sr_r : sr_c;
     const float g = dir ? g_c : g_r;
+    uint32_t* const sh_none = sh;
+    uint32_t* const sh_fail = sh + 4;                            // [dir * 8 + m]: bit c, candidate c fails
+    float* const sh_sr = reinterpret_cast<float*>(sh + 20);     // [dir * 8 + m]: the multiplier, or < 0
+    // candidates of representative (jd, m)
+    auto rep = [&](int jd, int m, float (&ym)[3]) {
+        float d = (1.0f + (float)m * 0.125f) * (jd ? g_c : g_r);
+        float y = 1.0f / d;
+        if (jd) { d *= 4.0f; y *= 0.25f; }
+        const uint32_t yb = __builtin_bit_cast(uint32_t, y);
+        ym[0] = y;
+        ym[1] = __builtin_bit_cast(float, yb - 1u);
+        ym[2] = __builtin_bit_cast(float, yb + 1u);
+        return d;
+    };
+    if (sr_r || sr_c) {                                          // uniform over the work-group
+        if (tid < 16) sh_fail[tid] = 0u;
+        __syncthreads();
+        // a wave's 64 pairs share one representative (128 per representative)
+        for (int idx = tid; idx < 16 * 128; idx += (int)blockDim.x) {
+            const int job = idx >> 7, jd = job >> 3;
+            if (!(jd == 0 ? sr_r : sr_c)) continue;
+            float ym[3];
+            const float d = rep(jd, job & 7, ym);
+            const float u = 1.0f + (float)(idx & 127) * 0x1p-7f;
+            const uint32_t want = __builtin_bit_cast(uint32_t, div_rn(u, d, ym[0])) >> 14;
+            uint32_t f = 0;
+#pragma unroll
+            for (int c = 0; c < 3; ++c) f |= ((__builtin_bit_cast(uint32_t, u * ym[c]) >> 14) != want ? 1u : 0u) << c;
+            f = (__ballot(f & 1u) ? 1u : 0u) | (__ballot(f & 2u) ? 2u : 0u) | (__ballot(f & 4u) ? 4u : 0u);
+            if (lane == 0 && f) atomicOr(sh_fail + job, f);
+        }
+        __syncthreads();
+        if (tid < 16) {
+            float ym[3];
+            rep(tid >> 3, tid & 7, ym);
+            const uint32_t f = sh_fail[tid];
+            sh_sr[tid] = !(f & 1u) ? ym[0] : !(f & 2u) ? ym[1] : !(f & 4u) ? ym[2] : -1.0f;
+        }
+        __syncthreads();
+    }
     float rep_ym = 0.0f;
-    if (active && lane < 8) {
+    if (active && !sr_dir && lane < 8) {
         float d = (1.0f + (float)lane * 0.125f) * g;
         float y = 1.0f / d;
         if (dir) { d *= 4.0f; y *= 0.25f; }
@@ -531,7 +616,11 @@ __device__ __forceinline__ void build_tables_wg(const Nvfp4Group& G, int s, floa
             float rd = (1.0f + (float)m * 0.125f) * g, ry = 1.0f / rd;
             if (dir == 1) { d *= 4.0f; y *= 0.25f; rd *= 4.0f; ry *= 0.25f; }
             const bool scaled = g < 0x1p100f && d == __builtin_ldexpf(rd, ex) && y == __builtin_ldexpf(ry, -ex);
-            const float ym = scaled ? __builtin_ldexpf(cls_ym, -ex) : product_multiplier(d, y);
+            float ym;
+            if (sr_dir)
+                ym = scaled ? __builtin_ldexpf(sh_sr[dir * 8 + m], -ex) : -y;
+            else
+                ym = scaled ? __builtin_ldexpf(cls_ym, -ex) : product_multiplier(d, y);
             ent = make_float4(d, y, ym, k_keep_codes());
         }
         none = ent.z < 0.0f;
@@ -645,7 +734,7 @@ constexpr int kScalesThreads = 1024;
 template <bool ROW, bool COL, bool GIVEN>
 __global__ __launch_bounds__(kScalesThreads) void k_nvfp4_scales(const Nvfp4Group G, int ppt) {
     __shared__ uint32_t red[2][kScalesThreads / 64];
-    __shared__ uint32_t sh_none[4];
+    __shared__ uint32_t sh_tab[kTableLdsWords];
     const int s = blockIdx.x, tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
     float a_r = 0.0f, a_c = 0.0f;
     if (GIVEN) {
@@ -690,7 +779,7 @@ __global__ __launch_bounds__(kScalesThreads) void k_nvfp4_scales(const Nvfp4Grou
         if (ROW && G.amax_out_row) G.amax_out_row[s] = GIVEN ? 0.0f : a_r;
         if (COL && G.amax_out_col) G.amax_out_col[s] = GIVEN ? 0.0f : a_c;
     }
-    build_tables_wg<ROW, COL>(G, s, g_r, g_c, nullptr, sh_none, tid);
+    build_tables_wg<ROW, COL>(G, s, g_r, g_c, nullptr, sh_tab, tid);
 }
 
 // LDS of one work-group's quant passes (W waves, one tile each).
@@ -776,14 +865,28 @@ __device__ __forceinline__ void quant_passes(const Nvfp4Group& G, uint4 (&p)[16]
         };
         if (SR && G.sr_col) {
             const int64_t b_local = r_local0 >> 4;                  // section-local 16-row block
+            // kSrChains columns' Philox chains drawn together, by product or by
+            // division (as in the row pass)
+            auto cols = [&](auto enc) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const u32x4 rnd = block_random(G.seed, G.col_off[s], (uint64_t)((c0 + j) * (int64_t)(ms >> 4) + b_local));
-                const BlockOut o = column_block<Enc::Sr>(p, j, mask, g_c, yg_c, tab_c, rnd);
-                put(j, o);
-                if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
-                if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two columns' Philox chains overlap
-            }
+                for (int j0 = 0; j0 < 16; j0 += kSrChains) {
+                    u32x4 rnd[kSrChains];
+#pragma unroll
+                    for (int i = 0; i < kSrChains; ++i)
+                        rnd[i] = block_random(G.seed, G.col_off[s], (uint64_t)((c0 + j0 + i) * (int64_t)(ms >> 4) + b_local));
+#pragma unroll
+                    for (int i = 0; i < kSrChains; ++i) {
+                        const BlockOut o = column_block<decltype(enc)::value>(p, j0 + i, mask, g_c, yg_c, tab_c, rnd[i]);
+                        put(j0 + i, o);
+                        if (AOUT) col_amax = __builtin_fmaxf(col_amax, o.amax);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (tab_c[127].x != 0.0f)
+                cols(EncTag<Enc::Sr>{});
+            else
+                cols(EncTag<Enc::SrMul>{});
         } else if (tab_c[127].x != 0.0f) {
             // the section's column table has a scale code without a multiplier:
             // exact division for the whole pass

@@ -25,7 +25,18 @@
  *    BF16 values, for a set of tensor scales (random maxima over 2^-40 .. 2^40,
  *    maxima carrying the factors 3 and 7 of 2688, BF16 extremes, the 1e-10 floor).
  *
- * Usage: div_rn_check bf16 | sixth | general N SEED | tables N SEED
+ * 3. Stochastic multipliers (the same tables when a direction rounds stochastically).
+ *    The stochastic E2M1 rule reads, of q = fl(u / d), the grid spacing D (0.5, 1, 2
+ *    below 2, 4, 6) and floor(256 |q| / D), or only that |q| >= 6.  For each
+ *    representative divisor (1 + m/8) g (times 4 for columns) the first of the
+ *    candidates y, y - 1 ulp, y + 1 ulp for which fl(u * ym) and fl(u / d) agree in
+ *    every bit above the 14th for the 128 BF16 significands u = 1 + k/128 is taken; an
+ *    entry takes its representative's scaled by 2^-e when its own d and fl(1/d) are
+ *    the representative's scaled exactly and g < 2^100, else none.  The claim: for
+ *    every entry with a multiplier, fl(u * ym) and fl(u / d) have the same D and
+ *    floor(256 |q| / D) (or both saturate) for EVERY BF16 u, by brute force.
+ *
+ * Usage: div_rn_check bf16 | sixth | general N SEED | tables N SEED | srtables N SEED
  * Prints the number of checks and mismatches; exit status 0 when there are none. */
 #include <math.h>
 #include <stdint.h>
@@ -200,9 +211,92 @@ static void mode_tables(int n, uint64_t seed) {
     free(A);
 }
 
+/* ---------------------------------------------------------------- stochastic tables */
+/* What the stochastic rule reads of a non-NaN quotient q: -1 when |q| >= 6, else
+ * floor(256 |q| / D) + 4096 * (index of D), computed in double from the rule's own
+ * terms (|q| / D = k + f; 256 k + floor(256 f)). */
+static long sr_cell(float q) {
+    const double a = fabs((double)q);
+    if (!(a < 6.0)) return -1;
+    const int di = a < 2.0 ? 0 : (a < 4.0 ? 1 : 2);
+    const double D = di == 0 ? 0.5 : (di == 1 ? 1.0 : 2.0);
+    return (long)floor(a / D * 256.0) + 4096L * di;
+}
+
+/* The stochastic multiplier search as the tables state it: the first candidate for
+ * which fl(u * ym) and fl(u / d) agree above bit 14 for every u = 1 + k/128; -1 when
+ * none does. */
+static float find_sr_multiplier(float d, float y) {
+    const float ym[3] = {y, from_bits(to_bits(y) - 1u), from_bits(to_bits(y) + 1u)};
+    for (int c = 0; c < 3; ++c) {
+        int ok = 1;
+        for (int k = 0; k < 128; ++k) {
+            const float u = 1.0f + (float)k / 128.0f;
+            ok &= (to_bits(u * ym[c]) >> 14) == (to_bits(u / d) >> 14);
+        }
+        if (ok) return ym[c];
+    }
+    return -1.0f;
+}
+
+static void mode_srtables(int n, uint64_t seed) {
+    float* A = malloc(sizeof(float) * (size_t)(n + 64));
+    int na = 0;
+    const float fixed[] = {0.0f, 1e-10f, 1.0f, 3.0f, 7.0f, 21.0f, 2688.0f, 6.0f, 448.0f, 0.75f, 1.5f,
+                           from_bits(0x7F7F0000u), from_bits(0x00800000u), 3.0f * 1024.0f, 7.0f / 1024.0f,
+                           from_bits(0x40400000u | 0x10000u), 12.0f, 1e30f, 1e-30f};
+    for (size_t i = 0; i < sizeof fixed / sizeof fixed[0]; ++i) A[na++] = fixed[i];
+    uint64_t s = seed;
+    while (na < n) {
+        const uint64_t r = sm_next(&s);
+        const int e = (int)(r % 81) - 40;
+        const uint32_t sig = (uint32_t)((r >> 8) & 0x7F) << 16;
+        A[na++] = from_bits(((uint32_t)(e + 127) << 23) | sig);
+    }
+    const float floor_ = from_bits(0x2EDBE6FFu), inv2688 = from_bits(0x39C30C31u);
+    long long bad = 0, found = 0, none = 0;
+#pragma omp parallel for reduction(+ : bad, found, none) schedule(dynamic)
+    for (int i = 0; i < na; ++i) {
+        const float g = fmaxf(A[i], floor_) * inv2688;
+        for (int dir = 0; dir < 2; ++dir) {
+            float cls[8];
+            for (int m = 0; m < 8; ++m) {
+                float d = (1.0f + (float)m * 0.125f) * g, y = 1.0f / d;
+                if (dir) { d *= 4.0f; y *= 0.25f; }
+                cls[m] = find_sr_multiplier(d, y);
+            }
+            for (int c = 1; c < 127; ++c) {
+                const float v = e4m3_value(c);
+                const uint32_t vb = to_bits(v);
+                const int m = (int)((vb >> 20) & 7), ex = (int)((vb >> 23) & 0xFF) - 127;
+                float d = v * g, y = 1.0f / d;
+                float rd = (1.0f + (float)m * 0.125f) * g, ry = 1.0f / rd;
+                if (dir) { d *= 4.0f; y *= 0.25f; rd *= 4.0f; ry *= 0.25f; }
+                const int scaled = g < 0x1p100f && d == ldexpf(rd, ex) && y == ldexpf(ry, -ex);
+                if (!scaled || cls[m] < 0.0f) { ++none; continue; }
+                const float ym = ldexpf(cls[m], -ex);
+                ++found;
+                for (uint32_t u16 = 0; u16 < 0x7F80u; ++u16) {
+                    const float u = from_bits(u16 << 16);
+                    if (sr_cell(u * ym) != sr_cell(u / d)) {
+                        ++bad;
+#pragma omp critical
+                        if (bad < 8) fprintf(stderr, "sr table mismatch: A=%a dir=%d code=%d u=%a\n", (double)A[i],
+                                             dir, c, (double)u);
+                    }
+                }
+            }
+        }
+    }
+    mismatches += bad;
+    checks += found * 0x7F80ll;
+    printf("srtables: %d tensor scales, %lld entries with a multiplier, %lld without\n", na, found, none);
+    free(A);
+}
+
 int main(int argc, char** argv) {
     if (argc < 2) {
-        fprintf(stderr, "usage: %s bf16 | sixth | general N SEED | tables N SEED\n", argv[0]);
+        fprintf(stderr, "usage: %s bf16 | sixth | general N SEED | tables N SEED | srtables N SEED\n", argv[0]);
         return 2;
     }
     if (!strcmp(argv[1], "bf16")) {
@@ -226,6 +320,8 @@ int main(int argc, char** argv) {
         mode_general(atoll(argv[2]), strtoull(argv[3], NULL, 0));
     } else if (!strcmp(argv[1], "tables") && argc >= 4) {
         mode_tables(atoi(argv[2]), strtoull(argv[3], NULL, 0));
+    } else if (!strcmp(argv[1], "srtables") && argc >= 4) {
+        mode_srtables(atoi(argv[2]), strtoull(argv[3], NULL, 0));
     } else {
         fprintf(stderr, "unknown mode\n");
         return 2;

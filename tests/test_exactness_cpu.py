@@ -10,7 +10,11 @@
   one-ulp differences at E4M3 midpoints that an inexact division causes.
 - The NVFP4 scale tables' product multipliers: a multiplier the search accepts at
   the 14 boundary-adjacent BF16 values gives the exact division's E2M1 code for
-  every BF16 input, for 512 tensor scales (brute force over all BF16 values)."""
+  every BF16 input, for 512 tensor scales (brute force over all BF16 values).
+- The stochastic multipliers: a multiplier the search accepts at the BF16 values next
+  to the stochastic rule's grid points gives, for every BF16 input, the same grid
+  spacing and floor(256 f) as the exact quotient (so the same code for every random
+  byte), for 512 tensor scales."""
 import os
 import shutil
 import subprocess
@@ -57,5 +61,13 @@ def test_product_multipliers_every_bf16_input(checker):
     # the search finds a multiplier for most entries and flags the rest (the
     # factor-3 maxima), so both kinds of entry occur
     line = next(l for l in out.splitlines() if l.startswith("tables:") and "without" in l)
+    found, without = int(line.split(",")[1].split()[0]), int(line.split(",")[2].split()[0])
+    assert found > 100000 and without > 0
+
+
+def test_stochastic_multipliers_every_bf16_input(checker):
+    out = run(checker, "srtables", 512, 0x5A7)
+    assert " 0 mismatches" in out
+    line = next(l for l in out.splitlines() if l.startswith("srtables:") and "without" in l)
     found, without = int(line.split(",")[1].split()[0]), int(line.split(",")[2].split()[0])
     assert found > 100000 and without > 0

@@ -9,7 +9,9 @@
   fl(E4M3(c) * g) (times 4 column-wise), every reciprocal fl(1/d), and every
   product multiplier gives the exact division's E2M1 code for every BF16 input
   (brute force), for sections whose maxima carry the factors 3 and 7 of 2688, span
-  2^-30 .. 2^40 and sit on the 1e-10 floor.
+  2^-30 .. 2^40 and sit on the 1e-10 floor; with stochastic rounding every
+  stochastic multiplier gives the exact quotient's grid spacing and floor(256 f),
+  the part of the quotient the rounding rule reads.
 
 onnxruntime PR #33644 (Description) is why: one-ulp differences at encoding
 midpoints change codes, so every decision must be the exact one."""
@@ -111,3 +113,65 @@ def test_scale_tables_exact_for_every_bf16_input():
                 assert bad.size == 0, f"section {s} dir {d_} code {c}: u={u[bad[0]]!r} ym={ym!r} d={d!r}"
                 checked += 1
     assert checked > 1500 and without > 0, (checked, without)
+
+
+def sr_cell(q: np.ndarray) -> np.ndarray:
+    """What the stochastic E2M1 rule reads of a quotient q: for grid spacing D (0.5 /
+    1 / 2 below 2 / 4 / 6) and |q| / D = k + f, the pair (D, 256 k + floor(256 f)),
+    encoded as one integer; -1 for |q| >= 6 (saturation)."""
+    a = np.abs(q.astype(np.float64))
+    di = np.where(a < 2.0, 0, np.where(a < 4.0, 1, 2))
+    D = np.array([0.5, 1.0, 2.0])[di]
+    cell = np.floor(np.minimum(a, 6.0) / D * 256.0).astype(np.int64)   # (inf saturates below)
+    return np.where(a < 6.0, cell + 4096 * di, -1)
+
+
+def test_stochastic_scale_tables_exact_for_every_bf16_input():
+    """With stochastic rounding the tables hold stochastic multipliers: fl(u * ym)
+    must give the rule the same grid spacing and floor(256 f) as the exact quotient
+    fl(u / d) for every BF16 u (then every random byte gives the same code).  A table
+    with a scale code that has none is flagged, and its pass divides."""
+    dev = device()
+    announce("stochastic scale tables: multipliers of a call's workspace")
+    factors = [1.0, 3.0, 3.0 * 2.0 ** -30, 2.0 ** 40, 7.0 * 2.0 ** -10, 21.0, 1e-13, 0.0, 0.37, 5.5e3, 1.9e-6, 42.0]
+    S = len(factors)
+    rng = np.random.default_rng(72)
+    base = rng.standard_normal((S * 128, 256)).astype(np.float32)
+    for s, f in enumerate(factors):
+        block = base[s * 128:(s + 1) * 128]
+        block *= np.float32(f) / np.float32(np.abs(block).max())
+    x = torch.from_numpy(base).to(torch.bfloat16).to(dev)
+    call = mxq.GroupedNVFP4(x, [128] * S, 0x2D3C, 3, 0x5EED, list(range(S)), list(range(100, 100 + S)))
+    res = call()
+    torch.cuda.synchronize()
+    tables = host(call.workspace)[mxq.WORKSPACE_TABLES:mxq.WORKSPACE_TABLES + S * 2 * 128 * 16].view(np.float32)
+    tables = tables.reshape(S, 2, 128, 4)
+    g_all = (host(res.row_global), host(res.col_global))
+    u = (np.arange(0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    e4m3 = np.array([oracle.e4m3_value(c) for c in range(127)], np.float32)
+    checked = without = complete = 0
+    for s in range(S):
+        for d_ in range(2):
+            g = np.float32(g_all[d_][s])
+            T = tables[s, d_]
+            flagged = T[127, 0] == 1.0
+            has_none = False
+            for c in range(1, 127):
+                d = np.float32(e4m3[c] * g)
+                if d_ == 1:
+                    d = np.float32(d * np.float32(4.0))
+                assert T[c, 0] == d and T[c, 1] == np.float32(np.float32(1.0) / d), (s, d_, c)
+                ym = T[c, 2]
+                if ym < 0:
+                    without += 1
+                    has_none = True
+                    continue
+                with np.errstate(over="ignore"):
+                    want = sr_cell(u / d)
+                    got = sr_cell(u * ym)
+                bad = np.nonzero(got != want)[0]
+                assert bad.size == 0, f"section {s} dir {d_} code {c}: u={u[bad[0]]!r} ym={ym!r} d={d!r}"
+                checked += 1
+            assert flagged == has_none, (s, d_, flagged, has_none)
+            complete += not has_none
+    assert checked > 1500 and complete > 0, (checked, without, complete)

@@ -693,6 +693,33 @@ def test_grouped_graph_capture_replays(orc):
                 assert_same(f"replay{rep}:{name}", host(v), eager[name])
 
 
+def test_calls_on_a_side_stream(orc):
+    """A call on another stream (a torch stream or a raw handle) is ordered after the
+    current stream, where the binding allocated its outputs and workspace, and gives the
+    current stream's result."""
+    dev = device()
+    announce("grouped and DSA NVFP4 calls on a side stream")
+    w = synth.grouped_nvfp4(total_rows=768, k=512, parts=3, seed=41)
+    x = w.tensors["x"].to(dev)
+    args = (w.params["split_sections"], w.params["sign_mask"], 7)
+    want = {k: host(v).copy() for k, v in vars(mxq.mxq_group_rht_quant_nvfp4(x, *args)).items() if v is not None}
+    d = synth.dsa_rotate_fp8(tokens=125, heads=8, d_pe=64, seed=42)
+    pe, nope = d.tensors["pe"].to(dev), d.tensors["nope"].to(dev)
+    want_dsa = {k: host(v).copy() for k, v in vars(mxq.mxq_hadamard_quant_nvfp4(pe, nope)).items()
+                if v is not None}
+    s = torch.cuda.Stream()
+    for handle in (s, s.cuda_stream):
+        got = mxq.mxq_group_rht_quant_nvfp4(x, *args, stream=handle)
+        got_dsa = mxq.mxq_hadamard_quant_nvfp4(pe, nope, stream=handle)
+        torch.cuda.synchronize()
+        for name, v in vars(got).items():
+            if v is not None:
+                assert_same(f"grouped:{name}", host(v), want[name])
+        for name, v in vars(got_dsa).items():
+            if v is not None:
+                assert_same(f"dsa:{name}", host(v), want_dsa[name])
+
+
 # ============================================================== Philox vs rocRAND
 def test_philox_matches_rocrand(orc):
     """The Philox4x32-10 of the oracle (and so of the kernels, which match it
