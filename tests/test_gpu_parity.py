@@ -419,6 +419,31 @@ def test_grouped_sr_small(orc, k):
                     p["row_offsets"], None)
 
 
+@pytest.mark.parametrize("k", [256, 512])
+def test_grouped_sr_product_and_division_passes(orc, k):
+    """Stochastic rounding over sections whose scale tables differ: a pass whose table
+    has a stochastic multiplier for every scale code multiplies, the others divide.
+    Both kinds occur in this call (read from the flags the tables leave in the
+    workspace), and every output matches the oracle.  k = 256: the three-kernel form;
+    k = 512: the single-read form (its tables built by 256-thread work-groups)."""
+    dev = device()
+    announce(f"grouped sr: product and division passes in one call, k={k}")
+    factors = [1.0, 3.0, 2.0 ** 40, 7.0 * 2.0 ** -10, 21.0, 0.37, 5.5e3, 1.9e-6, 42.0, 0.011, 613.0, 2.5]
+    S = len(factors)
+    rng = np.random.default_rng(73)
+    base = rng.standard_normal((S * 128, k)).astype(np.float32)
+    for i, f in enumerate(factors):
+        block = base[i * 128:(i + 1) * 128]
+        block *= np.float32(f) / np.float32(np.abs(block).max())
+    x = torch.from_numpy(base).to(torch.bfloat16).to(dev)
+    ro, co = list(range(7, 7 + S)), list(range(900, 900 + S))
+    call = mxq.GroupedNVFP4(x, [128] * S, 0x6C1B, 3, 0xC0FFEE, ro, co)
+    compare_grouped(orc, x, [128] * S, 0x6C1B, 3, 0xC0FFEE, ro, co, workspace=call.workspace)
+    tables = host(call.workspace)[mxq.WORKSPACE_TABLES:mxq.WORKSPACE_TABLES + S * 2 * 128 * 16].view(np.float32)
+    flags = tables.reshape(S, 2, 128, 4)[:, :, 127, 0]
+    assert (flags == 0.0).any() and (flags == 1.0).any(), flags
+
+
 @pytest.mark.parametrize("flags,sr", [(3, False), (3, True), (7, False), (1, False), (2, True)])
 def test_grouped_single_read_reuse(orc, flags, sr):
     """The single-read form (k a multiple of 512, every section within the resident
