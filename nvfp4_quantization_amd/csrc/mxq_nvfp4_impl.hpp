@@ -112,11 +112,9 @@ __device__ __forceinline__ uint32_t absmax_nonan_pairs(uint32_t acc, uint32_t w)
     return absmax_pk_nonan(acc, w);
 }
 
-// Blocks whose random words are drawn together under stochastic rounding.
-#ifndef MXQ_SR_CHAINS
-#define MXQ_SR_CHAINS 4
-#endif
-constexpr int kSrChains = MXQ_SR_CHAINS;
+// Blocks whose random words are drawn together under stochastic rounding (1, 2 and 4
+// measured: 4 is fastest).
+constexpr int kSrChains = 4;
 
 __device__ __forceinline__ u32x4 block_random(uint64_t seed, uint64_t off, uint64_t beta) {
     u32x4 c = {(uint32_t)off, (uint32_t)(off >> 32), (uint32_t)beta, (uint32_t)(beta >> 32)};
@@ -360,8 +358,8 @@ __device__ __forceinline__ BlockOut encode_block(const float (&u)[16], uint32_t 
     // |u / d| stays near 6 or less, where div_rn is exact).  The division path takes
     // the IEEE quotients throughout (one more operation per element, cheaper than a
     // branch per block); stochastic rounding by division, where the division is on
-    // every element, branches.  (A product is infinite exactly where the quotient is,
-    // and saturates the same way.)
+    // every element, branches.  (A product needs no such case: it is 6 or more, an
+    // infinity included, exactly where the quotient is, and both saturate.)
     if (E == Enc::Sr && sc == 0x7Eu) {
         o.codes = make_uint2(encode8<E, true>(u, d, y, rnd, 0) & keep, encode8<E, true>(u + 8, d, y, rnd, 8) & keep);
     } else {
