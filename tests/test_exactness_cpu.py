@@ -71,3 +71,26 @@ def test_stochastic_multipliers_every_bf16_input(checker):
     line = next(l for l in out.splitlines() if l.startswith("srtables:") and "without" in l)
     found, without = int(line.split(",")[1].split()[0]), int(line.split(",")[2].split()[0])
     assert found > 100000 and without > 0
+
+
+def test_stochastic_grid_points_are_short():
+    """The stochastic multiplier criterion compares quotients only down to 9 mantissa
+    bits. That is enough because every point where the stochastic rule's reading changes
+    (the multiples of D/256 below 6 for grid spacing D = 0.5, 1, 2 below 2, 4, 6, and
+    6 itself) is a multiple of 2^(E-9) in its binade [2^E, 2^(E+1))."""
+    from fractions import Fraction
+    points = set()
+    for lo, hi, D in ((0, 2, Fraction(1, 2)), (2, 4, Fraction(1)), (4, 6, Fraction(2))):
+        j = 1
+        while D * j / 256 < hi:
+            if D * j / 256 >= lo:
+                points.add(D * j / 256)
+            j += 1
+    points.add(Fraction(6))
+    assert len(points) == 1792
+    for g in points:
+        E = g.numerator.bit_length() - g.denominator.bit_length()
+        if Fraction(2) ** E > g:
+            E -= 1
+        assert Fraction(2) ** E <= g < Fraction(2) ** (E + 1)
+        assert (g / Fraction(2) ** (E - 9)).denominator == 1, g
