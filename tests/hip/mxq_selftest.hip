@@ -20,6 +20,9 @@
 //          |q| / D = k + f, the code rounds up iff floor(256 f) + r >= 256; |q| >= 6
 //          saturates; swept over every non-NaN q, both signs, every r and every
 //          nibble position (in two classes: |q| in [2^-20, 16), and the rest).
+//   Division by a hardware reciprocal (mxq::div_rcp_bf16, SwiGLU's SiLU): div_rn's
+//          correction step on v_rcp_f32's reciprocal against IEEE division, for every
+//          BF16 numerator significand, both signs, and every divisor in [1, 2^24).
 //
 // Every kernel is a grid-stride loop over a fixed index range whose only memory
 // accesses are one atomic per wave into its result words at the end.
@@ -190,6 +193,33 @@ __global__ __launch_bounds__(256) void k_sweep_sr(u64* out) {
     min_key(out, 9, first_out);
 }
 
+// mxq::div_rcp_bf16 against IEEE division: every BF16 numerator significand
+// (x = 1 + k/128, both signs) against every divisor t in [1, 2^24) (24 binades x 2^23
+// significands).  out[0] mismatches, out[2] pairs checked, out[8] the smallest
+// mismatching (t bits << 8 | k).
+__global__ __launch_bounds__(256) void k_sweep_div_rcp(u64* out) {
+    u64 bad = 0, seen = 0, first = ~0ull;
+    const u64 stride = (u64)gridDim.x * blockDim.x;
+    for (u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x; i < 24ull << 23; i += stride) {
+        const uint32_t tb = ((uint32_t)(127 + (i >> 23)) << 23) | (uint32_t)(i & 0x7FFFFFu);
+        const float t = __builtin_bit_cast(float, tb);
+        for (uint32_t k = 0; k < 128; ++k) {
+            const float x = __builtin_bit_cast(float, 0x3F800000u | (k << 16));
+            const float q = mxq::div_rcp_bf16(x, t), qn = mxq::div_rcp_bf16(-x, t);
+            const float want = x / t;
+            if (__builtin_bit_cast(uint32_t, q) != __builtin_bit_cast(uint32_t, want) ||
+                __builtin_bit_cast(uint32_t, qn) != (__builtin_bit_cast(uint32_t, want) ^ 0x80000000u)) {
+                ++bad;
+                keep_min(first, ((u64)tb << 8) | k);
+            }
+        }
+        seen += 256;
+    }
+    add_count(out, 0, bad);
+    add_count(out, 2, seen);
+    min_key(out, 8, first);
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,6 +229,12 @@ extern "C" {
 int mxq_selftest_conversions(unsigned long long* out, void* stream) {
     if (!out) return 1;
     hipLaunchKernelGGL(k_sweep_conversions, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream), out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int mxq_selftest_div_rcp(unsigned long long* out, void* stream) {
+    if (!out) return 1;
+    hipLaunchKernelGGL(k_sweep_div_rcp, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream), out);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -5,6 +5,8 @@
   with integer reference encoders written from the formats' definitions): BF16,
   E4M3 and E2M1 nearest-even over all 2^32 FP32 inputs, and the stochastic E2M1
   conversion (random operand r << 24) over every non-NaN input and every r;
+- SiLU's division by the hardware reciprocal and a correction step, against IEEE
+  division for every BF16 numerator significand and every divisor in [1, 2^24);
 - the NVFP4 scale tables a call leaves in its workspace: every divisor is
   fl(E4M3(c) * g) (times 4 column-wise), every reciprocal fl(1/d), and every
   product multiplier gives the exact division's E2M1 code for every BF16 input
@@ -35,7 +37,7 @@ def selftest():
     if not os.path.exists(path):
         pytest.fail(f"{path} is missing: build the library")
     L = ctypes.CDLL(path)
-    for fn in (L.mxq_selftest_conversions, L.mxq_selftest_sr):
+    for fn in (L.mxq_selftest_conversions, L.mxq_selftest_sr, L.mxq_selftest_div_rcp):
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return L
@@ -67,6 +69,18 @@ def test_stochastic_e2m1_every_input_and_r():
     first = [None if o[8 + i] == U64 else (hex(o[8 + i] >> 8), o[8 + i] & 255) for i in range(2)]
     assert o[0] == 0, f"|q| in [2^-20, 16): {o[0]} mismatches, first (q bits, r) {first[0]}"
     assert o[1] == 0, f"other q: {o[1]} mismatches, first (q bits, r) {first[1]}"
+
+
+def test_reciprocal_division_every_bf16_numerator():
+    """SwiGLU's SiLU divides a BF16 gate value g by t = 1 + EXP(-g) with div_rn's
+    correction step on the hardware reciprocal of t (where 2^-100 <= |g| <= 2^126 and
+    t < 2^24): against IEEE division for every BF16 numerator significand, both signs,
+    and every FP32 divisor in [1, 2^24)."""
+    announce("reciprocal division sweep: 256 numerators x 24 binades x 2^23 divisors")
+    o = sweep(selftest().mxq_selftest_div_rcp)
+    assert o[2] == (24 << 23) * 256, f"pairs checked: {o[2]}"
+    first = None if o[8] == U64 else (hex(o[8] >> 8), o[8] & 255)
+    assert o[0] == 0, f"{o[0]} mismatches, first (t bits, numerator k) {first}"
 
 
 def test_scale_tables_exact_for_every_bf16_input():
