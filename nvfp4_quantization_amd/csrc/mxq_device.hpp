@@ -93,11 +93,14 @@ __device__ __forceinline__ float div_rn(float x, float d, float y) {
 }
 
 // fl(x / t) for a BF16 numerator x (8-bit significand) and a divisor t in [1, 2^24),
-// with 2^-100 <= |x| <= 2^126 (callers check the range and divide otherwise): div_rn's
+// with 2^-56 <= |x| <= 2^126 (callers check the range and divide otherwise): div_rn's
 // correction step on the hardware reciprocal.  tests/test_gpu_exactness.py sweeps
 // every BF16 numerator significand, both signs, against every divisor in [1, 2^24) on
-// the device (5.2e10 pairs, no mismatch); scaling x by a power of two scales every
-// intermediate exactly in that range.
+// the device (5.2e10 pairs, no mismatch).  Scaling x by 2^e scales every intermediate
+// exactly, each rounding included, while all of them stay normal: for x in [1, 2) a
+// nonzero residual fma(q0, t, -x) is a multiple of 2^-70 (q0 >= 2^-24, t >= 1), so it
+// stays normal for e >= -56; q0 and the quotient stay above 2^-80, and below
+// |x| <= 2^126.
 __device__ __forceinline__ float div_rcp_bf16(float x, float t) {
     return div_rn(x, t, __builtin_amdgcn_rcpf(t));
 }

@@ -41,13 +41,13 @@ __device__ __forceinline__ float exp_stated(float x) {
     return __builtin_amdgcn_ldexpf(p, (int)k);
 }
 
-// g is a BF16 value.  For 2^-100 <= |g| <= 2^126 and t < 2^24 the reciprocal form is
+// g is a BF16 value.  For 2^-56 <= |g| <= 2^126 and t < 2^24 the reciprocal form is
 // the correctly rounded quotient (div_rcp_bf16); zeros, tiny, huge and non-finite g,
 // and t >= 2^24 (g below about -16.6), take the IEEE division.
 __device__ __forceinline__ float silu(float g) {
     const float t = 1.0f + exp_stated(-g);
     const float ag = __builtin_fabsf(g);
-    if (ag >= 0x1p-100f && ag <= 0x1p126f && t < 0x1p24f) return div_rcp_bf16(g, t);
+    if (ag >= 0x1p-56f && ag <= 0x1p126f && t < 0x1p24f) return div_rcp_bf16(g, t);
     return g / t;                               // IEEE division, correctly rounded
 }
 

@@ -73,7 +73,7 @@ def test_stochastic_e2m1_every_input_and_r():
 
 def test_reciprocal_division_every_bf16_numerator():
     """SwiGLU's SiLU divides a BF16 gate value g by t = 1 + EXP(-g) with div_rn's
-    correction step on the hardware reciprocal of t (where 2^-100 <= |g| <= 2^126 and
+    correction step on the hardware reciprocal of t (where 2^-56 <= |g| <= 2^126 and
     t < 2^24): against IEEE division for every BF16 numerator significand, both signs,
     and every FP32 divisor in [1, 2^24)."""
     announce("reciprocal division sweep: 256 numerators x 24 binades x 2^23 divisors")
