@@ -237,12 +237,54 @@ __device__ __forceinline__ float quad_swap(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), PERM, 0xF, 0xF, true));
 }
 
+// v[i] += sgn * (v[i] of the quad's lane PERM) for 32 values, one DPP v_fmac_f32 each
+// (a product by +-1 is exact: one rounding).  In 16-value blocks of inline assembly
+// (the compiler does not fold a DPP move into v_fmac_f32); each block starts with the
+// two wait states that a DPP read of a VGPR needs after a VALU write of it.
+#define MXQ_QF(n) "v_fmac_f32_dpp %" #n ", %" #n ", %16 " MXQ_QP " row_mask:0xf bank_mask:0xf\n\t"
+#define MXQ_QF16 MXQ_QF(0) MXQ_QF(1) MXQ_QF(2) MXQ_QF(3) MXQ_QF(4) MXQ_QF(5) MXQ_QF(6) MXQ_QF(7) \
+                 MXQ_QF(8) MXQ_QF(9) MXQ_QF(10) MXQ_QF(11) MXQ_QF(12) MXQ_QF(13) MXQ_QF(14) MXQ_QF(15)
+template <int PERM>
+__device__ __forceinline__ void quad_fmac16(float* v, float sgn) {
+    static_assert(PERM == 0xB1 || PERM == 0x4E, "quad_perm lane ^ 1 or lane ^ 2");
+    if constexpr (PERM == 0xB1) {
+#define MXQ_QP "quad_perm:[1,0,3,2]"
+        asm("s_nop 1\n\t" MXQ_QF16
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+              "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+            : "v"(sgn));
+#undef MXQ_QP
+    } else {
+#define MXQ_QP "quad_perm:[2,3,0,1]"
+        asm("s_nop 1\n\t" MXQ_QF16
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+              "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+            : "v"(sgn));
+#undef MXQ_QP
+    }
+}
+#undef MXQ_QF16
+#undef MXQ_QF
+template <int PERM>
+__device__ __forceinline__ void quad_fmac32(float (&v)[32], float sgn) {
+    quad_fmac16<PERM>(v, sgn);
+    quad_fmac16<PERM>(v + 16, sgn);
+}
+
 // The 128-point Walsh-Hadamard butterfly of v = cat(pe[r][0:d_pe], nope[r][0:128-d_pe])
 // held by 4 consecutive lanes: lane `quarter` loads elements 32q .. 32q+31 (d_pe a
 // multiple of 8, so an 8-element load never straddles pe and nope) and ends with
 // outputs 32q .. 32q+31 before the constant: stages h = 1..16 run inside the lane,
 // h = 32 and 64 pair lanes quarter ^ 1 and quarter ^ 2.  A lane that is not live
 // works on zeros (its partners' rows are its own, so it changes no live output).
+//
+// MAG: the caller reads only |v| (a maximum).  Each cross-lane step is then one
+// v_fmac_f32 whose partner operand comes over DPP, v + sgn * other, instead of a DPP
+// move and fma(v, sgn, other): the upper lane of a pair holds other - v negated, and
+// after both stages every lane holds plus or minus the butterfly's value, rounded
+// alike (rounding to nearest is symmetric; NaNs and infinities arise from the same
+// operands).
+template <bool MAG = false>
 __device__ __forceinline__ void wht128_quarter(const uint16_t* pe, int64_t ld_pe, int32_t d_pe,
                                                const uint16_t* nope, int64_t ld_nope, int64_t r, bool live,
                                                int quarter, float (&v)[32]) {
@@ -270,6 +312,11 @@ __device__ __forceinline__ void wht128_quarter(const uint16_t* pe, int64_t ld_pe
             v[i] = x0 + x1;
             v[i + h] = x0 - x1;
         }
+    }
+    if (MAG) {
+        quad_fmac32<0xB1>(v, (quarter & 1) ? -1.0f : 1.0f);
+        quad_fmac32<0x4E>(v, (quarter & 2) ? -1.0f : 1.0f);
+        return;
     }
     // the upper lane of a pair forms other - v, the lower v + other: both are
     // fma(v, +-1, other), exact products with one rounding (signed zeros included);

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_dsa_nvfp4_amax(const DsaNvfp4Args a) {
     const int64_t r = (int64_t)blockIdx.x * kDsaRows + (threadIdx.x >> 2);
     const bool live = r < a.m;
     float v[32];
-    wht128_quarter(a.pe, a.ld_pe, a.d_pe, a.nope, a.ld_nope, r, live, quarter, v);
+    wht128_quarter<true>(a.pe, a.ld_pe, a.d_pe, a.nope, a.ld_nope, r, live, quarter, v);   // |v| only
     // max |BF16(fl(v C))| = BF16(fl(max |v| C)) (both roundings are monotone), NaN
     // outputs left out (a NaN input makes all 128 of its row NaN: then m is NaN and
     // the lane gives 0; inf - inf makes some NaN and leaves the rest infinite)
