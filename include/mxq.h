@@ -285,7 +285,7 @@ mxq_status mxq_hadamard_quant_nvfp4(const uint16_t* pe, int64_t ld_pe, int32_t d
  * workspace: device memory of at least
  *   mxq_group_rht_quant_nvfp4_workspace_size(total_rows, k, num_sections, flags)
  *   bytes (0 when only MXQ_FP8_ROWWISE is requested; otherwise 135,680 bytes plus
- *   8 bytes per 16 rows per started 2048 columns of x, rounded up to 256), 256-byte
+ *   8 bytes per 16 rows per started 1024 columns of x, rounded up to 256), 256-byte
  *   aligned,
  *   ZERO-FILLED BEFORE ITS FIRST USE.  It holds partial maxima and per-section
  *   scale tables through which the kernels of a call meet in stream order, and the
@@ -373,8 +373,8 @@ mxq_status mxq_group_rht_quant_nvfp4_with_amax(const uint16_t* x_bf16, int64_t k
  * per device, on the first call with that device current, and the words the call
  * needs at zero are cleared then by a fill kernel on that call's stream).  A call
  * whose workspace would exceed the array (mxq_group_rht_quant_nvfp4_workspace_size
- * above MXQ_NOALLOC_SCRATCH_BYTES: more than 114,112 bands of 16 rows x 2048 columns,
- * e.g. more than 912,896 rows at k = 4096) gives
+ * above MXQ_NOALLOC_SCRATCH_BYTES: more than 114,112 bands of 16 rows x 1024 columns,
+ * e.g. more than 456,448 rows at k = 4096) gives
  * MXQ_ERR_UNSUPPORTED before anything is enqueued.  The call itself allocates
  * nothing (no hipMalloc, no allocating library routine).  The stream must belong to
  * the current device.  Every call on one GPU uses that GPU's array: calls that

@@ -311,8 +311,8 @@ size_t mxq_group_rht_quant_nvfp4_workspace_size(int64_t total_rows, int64_t k, i
     if (total_rows > kMaxRows || k > kMaxGroupK) return 0;         // outside the supported profile
     if (!(flags & (MXQ_ROWWISE | MXQ_COLUMNWISE))) return 0;
     // status line, scale tables and the single-read form's partial words of one
-    // launch group, then the amax pass's 8-byte partials: one per 16 rows and 2048
-    // columns (or part) of the largest group, bounded by all rows
+    // launch group, then the amax pass's 8-byte partials: one per 16 rows and
+    // kAmaxCols = 1024 columns (or part) of the largest group, bounded by all rows
     const int64_t partials = (total_rows / mxq::kAmaxRows) * ceil_div(k, mxq::kAmaxCols);
     return (size_t)round256(mxq::kPartialsOffset + 8 * partials);
 }

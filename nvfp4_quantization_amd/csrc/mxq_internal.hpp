@@ -85,7 +85,7 @@ constexpr int64_t kDsaPartialsOffset = kDsaTableOffset + 128 * 16;
 // ---------------------------------------------------------------- grouped NVFP4
 // One launch group per at most kGroupSections sections.  A group runs three kernels
 // on the caller's stream (with caller-supplied maxima, the last two):
-//   amax    one work-group per band of 16 rows x 2048 columns: max |x| and
+//   amax    one work-group per band of 16 rows x 1024 columns: max |x| and
 //           max |H16 D x| of the band, one partial each;
 //   scales  one work-group per section: folds the section's partials (or takes
 //           the supplied maxima) into the two tensor scales and writes the
@@ -98,7 +98,9 @@ constexpr int kGroupSections = 32;
 constexpr int kTileRows = 128;        // token tile
 constexpr int kTileCols = 128;        // column tile
 constexpr int kAmaxRows = 16;         // amax pass: a work-group's band of rows
-constexpr int kAmaxCols = 2048;       //   and of columns (256 threads x 8)
+constexpr int kAmaxCols = 1024;       //   and of columns (256 threads x kAmaxWords BF16 pairs)
+constexpr int kAmaxWords = kAmaxCols / 512;
+static_assert(kAmaxWords == 2 || kAmaxWords == 4, "a thread loads 8 or 16 bytes of each row");
 
 struct Nvfp4Group {
     const uint16_t* x;                // first row of the group
@@ -187,7 +189,7 @@ hipError_t fused_blocks_per_cu_sr(uint32_t flags, int* blocks);
 //                  kFusedMaxItems), zero between calls; the three-kernel form never
 //                  touches them, so calls of either form can share a workspace
 //   kPartialsOffset  one 8-byte partial per amax work-group: per 16 rows and
-//                  2048 columns (or part) of the largest launch group
+//                  kAmaxCols = 1024 columns (or part) of the largest launch group
 constexpr int64_t kStatusOffset = 0;
 constexpr int64_t kTablesOffset = kStatusOffset + 512;
 constexpr int64_t kTablesBytes = (int64_t)kGroupSections * 2 * 128 * 16;

@@ -11,7 +11,7 @@
 // The FP32 tensor scale of a section needs the section's amax before any code is
 // final, so a call runs three kernels per group of sections:
 //
-//   k_nvfp4_amax   one work-group per 16-row band and 2048 columns: max |x| and
+//   k_nvfp4_amax   one work-group per 16-row band and 1024 columns: max |x| and
 //                  max |H16 D x| of the band, one partial each (ordinary stores).
 //   k_nvfp4_scales one work-group per section: folds the section's partials into
 //                  the two tensor scales and writes the section's scale tables.
@@ -634,54 +634,66 @@ __device__ __forceinline__ void build_tables_wg(const Nvfp4Group& G, int s, floa
 }
 
 // The amax pass over bands of kAmaxRows = 16 rows: a 256-thread work-group takes
-// 16 rows x kAmaxCols = 2048 columns, each thread 8 adjacent columns of all 16 rows, so a
-// wave's load instruction reads 1 KB of one row and the 16-point RHT of a column
-// block runs inside the lane.  The work-group writes one partial, the (row, column)
-// maxima of its band, with an ordinary store; nothing in this kernel reads them
-// (the scales kernel that follows on the stream does), so no work-group waits for
-// another and the kernel leaves no state behind.  Partial p = band * n_chunks +
+// 16 rows x kAmaxCols = 1024 columns, each thread 4 adjacent columns of all 16 rows
+// (16 loads of 8 bytes), so a wave's load instruction reads 512 contiguous bytes of
+// one row and the 16-point RHT of a column block runs inside the lane.  About 50
+// VGPRs: 8 waves per SIMD, every work-group of a 16384 x 4096 call resident in two
+// rounds (with 8 columns per thread, 93 VGPRs and 5 waves per SIMD, the pass took
+// 27.0 against 24.5 us, MI355X).  The work-group writes one partial, the (row,
+// column) maxima of its band, with an ordinary store; nothing in this kernel reads
+// them (the scales kernel that follows on the stream does), so no work-group waits
+// for another and the kernel leaves no state behind.  Partial p = band * n_chunks +
 // chunk: bits 16..31 the BF16 bits of max |x| (NaN-free), bits 32..63 the FP32 bits
 // of max |H16 D x| (NaN-free, before the 1/4 and the BF16 rounding).  Columns at
-// or past k (the last chunk when k % 2048 != 0) are not read.  The loads are
+// or past k (the last chunk when k % 1024 != 0) are not read.  The loads are
 // ordinary ones, not non-temporal: this pass alone is faster with the non-temporal
-// hint (23.6 against 28 us on the 16384 x 4096 call, MI355X), but the input then
-// does not stay in the Infinity Cache, and the quant pass's second read costs
-// 9 us more (the call: 84 against 76.5 us).
+// hint (22.3 against 24.7 us on the 16384 x 4096 call), but the input then does not
+// stay in the Infinity Cache, and the quant pass's second read costs 8.5 us more
+// (the call: 78.9 against 72.9 us).
 template <bool ROW, bool COL>
 __global__ __launch_bounds__(256) void k_nvfp4_amax(const Nvfp4Group G, int n_chunks) {
     __shared__ uint32_t red[2][4];
     const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int band = (int)blockIdx.x / n_chunks, chunk = (int)blockIdx.x - band * n_chunks;
-    const int64_t c0 = (int64_t)chunk * kAmaxCols + tid * 8;
+    const int64_t c0 = (int64_t)chunk * kAmaxCols + tid * (2 * kAmaxWords);
     uint32_t mr = 0;
     float mc = 0.0f;
     if (c0 < G.k) {
         const uint16_t* base = G.x + (int64_t)band * 16 * G.k + c0;
-        uint4 v[16];
+        uint32_t v[16][kAmaxWords];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) v[t] = *reinterpret_cast<const uint4*>(base + (int64_t)t * G.k);
+        for (int t = 0; t < 16; ++t) {
+            if constexpr (kAmaxWords == 4) {
+                const uint4 q = *reinterpret_cast<const uint4*>(base + (int64_t)t * G.k);
+                v[t][0] = q.x; v[t][1] = q.y; v[t][2] = q.z; v[t][3] = q.w;
+            } else {
+                const uint2 q = *reinterpret_cast<const uint2*>(base + (int64_t)t * G.k);
+                v[t][0] = q.x; v[t][1] = q.y;
+            }
+        }
         if (ROW) {
             uint32_t m = 0;
 #pragma unroll
             for (int t = 0; t < 16; ++t)
-                m = absmax_pk(absmax_pk(absmax_pk(absmax_pk(m, v[t].x), v[t].y), v[t].z), v[t].w);
+#pragma unroll
+                for (int i = 0; i < kAmaxWords; ++i) m = absmax_pk(m, v[t][i]);
             m = fold_pk(m);
             if (m > 0x7F80u) {                       // a NaN: the maximum without it
                 m = 0;
 #pragma unroll
                 for (int t = 0; t < 16; ++t)
-                    m = absmax_nonan_pairs(absmax_nonan_pairs(absmax_nonan_pairs(absmax_nonan_pairs(m, v[t].x), v[t].y),
-                                                              v[t].z), v[t].w);
+#pragma unroll
+                    for (int i = 0; i < kAmaxWords; ++i) m = absmax_nonan_pairs(m, v[t][i]);
             }
             mr = m;
         }
         if (COL) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 2 * kAmaxWords; ++j) {
                 float f[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    const uint32_t wd = (j >> 1) == 0 ? v[t].x : (j >> 1) == 1 ? v[t].y : (j >> 1) == 2 ? v[t].z : v[t].w;
+                    const uint32_t wd = v[t][j >> 1];
                     const uint32_t neg = sign_of_row(G.sign_mask, t);
                     f[t] = (j & 1) ? hi_signed(wd, neg) : lo_signed(wd, neg);
                 }

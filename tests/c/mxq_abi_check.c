@@ -39,13 +39,13 @@ static void strings(void) {
 }
 
 static void workspace_sizes(void) {
-    /* grouped: a fixed 135,680 bytes, then 8 bytes per 16 rows x 2048 columns (or
+    /* grouped: a fixed 135,680 bytes, then 8 bytes per 16 rows x 1024 columns (or
      * part), rounded to 256 */
     CHECK(mxq_group_rht_quant_nvfp4_workspace_size(16384, 4096, 8, MXQ_ROWWISE | MXQ_COLUMNWISE) ==
-          (size_t)(135680 + 8 * 1024 * 2));
+          (size_t)(135680 + 8 * 1024 * 4));
     CHECK(mxq_group_rht_quant_nvfp4_workspace_size(128, 128, 1, MXQ_ROWWISE) == (size_t)(135680 + 256));
     CHECK(mxq_group_rht_quant_nvfp4_workspace_size(65536, 7168, 32, MXQ_ROWWISE) ==
-          (size_t)(135680 + 8 * 4096 * 4));
+          (size_t)(135680 + 8 * 4096 * 7));
     CHECK(mxq_group_rht_quant_nvfp4_workspace_size(16384, 4096, 8, MXQ_FP8_ROWWISE) == 0);
     CHECK(mxq_group_rht_quant_nvfp4_workspace_size(-1, 4096, 8, MXQ_ROWWISE) == 0);
     /* DSA NVFP4: 2 KB of table, then 4 bytes per 64 rows, rounded to 256 */

@@ -136,13 +136,13 @@ def test_workspace_size_query(L):
     assert q(16384, 4096, 8, 4) == 0                              # FP8 only: no amax pass
     # two status lines, scale tables (32 sections x 2 directions x 128 x 16 B) and
     # the single-read form's 1024 partial words of one launch group, then the amax
-    # pass's 8-byte partials, one per 16 rows x 2048 columns (or part)
+    # pass's 8-byte partials, one per 16 rows x 1024 columns (or part)
     fixed = 512 + 32 * 2 * 128 * 16 + 4 * 1024
     assert fixed == mxq.WORKSPACE_FIXED == 135680
     for total, k, S in [(0, 4096, 8), (16384, 4096, 8), (65536, 7168, 32), (128, 128, 1), (16384, 4096, 256)]:
         for flags in (1, 2, 3, 7):
             need = q(total, k, S, flags)
-            partials = (total // 16) * -(-k // 2048)
+            partials = (total // 16) * -(-k // 1024)
             assert need % 256 == 0
             assert fixed + 8 * partials <= need < fixed + 8 * partials + 256
 
@@ -308,7 +308,7 @@ def test_noalloc_rejects_beyond_scratch(L):
     text = open(os.path.join(ROOT, "include", "mxq.h")).read()
     limit = int(eval(re.search(r"#define MXQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).expand(r"\1 << \2")))
     q = mxq.mxq_group_rht_quant_nvfp4_workspace_size
-    rows = 1 << 20                                      # 2^20 x 8192: 262,144 amax partials
+    rows = 1 << 20                                      # 2^20 x 8192: 524,288 amax partials
     assert q(rows, 8192, 1, 3) > limit
     sections = (ctypes.c_int64 * 1)(rows)
     out = mxq._NVFP4Out(A, A, A)
