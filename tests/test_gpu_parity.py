@@ -265,6 +265,47 @@ def test_dsa_strided_and_edges(orc):
     assert_same("scales", host(s), rs)
 
 
+def rotation_cancel_rows(m, seed, inf=True):
+    """BF16 rows whose 128-point rotation has exact zeros among nonzero outputs, in every
+    lane quarter: small integers (their sums cancel often), a few equal or opposite
+    entries, all -0, mixed +-0, and (inf) one infinity among zeros (inf and NaN
+    outputs; otherwise a row of small integers)."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-2, 3, size=(m, 128)).astype(np.float32)
+    for r in range(0, m, 8):
+        x[r] = 0.0
+        i, j = rng.choice(128, 2, replace=False)
+        x[r, i] = 1.5
+        x[r, j] = 1.5 if r % 16 else -1.5
+        x[r + 1] = -0.0
+        x[r + 2] = np.where(rng.integers(0, 2, 128) == 1, -0.0, 0.0)
+        if inf:
+            x[r + 3] = 0.0
+            x[r + 3, rng.integers(0, 128)] = np.inf if r % 16 else -np.inf
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("d_pe", [64, 8])
+def test_dsa_rotation_exact_zeros(orc, d_pe):
+    """The rotation's cross-lane stages run on negated operands in two of the four lanes
+    of a row, which is exact except for the sign of an exact zero; a wave with a zero
+    output recomputes its rows.  Rows with exact cancellations, -0 and infinities match
+    the oracle byte for byte, through the FP8 and the NVFP4 paths."""
+    dev = device()
+    announce(f"dsa rotation exact zeros d_pe={d_pe}")
+    b = rotation_cancel_rows(512, 61 + d_pe)
+    pe, nope = bf16_dev(b[:, :d_pe].copy(), dev), bf16_dev(b[:, d_pe:].copy(), dev)
+    q, s = mxq.mxq_hadamard_quant_fp8(pe, nope)
+    torch.cuda.synchronize()
+    rq, rs = orc.hadamard_quant_fp8(b[:, :d_pe].copy(), b[:, d_pe:].copy())
+    assert_same("codes", host(q), rq)
+    assert_same("scales", host(s), rs)
+    # NVFP4: one tensor scale, so no infinities (they would zero every other code)
+    b = rotation_cancel_rows(512, 62 + d_pe, inf=False)
+    pe, nope = bf16_dev(b[:, :d_pe].copy(), dev), bf16_dev(b[:, d_pe:].copy(), dev)
+    compare_dsa4(orc, b[:, :d_pe].copy(), b[:, d_pe:].copy(), pe, nope, amax_out=True)
+
+
 # ============================================================== DSA rotate + NVFP4
 def compare_dsa4(orc, pe_np, nope_np, pe, nope, amax_in=None, amax_out=False, call=None):
     """The DSA rotate + NVFP4 call on device tensors pe / nope against the oracle on
