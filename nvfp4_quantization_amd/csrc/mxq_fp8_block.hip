@@ -12,8 +12,9 @@
 // A 256-thread work-group stages one 128 x 128 BF16 tile in LDS with rows padded to
 // 65 dwords, so that both read patterns below are free of bank conflicts:
 //   row-wise     thread (row t/2, half t&1) reads 32 dwords of its row;
-//   column-wise  thread (column t&127, half t/128) reads 64 halfwords down its column
-//                (the 64 lanes of a wave read 64 consecutive columns of one row).
+//   column-wise  thread (wave w, lane 16 q + pl) reads the dword of columns 2p, 2p+1
+//                (p = 16 w + pl) in rows 64 a + 16 q + b, once each (the four
+//                quarters' rows are 16 rows = 16 banks apart).
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -37,6 +38,13 @@ __device__ __forceinline__ float quotient(float x, float s, float y) {
     return UE8M0 ? x * y : div_rn(x, s, y);
 }
 
+// Packed max |x| of BF16 pairs per half, a half that is a NaN (|bits| > 0x7F80)
+// counting as 0.
+__device__ __forceinline__ uint32_t absmax_pk_nonan_halves(uint32_t acc, uint32_t p) {
+    const uint32_t lo = p & 0x7FFFu, hi = (p >> 16) & 0x7FFFu;
+    return absmax_pk(acc, (lo > 0x7F80u ? 0u : lo) | (hi > 0x7F80u ? 0u : hi << 16));
+}
+
 template <bool UE8M0>
 __device__ __forceinline__ float block_scale(float amax) {
     const float s = (amax > k_floor() ? amax : k_floor()) * k_inv448();
@@ -48,7 +56,6 @@ __device__ __forceinline__ float block_scale(float amax) {
 template <bool ROW, bool COL, bool UE8M0>
 __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t tile[128 * kRowDwords];
-    __shared__ uint32_t red[2][128];
     const int t = threadIdx.x;
     const int64_t n_ct = a.k >> 7;
     const int64_t rb = blockIdx.x / n_ct, ct = blockIdx.x - rb * n_ct;
@@ -112,47 +119,77 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
     }
 
     if (COL) {
-        const int c = t & 127, half = t >> 7;
-        const uint16_t* col = reinterpret_cast<const uint16_t*>(tile) + c;
-        // max |x| of the half column without NaNs (|bits| above 0x7F80 are NaNs)
+        // Thread (wave w, lane q * 16 + pl) takes columns 2p and 2p + 1, p = 16 w + pl
+        // (one BF16 pair, one dword of each row), over the 32 rows 64 a + 16 q + b
+        // (a = 0, 1; b = 0 .. 15).  One 32-bit read per row brings both columns, and
+        // each value is read from LDS once.  For a fixed (a, b) the four quarters' rows
+        // lie 16 rows apart, 16 x 65 dwords = 16 banks modulo 64, and the 16 pairs of a
+        // quarter take consecutive banks: a wave's read is free of bank conflicts.  The
+        // four threads of a column pair are lanes pl + 16 q of one wave, so the column
+        // maxima meet over lane shuffles, with no LDS exchange and no barrier.
+        const int lane = t & 63, q = lane >> 4, p = (t >> 6) * 16 + (lane & 15);
+        uint32_t vv[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) vv[i] = tile[(64 * (i >> 4) + 16 * q + (i & 15)) * kRowDwords + p];
+        // per-column max |x| (packed halves: column 2p low, 2p + 1 high), NaNs aside
         uint32_t m = 0;
-        bool nan = false;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            const uint32_t v = col[(half * 64 + i) * (2 * kRowDwords)] & 0x7FFFu;
-            nan |= v > 0x7F80u;
-            m = (v <= 0x7F80u && v > m) ? v : m;
+        for (int i = 0; i < 32; ++i) m = absmax_pk(m, vv[i]);
+        uint32_t nan = ((m & 0xFFFFu) > 0x7F80u ? 1u : 0u) | ((m >> 16) > 0x7F80u ? 2u : 0u);
+        if (nan) {
+            m = 0;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) m = absmax_pk_nonan_halves(m, vv[i]);
         }
-        red[half][c] = m | (nan ? 0x80000000u : 0u);
-        __syncthreads();
-        const uint32_t p0 = red[0][c], p1 = red[1][c];
-        const uint32_t m0 = p0 & 0xFFFFu, m1 = p1 & 0xFFFFu;
-        const float s = block_scale<UE8M0>(bf16_mag(m0 > m1 ? m0 : m1));
-        const float y = 1.0f / s, sd = fp8_divisor(s);
-        const bool fix = nan || s == __builtin_inff();
-        uint32_t code[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = lo_bf16(col[(half * 64 + 4 * j + e) * (2 * kRowDwords)]);
-            code[j] = e4m3_pack4(quotient<UE8M0>(v[0], sd, y), quotient<UE8M0>(v[1], sd, y),
-                                 quotient<UE8M0>(v[2], sd, y), quotient<UE8M0>(v[3], sd, y));
-            if (fix) code[j] = nan_to_7f(code[j]);
+        for (int o = 16; o < 64; o <<= 1) {
+            m = absmax_pk(m, shfl_xor_u32(m, o));
+            nan |= shfl_xor_u32(nan, o);
         }
-        const int64_t r_first = row0 + half * 64;
-        uint8_t* dst = a.cq + (c0 + c) * a.cld + r_first;
+        float sc[2], yc[2], sdc[2];
+        bool fixc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            sc[h] = block_scale<UE8M0>(bf16_mag(h ? m >> 16 : m & 0xFFFFu));
+            yc[h] = 1.0f / sc[h];
+            sdc[h] = fp8_divisor(sc[h]);
+            fixc[h] = ((nan >> h) & 1u) || sc[h] == __builtin_inff();   // 0xFF codes: NaN inputs, or inf / inf
+        }
+        // code[h][a][j]: column 2p + h, rows 64 a + 16 q + 4 j .. + 3
+        uint32_t code[2][2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w = vv[a2 * 16 + 4 * j + e];
+                        v[e] = h ? hi_bf16(w) : lo_bf16(w);
+                    }
+                    uint32_t cw = e4m3_pack4(quotient<UE8M0>(v[0], sdc[h], yc[h]), quotient<UE8M0>(v[1], sdc[h], yc[h]),
+                                             quotient<UE8M0>(v[2], sdc[h], yc[h]), quotient<UE8M0>(v[3], sdc[h], yc[h]));
+                    if (fixc[h]) cw = nan_to_7f(cw);
+                    code[h][a2][j] = cw;
+                }
+        if (q == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) a.cs[(c0 + 2 * p + h) * a.csc + rb * a.csb] = sc[h];
+        }
         if (row0 + 128 <= a.m) {
             // A whole row block (uniform over the work-group): the 128 x 128 codes go
             // through LDS (over the input tile, which both passes have read by the
             // barrier), so that 8 lanes store each column's 128 bytes as one line
-            // instead of every lane storing 16-byte pieces of its own column.
-            if (half == 0) a.cs[(c0 + c) * a.csc + rb * a.csb] = s;
+            // instead of every lane storing 16-byte pieces of its own columns.
             __syncthreads();
-            uint32_t* stage = tile + c * kCodeDwords + half * 16;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint4*>(stage + 4 * q) = make_uint4(code[4 * q], code[4 * q + 1], code[4 * q + 2], code[4 * q + 3]);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int a2 = 0; a2 < 2; ++a2)
+                    *reinterpret_cast<uint4*>(tile + (2 * p + h) * kCodeDwords + 16 * a2 + 4 * q) =
+                        make_uint4(code[h][a2][0], code[h][a2][1], code[h][a2][2], code[h][a2][3]);
             __syncthreads();
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
@@ -164,8 +201,9 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
                 __syncthreads();                                  // the column lines are read
                 uint32_t* rstage = tile + (t >> 1) * kCodeDwords + (t & 1) * 16;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<uint4*>(rstage + 4 * q) = make_uint4(rc[4 * q], rc[4 * q + 1], rc[4 * q + 2], rc[4 * q + 3]);
+                for (int qq = 0; qq < 4; ++qq)
+                    *reinterpret_cast<uint4*>(rstage + 4 * qq) =
+                        make_uint4(rc[4 * qq], rc[4 * qq + 1], rc[4 * qq + 2], rc[4 * qq + 3]);
                 __syncthreads();
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
@@ -176,17 +214,23 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
             }
             return;
         }
-        if (r_first + 64 <= a.m) {
+        // the ragged last row block: 16-byte runs where all 16 rows exist, else only
+        // the rows that exist
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                reinterpret_cast<uint4*>(dst)[q] = make_uint4(code[4 * q], code[4 * q + 1], code[4 * q + 2], code[4 * q + 3]);
-        } else {
-            // the ragged last row block: only the rows that exist
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 64; ++i)
-                if (r_first + i < a.m) dst[i] = (uint8_t)(code[i >> 2] >> (8 * (i & 3)));
-        }
-        if (half == 0) a.cs[(c0 + c) * a.csc + rb * a.csb] = s;
+            for (int a2 = 0; a2 < 2; ++a2) {
+                const int64_t r_first = row0 + 64 * a2 + 16 * q;
+                uint8_t* dst = a.cq + (c0 + 2 * p + h) * a.cld + r_first;
+                if (r_first + 16 <= a.m) {
+                    *reinterpret_cast<uint4*>(dst) =
+                        make_uint4(code[h][a2][0], code[h][a2][1], code[h][a2][2], code[h][a2][3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (r_first + i < a.m) dst[i] = (uint8_t)(code[h][a2][i >> 2] >> (8 * (i & 3)));
+                }
+            }
     }
 }
 
