@@ -123,6 +123,44 @@ def test_fp8_blockwise(orc, m, k, options, dirs):
         assert_same("col_codes", host(cq.contiguous()), wcq)
 
 
+@pytest.mark.parametrize("m", [300, 256])
+def test_fp8_blockwise_strided_layouts(orc, m):
+    """Both outputs of the blockwise call through the C ABI with padded code rows and
+    transposed scale layouts (row-wise scale (r, g) at r + g * (m + 4); column-wise
+    scale (c, b) at c + b * (k + 8)): every code and scale lands where the strides say
+    and matches the oracle, and no padding byte is written."""
+    dev = device()
+    announce(f"fp8 blockwise strided layouts m={m}")
+    k = 384
+    rng = np.random.default_rng(90 + m)
+    x = rng.standard_normal((m, k)).astype(np.float32) * np.exp2(rng.integers(-8, 8, (m, 1)))
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    xd = bf16_dev(xb, dev)
+    nb = (m + 127) // 128
+    rld, cld = k + 32, (m + 15) // 16 * 16 + 32
+    rs_b, cs_b = m + 4, k + 8
+    rq = torch.full((m, rld), 0xEE, dtype=torch.uint8, device=dev)
+    cq = torch.full((k, cld), 0xEE, dtype=torch.uint8, device=dev)
+    rs = torch.full((k // 128 * rs_b,), -7.0, dtype=torch.float32, device=dev)
+    cs = torch.full((nb * cs_b,), -7.0, dtype=torch.float32, device=dev)
+    ro = mxq._FP8BlockOut(rq.data_ptr(), rld, rs.data_ptr(), 1, rs_b)
+    co = mxq._FP8BlockOut(cq.data_ptr(), cld, cs.data_ptr(), 1, cs_b)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert mxq.lib().mxq_quant_fp8_blockwise(ctypes.c_void_p(xd.data_ptr()), m, k, k, 0, ctypes.byref(ro),
+                                             ctypes.byref(co), st) == 0
+    torch.cuda.synchronize()
+    wq, ws, wcq, wcs = orc.quant_fp8_blockwise(xb, 0)
+    rq_h, cq_h, rs_h, cs_h = host(rq), host(cq), host(rs), host(cs)
+    assert_same("row_codes", rq_h[:, :k].copy(), wq)
+    assert_same("col_codes", cq_h[:, :m].copy(), wcq)
+    assert (rq_h[:, k:] == 0xEE).all() and (cq_h[:, m:] == 0xEE).all(), "padding written"
+    rs_t = rs_h.reshape(k // 128, rs_b)
+    cs_t = cs_h.reshape(nb, cs_b)
+    assert_same("row_scales", rs_t[:, :m].T.copy(), ws)
+    assert_same("col_scales", cs_t[:, :k].T.copy(), wcs)
+    assert (rs_t[:, m:] == -7.0).all() and (cs_t[:, k:] == -7.0).all(), "scale padding written"
+
+
 def test_fp8_blockwise_edges(orc):
     """NaN (quiet, signalling, negative), zero and -0 blocks, subnormals and exact ties
     in both directions, with a ragged last row block."""
