@@ -58,7 +58,14 @@ __global__ __launch_bounds__(256) void k_quant_fp8_blockwise(const Fp8BlockArgs 
     __shared__ __attribute__((aligned(16))) uint32_t tile[128 * kRowDwords];
     const int t = threadIdx.x;
     const int64_t n_ct = a.k >> 7;
-    const int64_t rb = blockIdx.x / n_ct, ct = blockIdx.x - rb * n_ct;
+    // Work-groups are dealt to the 8 XCDs in turn (b % 8), each with its own L2.  When
+    // the tiles split evenly, XCD x takes the contiguous tiles x N/8 .. (x+1) N/8 - 1, so
+    // that the 4-byte scales of one row block (one line per row across its k/128
+    // tiles) are all written through one L2 and leave as whole lines.
+    const int64_t n_tiles = (int64_t)gridDim.x;
+    const int64_t tile_id = n_tiles % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (n_tiles / 8) + blockIdx.x / 8
+                                             : (int64_t)blockIdx.x;
+    const int64_t rb = tile_id / n_ct, ct = tile_id - rb * n_ct;
     const int64_t row0 = rb * 128, c0 = ct * 128;
 
     // stage the tile: 2048 16-byte chunks, 8 per thread; rows past m are zeros
